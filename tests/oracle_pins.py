@@ -1,0 +1,301 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Each pin takes the oracle module as its argument and raises AssertionError when
+the oracle disagrees with something the pages or the mathematics fix:
+  * the hand-worked example in tests/golden/worked_example.json,
+  * closed forms and invariants (scores sum to G, refine scores sum to B*G,
+    constant values, identical keys),
+  * special cases that reduce to library routines: torch's
+    scaled_dot_product_attention (fp64, its own 1/sqrt(d) scale and its own
+    grouped-query head mapping), scipy's softmax, numpy's argsort,
+  * brute force by Python's sort on tiny inputs.
+They take the module as an argument so that tests/test_oracle_mutations.py can
+plant mistakes in a patched copy and check that some pin catches each one.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_example.json")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def _num(s: str) -> float:
+    """Parse the fixture's tiny expression language: a product of numbers and log(n)."""
+    v = 1.0
+    for f in s.split("*"):
+        f = f.strip()
+        if f.startswith("log(") and f.endswith(")"):
+            v *= math.log(float(f[4:-1]))
+        else:
+            v *= float(Fraction(f))
+    return v
+
+
+def _arr(x) -> np.ndarray:
+    return np.vectorize(_num, otypes=[np.float64])(np.array(x, dtype=object))
+
+
+def _frac(x) -> np.ndarray:
+    return np.vectorize(lambda s: float(Fraction(s)), otypes=[np.float64])(np.array(x, dtype=object))
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _sdpa_weights(q: np.ndarray, k: np.ndarray, scale=None) -> np.ndarray:
+    """Attention weights from torch SDPA, read out through identity values.
+
+    q: [Hq][n][d], k: [Hkv][L][d] -> [Hq][n][L]; torch maps query head h to KV head
+    h // (Hq/Hkv) itself (enable_gqa) and uses 1/sqrt(d) when scale is None.
+    """
+    Hkv, L, _ = k.shape
+    eye = torch.eye(L, dtype=torch.float64).expand(Hkv, L, L).contiguous()
+    w = F.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                       eye[None], scale=scale, enable_gqa=True)
+    return w[0].numpy()
+
+
+def _sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Dense attention from torch SDPA. q [Hq][n][d], k/v [Hkv][L][d] -> [Hq][n][d]."""
+    o = F.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                       torch.from_numpy(v)[None], enable_gqa=True)
+    return o[0].numpy()
+
+
+def _tiny(seed, L=40, Hq=6, Hkv=2, d=8, B=3):
+    r = _rng(seed)
+    return (r.standard_normal((B, Hq, d)), r.standard_normal((L, Hkv, d)),
+            r.standard_normal((L, Hkv, d)))
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_worked_example(orc):
+    """Every stage against the hand-derived fractions of the golden fixture."""
+    ex = json.load(open(GOLDEN))
+    d = ex["head_dim"]
+    scale = orc.default_scale(d)
+    qm, kc, vc = _arr(ex["q_merge"]), _arr(ex["k_cache"]), _arr(ex["v_cache"])
+    cand2, S = orc.select_merged(qm, kc, 2, scale)
+    np.testing.assert_allclose(S, _frac(ex["expected_scores"]), rtol=0, atol=1e-12)
+    for C, want in ex["expected_candidates"].items():
+        cand, _ = orc.select_merged(qm, kc, int(C), scale)
+        assert cand.tolist() == want, (C, cand.tolist(), want)
+    qr = _arr(ex["q_refine"])
+    for C, spec in ex["expected_refine"].items():
+        cand = np.array(ex["expected_candidates"][C])
+        R = orc.refine_scores(qr, kc, cand, scale)
+        np.testing.assert_allclose(R, _frac(spec["R"]), rtol=0, atol=1e-12)
+        for k, want in spec["topk"].items():
+            sel, _ = orc.refine_topk(qr, kc, cand, int(k), scale)
+            assert sel.tolist() == want, (C, k, sel.tolist(), want)
+    at = ex["attention"]
+    sel = np.array(at["selected"])
+    ks, vs = orc.gather_kv(kc, vc, sel)
+    out = orc.block_attention(_arr(at["q"]), _arr(at["k_blk"]), _arr(at["v_blk"]), ks, vs, scale)
+    np.testing.assert_allclose(out, _frac(at["expected_out"]), rtol=0, atol=1e-12)
+
+
+def pin_scores_sum_to_G(orc):
+    """Each KV head's score row sums to G (a sum of G softmaxes)."""
+    q, k, _ = _tiny(1, L=300, Hq=8, Hkv=2)
+    _, S = orc.select_merged(q, k, 10, orc.default_scale(8))
+    np.testing.assert_allclose(S.sum(axis=1), 4.0, rtol=0, atol=1e-12)
+
+
+def pin_scores_match_library_attention(orc):
+    """Selection scores = sum over the group of torch SDPA weights of the mean query.
+
+    The mean query is formed here from the linearity of the logits: the logits of
+    the mean equal the mean of the logits, checked against torch matmul.
+    """
+    B, Hq, Hkv, d, L = 5, 6, 2, 16, 50
+    q, k, _ = _tiny(2, L=L, Hq=Hq, Hkv=Hkv, d=d, B=B)
+    scale = orc.default_scale(d)
+    qbar = orc.merge_queries(q)
+    # linearity: <mean_b q_b, k> = mean_b <q_b, k>, checked with torch matmul per query
+    per_query = torch.einsum("bhd,lgd->bhgl", torch.from_numpy(q), torch.from_numpy(k)).numpy()
+    G = Hq // Hkv
+    want_logits = np.stack([per_query[:, h, h // G, :].mean(axis=0) for h in range(Hq)]) / math.sqrt(d)
+    np.testing.assert_allclose(orc.scan_logits(qbar, k, scale), want_logits, rtol=0, atol=1e-12)
+    w = _sdpa_weights(q.mean(axis=0)[:, None, :], np.ascontiguousarray(k.transpose(1, 0, 2)))[:, 0, :]
+    want = np.stack([w[g * G:(g + 1) * G].sum(axis=0) for g in range(Hkv)])
+    _, S = orc.select_merged(q, k, 5, scale)
+    np.testing.assert_allclose(S, want, rtol=0, atol=1e-12)
+
+
+def pin_softmax_library(orc):
+    """The oracle's softmax equals scipy's."""
+    x = _rng(3).standard_normal((4, 33)) * 7
+    np.testing.assert_allclose(orc.softmax(x, axis=1), scipy.special.softmax(x, axis=1), rtol=1e-13, atol=0)
+
+
+def pin_merge_single_query(orc):
+    """B = 1: the merged query is the query itself."""
+    q = _rng(4).standard_normal((1, 3, 5))
+    np.testing.assert_array_equal(orc.merge_queries(q), q[0])
+
+
+def pin_topk_is_argsort_when_G1_B1(orc):
+    """G = 1, B = 1: selection order = logit order, i.e. numpy argsort of K q."""
+    q, k, _ = _tiny(5, L=200, Hq=1, Hkv=1, d=16, B=1)
+    C = 37
+    cand, _ = orc.select_merged(q, k, C, orc.default_scale(16))
+    want = np.sort(np.argsort(-(k[:, 0, :] @ q[0, 0]), kind="stable")[:C])
+    assert cand[0].tolist() == want.tolist()
+
+
+def pin_topk_ties_brute_force(orc):
+    """Heavy ties: the k best by (score desc, position asc), by Python's sort."""
+    r = _rng(6)
+    for trial in range(50):
+        n = int(r.integers(1, 30))
+        s = r.integers(0, 4, size=n).astype(np.float64)
+        k = int(r.integers(1, n + 1))
+        want = sorted(sorted(range(n), key=lambda j: (-s[j], j))[:k])
+        assert orc.top_k_ascending(s, k).tolist() == want, (s, k)
+        tb = r.permutation(n)
+        want = sorted(sorted(range(n), key=lambda j: (-s[j], tb[j]))[:k])
+        assert orc.top_k_ascending(s, k, tiebreak=tb).tolist() == want
+
+
+def pin_all_equal_keys(orc):
+    """Identical keys: every score ties, so the candidates are [0, C) and the selection [0, K)."""
+    r = _rng(7)
+    q = r.standard_normal((4, 4, 8))
+    k = np.repeat(r.standard_normal((1, 2, 8)), 64, axis=0)
+    cand, S = orc.select_merged(q, k, 20, orc.default_scale(8))
+    assert (S == S[:, :1]).all()
+    assert cand.tolist() == [list(range(20))] * 2
+    sel, _ = orc.refine_topk(q, k, cand, 7, orc.default_scale(8))
+    assert sel.tolist() == [list(range(7))] * 2
+
+
+def pin_planted_keys_selected(orc):
+    """Keys planted along the group's mean query direction with 4x norm are always kept."""
+    from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, make_batch
+
+    wl = WORKLOADS["tiny_f32_L4096"]
+    for seed in (11, 12):
+        b = make_batch(wl.with_(L=1024, C=64, topk=32, T=1, seed_base=seed), steps=1)
+        q = b.as_f64("q0")[0]
+        k = b.as_f64("k_cache")
+        cand, _ = orc.select_merged(q, k, 64, orc.default_scale(wl.d))
+        sel, _ = orc.refine_topk(q, k, cand, 32, orc.default_scale(wl.d))
+        for g in range(wl.Hkv):
+            assert set(b.planted[0][g].tolist()) <= set(cand[g].tolist())
+            assert set(b.planted[0][g].tolist()) <= set(sel[g].tolist())
+
+
+def pin_permutation_equivariance(orc):
+    """Permuting the cache rows permutes the selected indices."""
+    q, k, _ = _tiny(8, L=120, Hq=4, Hkv=2, d=8)
+    perm = _rng(9).permutation(120)
+    scale = orc.default_scale(8)
+    cand, _ = orc.select_merged(q, k, 15, scale)
+    cand_p, _ = orc.select_merged(q, k[perm], 15, scale)
+    inv = np.argsort(perm)
+    for g in range(2):
+        assert sorted(perm[cand_p[g]].tolist()) == cand[g].tolist()
+        assert sorted(inv[cand[g]].tolist()) == cand_p[g].tolist()
+
+
+def pin_refine_sums_to_BG(orc):
+    """Each refine row sums to B*G (B*G softmaxes over the candidates)."""
+    q, k, _ = _tiny(10, L=90, Hq=6, Hkv=2, d=8, B=5)
+    cand, _ = orc.select_merged(q, k, 30, orc.default_scale(8))
+    R = orc.refine_scores(q, k, cand, orc.default_scale(8))
+    np.testing.assert_allclose(R.sum(axis=1), 15.0, rtol=0, atol=1e-12)
+
+
+def pin_refine_library_attention(orc):
+    """Refine scores = summed torch SDPA weights of the real queries over the candidate keys."""
+    B, Hq, Hkv, d = 4, 6, 3, 16
+    q, k, _ = _tiny(13, L=70, Hq=Hq, Hkv=Hkv, d=d, B=B)
+    cand, _ = orc.select_merged(q, k, 25, orc.default_scale(d))
+    R = orc.refine_scores(q, k, cand, orc.default_scale(d))
+    G = Hq // Hkv
+    for g in range(Hkv):
+        keys = k[cand[g], g, :][None]                                       # [1][C][d]
+        qs = np.ascontiguousarray(q[:, g * G:(g + 1) * G, :].transpose(1, 0, 2))  # [G][B][d]
+        w = _sdpa_weights(qs, keys)                                         # [G][B][C]
+        np.testing.assert_allclose(R[g], w.sum(axis=(0, 1)), rtol=0, atol=1e-12)
+
+
+def pin_refine_full_cache_single_query(orc):
+    """C = L, B = 1, same query for merge and refine: refine scores = selection scores."""
+    q, k, _ = _tiny(14, L=60, Hq=4, Hkv=2, d=8, B=1)
+    scale = orc.default_scale(8)
+    cand, S = orc.select_merged(q, k, 60, scale)
+    R = orc.refine_scores(q, k, cand, scale)
+    np.testing.assert_allclose(R, S, rtol=0, atol=1e-13)
+
+
+def pin_refine_keeps_all_when_topk_is_C(orc):
+    q, k, _ = _tiny(15, L=50, Hq=4, Hkv=2, d=8)
+    scale = orc.default_scale(8)
+    cand, _ = orc.select_merged(q, k, 12, scale)
+    sel, _ = orc.refine_topk(q, k, cand, 12, scale)
+    np.testing.assert_array_equal(sel, cand)
+
+
+def pin_gather_brute_force(orc):
+    r = _rng(16)
+    k = r.standard_normal((30, 3, 4))
+    v = r.standard_normal((30, 3, 4))
+    sel = np.stack([np.sort(r.choice(30, 7, replace=False)) for _ in range(3)])
+    ks, vs = orc.gather_kv(k, v, sel)
+    for g in range(3):
+        for i in range(7):
+            assert (ks[g, i] == k[sel[g, i], g]).all() and (vs[g, i] == v[sel[g, i], g]).all()
+
+
+def pin_dense_equivalence(orc):
+    """topk = C = L: the whole path is dense attention over [cache; in-block keys] (torch SDPA)."""
+    B, Hq, Hkv, d, L = 4, 6, 2, 16, 48
+    r = _rng(17)
+    q0 = r.standard_normal((B, Hq, d))
+    kc, vc = r.standard_normal((L, Hkv, d)), r.standard_normal((L, Hkv, d))
+    qs = r.standard_normal((2, B, Hq, d))
+    kb, vb = r.standard_normal((2, B, Hkv, d)), r.standard_normal((2, B, Hkv, d))
+    res = orc.herald_block(q0, kc, vc, qs, kb, vb, L, L, orc.default_scale(d))
+    assert res["sel"].tolist() == [list(range(L))] * Hkv
+    for t in range(2):
+        keys = np.ascontiguousarray(np.concatenate([kc, kb[t]]).transpose(1, 0, 2))
+        vals = np.ascontiguousarray(np.concatenate([vc, vb[t]]).transpose(1, 0, 2))
+        want = _sdpa(np.ascontiguousarray(qs[t].transpose(1, 0, 2)), keys, vals).transpose(1, 0, 2)
+        np.testing.assert_allclose(res["out"][t], want, rtol=0, atol=1e-12)
+
+
+def pin_attention_closed_forms(orc):
+    """Constant values give that value; identical keys give the mean of the values."""
+    r = _rng(18)
+    q = r.standard_normal((3, 4, 8))
+    ks, kb = r.standard_normal((2, 10, 8)), r.standard_normal((3, 2, 8))
+    c = r.standard_normal(8)
+    vs, vb = np.broadcast_to(c, (2, 10, 8)), np.broadcast_to(c, (3, 2, 8))
+    out = orc.block_attention(q, kb, vb, ks, vs, orc.default_scale(8))
+    np.testing.assert_allclose(out, np.broadcast_to(c, out.shape), rtol=0, atol=1e-12)
+    key = r.standard_normal(8)
+    ks, kb = np.broadcast_to(key, (2, 10, 8)), np.broadcast_to(key, (3, 2, 8))
+    vs, vb = r.standard_normal((2, 10, 8)), r.standard_normal((3, 2, 8))
+    out = orc.block_attention(q, kb, vb, ks, vs, orc.default_scale(8))
+    for h in range(4):
+        g = h // 2
+        mean = np.concatenate([vs[g], vb[:, g]]).mean(axis=0)
+        np.testing.assert_allclose(out[:, h], np.broadcast_to(mean, (3, 8)), rtol=0, atol=1e-12)
+
+
+ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]
