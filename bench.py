@@ -1,0 +1,211 @@
+"""Benchmark: blocks/s of the whole per-block path on one GPU.
+
+One step = one block for every sequence of the batch: herald_select_merged
+(merged-query full-cache scan + top-C), herald_refine_topk, herald_gather_kv,
+then herald_block_attn for each of the T denoising steps. Inputs are seeded
+synthetic tensors already resident in HBM. To keep the 256 MiB Infinity Cache
+from serving the scan, the K/V cache is replicated until the replicas span at
+least 512 MiB and consecutive steps rotate through them.
+
+Prints one JSON line. `roofline` is for the kernel that takes the most time per
+step, timed with HIP events recorded by the library around that kernel on the
+stream it runs on. `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "blocks/sec (select+refine+T-step sparse attn) at L=32K; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(wl, lengths):
+    """Algorithmic bytes / flops per launch of each kernel that gets a roofline."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    total = int(sum(lengths))
+    nk = wl.topk + wl.B
+    return {
+        # the merged-query scan streams the whole K cache once
+        "scan": ("hbm", total * wl.Hkv * wl.d * esz),
+        # refine: the two refine kernels each contract B*G query rows with C candidate rows
+        "refine_stats": ("mfma", 2.0 * wl.nseq * wl.Hq * wl.B * wl.C * wl.d),
+        "refine_scores": ("mfma", 2.0 * wl.nseq * wl.Hq * wl.B * wl.C * wl.d),
+        # gather reads and writes topk rows of K and V
+        "gather": ("hbm", 2 * 2 * wl.nseq * wl.Hkv * wl.topk * wl.d * esz),
+        # attention: QK^T and PV over topk + B keys for every query row
+        "attn": ("mfma", 4.0 * wl.nseq * wl.Hq * wl.B * nk * wl.d),
+    }
+
+
+def cpu_baseline(wl, batch, budget_s: float):
+    """The CPU oracle, one BLAS thread, whole blocks of sequence 0 until the time budget is used."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.herald_oracle as orc
+    from block_diffusion_sparse_herald_amd.inputs import bf16_bits_to_f32
+
+    def w(a):
+        return (bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+    a, e = int(batch.seq_start[0]), int(batch.seq_start[1])
+    args = (w(batch.q0[0]), w(batch.k_cache[a:e]), w(batch.v_cache[a:e]), w(batch.q_steps[:, 0]),
+            w(batch.kb_steps[:, 0]), w(batch.vb_steps[:, 0]))
+    n = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            orc.herald_block(*args, wl.C, wl.topk, orc.default_scale(wl.d))
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "blocks/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole block(s) of sequence 0 (L={e - a}, select+refine+gather+{wl.T} attention steps), "
+                      f"numpy fp64, 1 thread, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa32x8_L32768_b1")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the per-block path needs no "
+              f"cross-GPU exchange, so N GPUs would each run this same single-GPU workload)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_sparse_herald_amd import herald as H
+    from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, make_batch
+    from block_diffusion_sparse_herald_amd.runner import BlockRunner, batch_to_device, device_tensor
+
+    H.load()
+    wl = WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name}: generating inputs")
+    batch = make_batch(wl)
+    dev = batch_to_device(batch)
+    cache_bytes = 2 * dev["k_cache"].numel() * dev["k_cache"].element_size()
+    replicas = max(1, math.ceil(512 * 2**20 / cache_bytes))
+    kv = [(dev["k_cache"], dev["v_cache"])] + [(dev["k_cache"].clone(), dev["v_cache"].clone())
+                                              for _ in range(replicas - 1)]
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
+    q0, qs, kbs, vbs = dev["q0"], dev["q_steps"], dev["kb_steps"], dev["vb_steps"]
+
+    def step(i):
+        k, v = kv[i % replicas]
+        r.run_block(q0, k, v, qs, kbs, vbs)
+
+    def new_event():
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()  # instantiates the underlying HIP event
+        return ev
+
+    # warm-up; then one instrumented step per kernel to find the one that dominates a step
+    log(f"[bench] {replicas} K/V replica(s); warm-up {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    launches = {"scan": 1, "score_hist": 1, "radix": 2, "emit": 1, "refine_stats": 1 if wl.dtype == "bf16" else 0,
+                "refine_scores": 1, "refine_select": 1, "gather": 1, "attn": wl.T,
+                "attn_combine": wl.T if r.attn_splits > 1 else 0}
+    per_launch_us = {}
+    for name, n in launches.items():
+        if n == 0:
+            continue
+        times = []
+        for rep in range(3):
+            st, sp = new_event(), new_event()
+            H.herald_set_kernel_events(name, st, sp)
+            step(rep)
+            H.herald_set_kernel_events(name, None, None)
+            torch.cuda.synchronize()
+            times.append(st.elapsed_time(sp) * 1e3)
+        per_launch_us[name] = float(np.median(times))
+    per_step_us = {k: per_launch_us[k] * launches[k] for k in per_launch_us}
+    dominant = max((k for k in per_step_us if k in ("scan", "refine_stats", "refine_scores", "gather", "attn")),
+                   key=lambda k: per_step_us[k])
+    log(f"[bench] per-launch us: {json.dumps({k: round(v, 2) for k, v in per_launch_us.items()})}; "
+        f"dominant: {dominant}")
+
+    # timed region: K steps, the dominant kernel bracketed by fresh events every step
+    evs = [(new_event(), new_event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start, t_end = new_event(), new_event()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        H.herald_set_kernel_events(dominant, *evs[i])
+        step(i)
+    H.herald_set_kernel_events(dominant, None, None)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = t_start.elapsed_time(t_end)
+    ms_per_step = ms / args.steps
+    dom_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    blocks_per_s = wl.nseq * args.steps / (ms / 1e3)
+    log(f"[bench] {args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); {ms_per_step * 1e3:.1f} us/step")
+
+    bound, work = kernel_work(wl, batch.lengths)[dominant]
+    if bound == "hbm":
+        achieved, peak, unit = work / (dom_us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = work / (dom_us * 1e-6) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+        unit = "TFLOP/s"
+    roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None, "avg_launch_us": round(dom_us, 3)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(blocks_per_s, 2),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "nseq": wl.nseq, "L": int(max(batch.lengths)), "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "head_dim": wl.d, "B": wl.B, "C": wl.C, "topk": wl.topk, "T": wl.T, "kv_replicas": replicas,
+                   "attn_splits": r.attn_splits},
+        "tokens_per_s": round(blocks_per_s * wl.B, 1),
+        "per_launch_us": {k: round(v, 2) for k, v in per_launch_us.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl, batch, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

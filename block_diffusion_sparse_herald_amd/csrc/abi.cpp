@@ -1,0 +1,358 @@
+// C ABI of libherald.so: argument validation (before any HIP call), workspace
+// sizing and carving, kernel launches, error reporting and the host-pool gather.
+// The operations and their definitions are documented in include/herald.h.
+#include "herald.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+using namespace herald;
+
+namespace {
+
+thread_local std::string g_error;
+
+constexpr int kNumKernels = 10;
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+thread_local KernelEvents g_events[kNumKernels];
+
+herald_status fail(herald_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+herald_status ok() {
+  g_error.clear();
+  return HERALD_OK;
+}
+
+#define HERALD_HIP(call)                                                                    \
+  do {                                                                                      \
+    const hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess) return fail(HERALD_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+// Launch `call` (returns hipError_t) as kernel `id`, bracketed by its events if set.
+#define HERALD_LAUNCH(id, stream, call)                                                 \
+  do {                                                                                  \
+    if (g_events[id].start) HERALD_HIP(hipEventRecord(g_events[id].start, stream));     \
+    HERALD_HIP(call);                                                                   \
+    if (g_events[id].stop) HERALD_HIP(hipEventRecord(g_events[id].stop, stream));       \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+herald_status check_ptr(const void* p, const char* name, bool nullable = false) {
+  if (!p) return nullable ? HERALD_OK : fail(HERALD_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(HERALD_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return HERALD_OK;
+}
+
+#define HERALD_TRY(expr)                         \
+  do {                                           \
+    const herald_status st_ = (expr);            \
+    if (st_ != HERALD_OK) return st_;            \
+  } while (0)
+
+// Validates the problem and fills the kernel-side shape. Host memory only.
+herald_status make_shape(const herald_problem* p, Shape* s) {
+  if (!p) return fail(HERALD_ERR_INVALID_ARG, "problem is NULL");
+  if (p->reserved != 0) return fail(HERALD_ERR_INVALID_ARG, "reserved field must be 0");
+  if (p->nseq < 0) return fail(HERALD_ERR_INVALID_ARG, "nseq = %d is negative", p->nseq);
+  if (p->nseq > 65535) return fail(HERALD_ERR_UNSUPPORTED, "nseq = %d exceeds 65535", p->nseq);
+  if (p->block_size < 1 || p->block_size > 64)
+    return fail(p->block_size < 1 ? HERALD_ERR_INVALID_ARG : HERALD_ERR_UNSUPPORTED,
+                "block_size = %d outside [1, 64]", p->block_size);
+  if (p->num_kv_heads < 1) return fail(HERALD_ERR_INVALID_ARG, "num_kv_heads = %d < 1", p->num_kv_heads);
+  if (p->num_kv_heads > 65535) return fail(HERALD_ERR_UNSUPPORTED, "num_kv_heads = %d exceeds 65535", p->num_kv_heads);
+  if (p->num_q_heads < p->num_kv_heads || p->num_q_heads % p->num_kv_heads != 0)
+    return fail(HERALD_ERR_INVALID_ARG, "num_q_heads = %d is not a positive multiple of num_kv_heads = %d",
+                p->num_q_heads, p->num_kv_heads);
+  if ((int64_t)p->nseq * p->num_kv_heads > 65535)
+    return fail(HERALD_ERR_UNSUPPORTED, "nseq * num_kv_heads = %lld exceeds 65535", (long long)p->nseq * p->num_kv_heads);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (G > 8) return fail(HERALD_ERR_UNSUPPORTED, "group size G = %d exceeds 8", G);
+  if (p->block_size * G > 256)
+    return fail(HERALD_ERR_UNSUPPORTED, "block_size * G = %d exceeds 256", p->block_size * G);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(HERALD_ERR_UNSUPPORTED, "head_dim = %d is not 64 or 128", p->head_dim);
+  if (p->dtype != HERALD_F32 && p->dtype != HERALD_BF16) return fail(HERALD_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (p->num_candidates < 1) return fail(HERALD_ERR_INVALID_ARG, "num_candidates = %d < 1", p->num_candidates);
+  if (p->num_candidates > kMaxCandidates)
+    return fail(HERALD_ERR_UNSUPPORTED, "num_candidates = %d exceeds %d", p->num_candidates, kMaxCandidates);
+  if (p->topk < 1 || p->topk > p->num_candidates)
+    return fail(HERALD_ERR_INVALID_ARG, "topk = %d outside [1, num_candidates = %d]", p->topk, p->num_candidates);
+  if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
+    return fail(HERALD_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!p->seq_start_host) return fail(HERALD_ERR_INVALID_ARG, "seq_start_host is NULL");
+  if (!p->seq_start_dev) return fail(HERALD_ERR_INVALID_ARG, "seq_start_dev is NULL");
+  if (p->seq_start_host[0] != 0) return fail(HERALD_ERR_INVALID_ARG, "seq_start[0] must be 0");
+  int64_t max_len = 0;
+  for (int i = 0; i < p->nseq; ++i) {
+    const int64_t L = p->seq_start_host[i + 1] - p->seq_start_host[i];
+    if (L < p->num_candidates)
+      return fail(HERALD_ERR_INVALID_ARG, "sequence %d has length %lld < num_candidates = %d", i, (long long)L,
+                  p->num_candidates);
+    if (L > (int64_t(1) << 30)) return fail(HERALD_ERR_UNSUPPORTED, "sequence %d is longer than 2^30", i);
+    max_len = std::max(max_len, L);
+  }
+  s->nseq = p->nseq;
+  s->B = p->block_size;
+  s->Hq = p->num_q_heads;
+  s->Hkv = p->num_kv_heads;
+  s->D = p->head_dim;
+  s->G = G;
+  s->C = p->num_candidates;
+  s->topk = p->topk;
+  s->bf16 = p->dtype == HERALD_BF16;
+  s->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.f / std::sqrt((float)p->head_dim);
+  s->total = p->seq_start_host[p->nseq];
+  s->max_len = max_len;
+  s->seq_start = p->seq_start_dev;
+  return HERALD_OK;
+}
+
+size_t elem_bytes(const Shape& s) { return s.bf16 ? 2 : 4; }
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Carves consecutive 256-byte-aligned regions out of a workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+SelectWs carve_select(const Shape& s, void* ws, size_t* bytes) {
+  Carver c{static_cast<char*>(ws)};
+  SelectWs w;
+  w.nchunk = (int)((s.max_len + kScanTok - 1) / kScanTok);
+  w.nwords = (int)((s.max_len + 63) / 64);
+  w.qbar = c.take<float>((size_t)s.nseq * s.Hq * s.D);
+  w.logits = c.take<float>((size_t)s.Hq * s.total);
+  w.partials = c.take<float2>((size_t)s.nseq * s.Hq * w.nchunk);
+  w.scores = c.take<float>((size_t)s.Hkv * s.total);
+  w.hist = c.take<uint32_t>((size_t)s.nseq * s.Hkv * 3 * kRadixBins);
+  w.bits = c.take<uint64_t>((size_t)s.nseq * s.Hkv * 2 * w.nwords);
+  *bytes = c.off;
+  return w;
+}
+
+RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
+  Carver c{static_cast<char*>(ws)};
+  RefineWs w;
+  w.ntile = (s.C + kRefineTile - 1) / kRefineTile;
+  w.row_stats = c.take<float2>((size_t)s.nseq * s.Hkv * w.ntile * s.B * s.G);
+  w.rscore = c.take<float>((size_t)s.nseq * s.Hkv * s.C);
+  *bytes = c.off;
+  return w;
+}
+
+AttnWs carve_attn(const Shape& s, void* ws, size_t* bytes) {
+  Carver c{static_cast<char*>(ws)};
+  AttnWs w;
+  w.nsplit = attn_splits(s, &w.keys_per_split);
+  w.o_part = nullptr;
+  w.ml = nullptr;
+  if (w.nsplit > 1) {
+    const size_t rows = (size_t)s.nseq * s.Hkv * w.nsplit * attn_rpad(s);
+    w.o_part = c.take<float>(rows * s.D);
+    w.ml = c.take<float2>(rows);
+  }
+  *bytes = c.off;
+  return w;
+}
+
+size_t gather_host_bytes(const Shape& s) { return align256(2 * (size_t)s.nseq * s.Hkv * s.topk * s.D * elem_bytes(s)); }
+
+herald_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return HERALD_OK;
+  if (!ws) return fail(HERALD_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (!aligned16(ws)) return fail(HERALD_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (have < need) return fail(HERALD_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return HERALD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+herald_status herald_workspace_size(const herald_problem* p, int op, size_t* bytes) {
+  if (!bytes) return fail(HERALD_ERR_INVALID_ARG, "bytes is NULL");
+  Shape s;
+  HERALD_TRY(make_shape(p, &s));
+  size_t n = 0;
+  switch (op) {
+    case HERALD_OP_SELECT: carve_select(s, nullptr, &n); break;
+    case HERALD_OP_REFINE: carve_refine(s, nullptr, &n); break;
+    case HERALD_OP_ATTN: carve_attn(s, nullptr, &n); break;
+    case HERALD_OP_GATHER_HOST: n = gather_host_bytes(s); break;
+    default: return fail(HERALD_ERR_INVALID_ARG, "unknown op %d", op);
+  }
+  if (s.nseq == 0) n = 0;
+  *bytes = n;
+  return ok();
+}
+
+int64_t herald_vsel_ld(int32_t topk) { return topk < 1 ? 0 : vsel_ld(topk); }
+
+herald_status herald_select_merged(const herald_problem* p, const void* q_merge, const void* k_cache,
+                                   int32_t* cand_idx, float* cand_score, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  Shape s;
+  HERALD_TRY(make_shape(p, &s));
+  if (s.nseq == 0) return ok();
+  HERALD_TRY(check_ptr(q_merge, "q_merge"));
+  HERALD_TRY(check_ptr(k_cache, "k_cache"));
+  HERALD_TRY(check_ptr(cand_idx, "cand_idx"));
+  HERALD_TRY(check_ptr(cand_score, "cand_score", true));
+  size_t need;
+  carve_select(s, nullptr, &need);
+  HERALD_TRY(check_ws(ws, ws_bytes, need));
+  const SelectWs w = carve_select(s, ws, &need);
+  HERALD_LAUNCH(0, stream, launch_merge(s, q_merge, w, stream));
+  HERALD_LAUNCH(0, stream, launch_scan(s, k_cache, w, stream));
+  HERALD_LAUNCH(1, stream, launch_score_hist(s, w, stream));
+  HERALD_LAUNCH(2, stream, launch_radix_pass(s, w, 2, stream));
+  HERALD_LAUNCH(2, stream, launch_radix_pass(s, w, 3, stream));
+  HERALD_LAUNCH(3, stream, launch_emit_candidates(s, w, cand_idx, cand_score, stream));
+  return ok();
+}
+
+herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, const void* k_cache,
+                                 const int32_t* cand_idx, int32_t* topk_idx, float* topk_score, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  HERALD_TRY(make_shape(p, &s));
+  if (s.nseq == 0) return ok();
+  HERALD_TRY(check_ptr(q_refine, "q_refine"));
+  HERALD_TRY(check_ptr(k_cache, "k_cache"));
+  HERALD_TRY(check_ptr(cand_idx, "cand_idx"));
+  HERALD_TRY(check_ptr(topk_idx, "topk_idx"));
+  HERALD_TRY(check_ptr(topk_score, "topk_score", true));
+  size_t need;
+  carve_refine(s, nullptr, &need);
+  HERALD_TRY(check_ws(ws, ws_bytes, need));
+  const RefineWs w = carve_refine(s, ws, &need);
+  if (s.bf16) {
+    HERALD_LAUNCH(4, stream, launch_refine_stats(s, q_refine, k_cache, cand_idx, w, stream));
+    HERALD_LAUNCH(5, stream, launch_refine_scores(s, q_refine, k_cache, cand_idx, w, stream));
+  } else {
+    HERALD_LAUNCH(5, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, stream));
+  }
+  HERALD_LAUNCH(6, stream, launch_refine_select(s, cand_idx, w, topk_idx, topk_score, stream));
+  return ok();
+}
+
+herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const void* v_src, int32_t src_is_host,
+                               const int32_t* topk_idx, void* k_sel, void* v_sel, void* host_staging,
+                               int32_t* host_idx, void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t done) {
+  Shape s;
+  HERALD_TRY(make_shape(p, &s));
+  if (s.nseq == 0) return ok();
+  HERALD_TRY(check_ptr(k_src, "k_src"));
+  HERALD_TRY(check_ptr(v_src, "v_src"));
+  HERALD_TRY(check_ptr(topk_idx, "topk_idx"));
+  HERALD_TRY(check_ptr(k_sel, "k_sel"));
+  HERALD_TRY(check_ptr(v_sel, "v_sel"));
+  if (src_is_host != 0 && src_is_host != 1) return fail(HERALD_ERR_INVALID_ARG, "src_is_host must be 0 or 1");
+  if (!src_is_host) {
+    HERALD_LAUNCH(7, stream, launch_gather(s, k_src, v_src, topk_idx, k_sel, v_sel, stream));
+    if (done) HERALD_HIP(hipEventRecord(done, stream));
+    return ok();
+  }
+  HERALD_TRY(check_ptr(host_staging, "host_staging"));
+  HERALD_TRY(check_ptr(host_idx, "host_idx"));
+  if (!done) return fail(HERALD_ERR_INVALID_ARG, "done event is required on the host-pool path");
+  const size_t need = gather_host_bytes(s);
+  HERALD_TRY(check_ws(ws, ws_bytes, need));
+  const size_t n = (size_t)s.nseq * s.Hkv * s.topk;
+  const size_t row = (size_t)s.D * elem_bytes(s);
+  HERALD_HIP(hipMemcpyAsync(host_idx, topk_idx, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  HERALD_HIP(hipStreamSynchronize(stream));
+  const char* kh = static_cast<const char*>(k_src);
+  const char* vh = static_cast<const char*>(v_src);
+  char* kst = static_cast<char*>(host_staging);
+  char* vst = kst + n * row;
+  for (int sq = 0; sq < s.nseq; ++sq) {
+    const int64_t j0 = p->seq_start_host[sq];
+    const int64_t L = p->seq_start_host[sq + 1] - j0;
+    for (int g = 0; g < s.Hkv; ++g) {
+      const size_t unit = (size_t)sq * s.Hkv + g;
+      for (int i = 0; i < s.topk; ++i) {
+        const int32_t j = host_idx[unit * s.topk + i];
+        if (j < 0 || j >= L)
+          return fail(HERALD_ERR_INVALID_ARG, "topk_idx[%d][%d][%d] = %d outside [0, %lld)", sq, g, i, j, (long long)L);
+        const size_t src = ((size_t)(j0 + j) * s.Hkv + g) * row;
+        std::memcpy(kst + (unit * s.topk + i) * row, kh + src, row);
+        std::memcpy(vst + (unit * s.topk + i) * row, vh + src, row);
+      }
+    }
+  }
+  HERALD_HIP(hipMemcpyAsync(ws, host_staging, 2 * n * row, hipMemcpyHostToDevice, stream));
+  const char* wsc = static_cast<const char*>(ws);
+  HERALD_LAUNCH(7, stream, launch_layout_packed(s, wsc, wsc + n * row, k_sel, v_sel, stream));
+  HERALD_HIP(hipEventRecord(done, stream));
+  return ok();
+}
+
+herald_status herald_block_attn(const herald_problem* p, const void* q, const void* k_blk, const void* v_blk,
+                                const void* k_sel, const void* v_sel, void* out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  Shape s;
+  HERALD_TRY(make_shape(p, &s));
+  if (s.nseq == 0) return ok();
+  HERALD_TRY(check_ptr(q, "q"));
+  HERALD_TRY(check_ptr(k_blk, "k_blk"));
+  HERALD_TRY(check_ptr(v_blk, "v_blk"));
+  HERALD_TRY(check_ptr(k_sel, "k_sel"));
+  HERALD_TRY(check_ptr(v_sel, "v_sel"));
+  HERALD_TRY(check_ptr(out, "out"));
+  size_t need;
+  carve_attn(s, nullptr, &need);
+  HERALD_TRY(check_ws(ws, ws_bytes, need));
+  const AttnWs w = carve_attn(s, ws, &need);
+  HERALD_LAUNCH(8, stream, launch_attn(s, q, k_blk, v_blk, k_sel, v_sel, out, w, stream));
+  if (w.nsplit > 1) HERALD_LAUNCH(9, stream, launch_attn_combine(s, w, out, stream));
+  return ok();
+}
+
+const char* herald_last_error(void) { return g_error.c_str(); }
+
+herald_status herald_set_kernel_events(int32_t kernel_id, hipEvent_t start, hipEvent_t stop) {
+  if (kernel_id < 0 || kernel_id >= kNumKernels) return fail(HERALD_ERR_INVALID_ARG, "kernel id %d", kernel_id);
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(HERALD_ERR_INVALID_ARG, "start and stop must both be set or both be NULL");
+  g_events[kernel_id].start = start;
+  g_events[kernel_id].stop = stop;
+  return ok();
+}
+
+int32_t herald_attn_splits(const herald_problem* p) {
+  Shape s;
+  if (make_shape(p, &s) != HERALD_OK) return -1;
+  int kps;
+  return attn_splits(s, &kps);
+}
+
+}  // extern "C"

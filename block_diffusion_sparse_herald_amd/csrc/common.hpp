@@ -1,0 +1,183 @@
+// Device helpers shared by the HERALD kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace herald {
+
+typedef uint16_t bf16;  // storage type of bf16 tensors (bit pattern)
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<bf16>(bf16 v) { return bf16_to_f32(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float v) { return f32_to_bf16(v); }
+
+// 16-byte vector: elements per vector and unpacking to fp32.
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+  }
+};
+template <>
+struct Vec16<bf16> {
+  static constexpr int N = 8;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+    o[4] = __uint_as_float(v.z << 16);
+    o[5] = __uint_as_float(v.z & 0xffff0000u);
+    o[6] = __uint_as_float(v.w << 16);
+    o[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- (max, sum) pairs
+
+// Merge two (max, sum-of-2^(x-max)) pairs. Commutative bit for bit, so butterfly
+// reductions leave the same value in every lane. Empty pairs are (-inf, 0).
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * fast_exp2(m - M) + s2 * fast_exp2(m2 - M);
+  m = M;
+}
+
+__device__ __forceinline__ void ms_wave_merge(float& m, float& s) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const float s2 = __shfl_xor(s, o);
+    ms_merge(m, s, m2, s2);
+  }
+}
+
+// ---------------------------------------------------------------- block-wide scans
+
+// Exclusive prefix sum of `v` over the NT threads of the block (NT multiple of 64).
+// `lds` holds NT/64 + 1 ints. Every thread receives the block total in *total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) lds[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int w = 0; w < NT / kWave; ++w) {
+      const uint32_t t = lds[w];
+      lds[w] = acc;
+      acc += t;
+    }
+    lds[NT / kWave] = acc;
+  }
+  __syncthreads();
+  const uint32_t r = lds[wid] + x - v;
+  *total = lds[NT / kWave];
+  __syncthreads();
+  return r;
+}
+
+// Radix-select step. hist[0..nbins) counts the keys of each digit value. Finds the
+// largest digit b whose suffix count sum_{b' >= b} hist[b'] reaches k, and the
+// count strictly above it. Result broadcast to every thread. Requires nbins % NT == 0.
+template <int NT>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t* lds,
+                                           int* digit, uint32_t* above) {
+  const int per = nbins / NT;
+  // thread t owns the per bins [nbins-(t+1)*per, nbins-t*per): thread 0 the top ones
+  const int hi = nbins - threadIdx.x * per;  // exclusive
+  uint32_t sum = 0;
+  for (int b = hi - 1; b >= hi - per; --b) sum += hist[b];
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan<NT>(sum, lds, &total);
+  if (threadIdx.x == 0) {
+    lds[NT / kWave + 1] = 0;
+    lds[NT / kWave + 2] = 0;
+  }
+  __syncthreads();
+  if (before < k && before + sum >= k) {
+    uint32_t acc = before;
+    for (int b = hi - 1; b >= hi - per; --b) {
+      const uint32_t c = hist[b];
+      if (acc + c >= k) {
+        lds[NT / kWave + 1] = (uint32_t)b;
+        lds[NT / kWave + 2] = acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  *digit = (int)lds[NT / kWave + 1];
+  *above = lds[NT / kWave + 2];
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate (v_mfma_f32_16x16x32_bf16).
+// Lane l supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16], and holds
+// D[4*(l/16) + i][l%16] for i = 0..3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  c, 0, 0, 0);
+}
+
+// Raise a kernel's dynamic LDS limit when a launch needs more than 64 KiB (gfx950
+// has 160 KiB per CU). Host side.
+inline hipError_t allow_smem(const void* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace herald

@@ -1,0 +1,99 @@
+// Fetch the selected subset into the sparse KV pool, once per block (HERALD
+// abstract on the mlsift "KV cache offloading" listing: only a small critical
+// subset is fetched; HERALD v3 abstract: the final top-K subset).
+//
+// Pool layout: K rows as they are in the cache ([nseq][Hkv][topk][d]); V stored
+// d-major ([nseq][Hkv][d][ldv], ldv = topk rounded up to 64, padding zero) so the
+// attention kernel can load V^T tiles, the left operand of its P.V product, with
+// plain 16-byte loads. A bit-exact byte copy; HBM-bound.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace herald {
+
+// One workgroup per 64 picks of one (sequence, KV head). PACKED selects where row i
+// of the group comes from: the cache by index (device path) or packed
+// [nseq][Hkv][topk][D] buffers (host-pool path, after their copy to the device).
+template <typename T, int D, bool PACKED>
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                     const int32_t* __restrict__ idx,
+                                                     const int64_t* __restrict__ seq_start, int Hkv, int topk,
+                                                     int64_t ldv, T* __restrict__ k_sel, T* __restrict__ v_sel) {
+  constexpr int EPL = Vec16<T>::N;
+  constexpr int CPR = D / EPL;  // 16-byte chunks per row
+  constexpr int LDT = D + EPL;  // padded LDS row (elements)
+  __shared__ __align__(16) T tile[64 * LDT];
+  const int blk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int i0 = blk * 64;
+  const int64_t unit = (int64_t)s * Hkv + g;
+  const int64_t j0 = PACKED ? 0 : seq_start[s];
+
+  auto src_row = [&](const T* base, int i) -> const T* {
+    if (PACKED) return base + (unit * topk + i) * D;
+    return base + ((j0 + idx[unit * topk + i]) * Hkv + g) * D;
+  };
+
+  // K: straight row copy
+  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, ch = c % CPR;
+    const int i = i0 + r;
+    if (i < topk) st16(k_sel + (unit * topk + i) * D + ch * EPL, ld16(src_row(k, i) + ch * EPL));
+  }
+  // V: rows into LDS, then out d-major
+  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, ch = c % CPR;
+    const int i = i0 + r;
+    const uint4 val = i < topk ? ld16(src_row(v, i) + ch * EPL) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&tile[r * LDT + ch * EPL]) = val;
+  }
+  __syncthreads();
+  // each 16-byte output chunk holds EPL consecutive picks of one dimension
+  constexpr int KCH = 64 / EPL;  // chunks per dimension row within this block
+  T* vout = v_sel + unit * D * ldv;
+  for (int c = threadIdx.x; c < D * KCH; c += 256) {
+    const int e = c / KCH, kc = c % KCH;
+    union {
+      T t[EPL];
+      uint4 u;
+    } pk;
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) pk.t[t] = tile[(kc * EPL + t) * LDT + e];
+    st16(vout + (int64_t)e * ldv + i0 + kc * EPL, pk.u);
+  }
+}
+
+template <bool PACKED>
+static hipError_t gather_dispatch(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel,
+                                  void* v_sel, hipStream_t st) {
+  dim3 grid((s.topk + 63) / 64, s.Hkv, s.nseq);
+  const int64_t ldv = vsel_ld(s.topk);
+  if (s.bf16) {
+    if (s.D == 128)
+      gather_kernel<bf16, 128, PACKED><<<grid, 256, 0, st>>>((const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
+                                                             s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel);
+    else
+      gather_kernel<bf16, 64, PACKED><<<grid, 256, 0, st>>>((const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
+                                                            s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel);
+  } else {
+    if (s.D == 128)
+      gather_kernel<float, 128, PACKED><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, idx, s.seq_start,
+                                                              s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel);
+    else
+      gather_kernel<float, 64, PACKED><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, idx, s.seq_start,
+                                                             s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
+                         hipStream_t st) {
+  return gather_dispatch<false>(s, k, v, idx, k_sel, v_sel, st);
+}
+
+// Host-pool path: `packed_k` / `packed_v` hold the picked rows as [nseq][Hkv][topk][D].
+hipError_t launch_layout_packed(const Shape& s, const void* packed_k, const void* packed_v, void* k_sel, void* v_sel,
+                                hipStream_t st) {
+  return gather_dispatch<true>(s, packed_k, packed_v, nullptr, k_sel, v_sel, st);
+}
+
+}  // namespace herald

@@ -1,0 +1,83 @@
+// Internal launch interface between the C ABI layer (abi.cpp) and the kernels.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace herald {
+
+// Tokens one scan workgroup covers, and tokens one score / radix workgroup covers.
+constexpr int kScanTok = 256;
+constexpr int kScoreTok = 4096;
+constexpr int kRadixBins = 2048;
+// Candidates one refine workgroup covers (bf16 MFMA path).
+constexpr int kRefineTile = 256;
+// Keys per attention block and the largest supported candidate count.
+constexpr int kAttnKeyBlock = 64;
+constexpr int kMaxCandidates = 16384;
+
+struct Shape {
+  int nseq, B, Hq, Hkv, D, G, C, topk;
+  int bf16;        // 1: bf16 tensors, 0: fp32
+  float scale;     // softmax scale (already resolved)
+  int64_t total;   // sum of the sequence lengths
+  int64_t max_len; // longest sequence
+  const int64_t* seq_start;  // device
+};
+
+struct SelectWs {
+  float* qbar;       // [nseq][Hq][D] merged query * scale * log2(e)
+  float* logits;     // [Hq][total] base-2 logits of the merged query
+  float2* partials;  // [nseq][Hq][nchunk] (max, sum 2^(x-max)) per scan chunk
+  float* scores;     // [Hkv][total] selection score S
+  uint32_t* hist;    // [nseq][Hkv][3][kRadixBins]
+  uint64_t* bits;    // [nseq][Hkv][2][nwords] (above-prefix, equal-prefix) bitmaps
+  int nchunk;        // scan chunks per sequence (max over sequences)
+  int nwords;        // bitmap words per (sequence, KV head)
+};
+
+struct RefineWs {
+  float2* row_stats;  // [nseq][Hkv][ntile][rows] (max, sum) per refine tile
+  float* rscore;      // [nseq][Hkv][C]
+  int ntile;
+};
+
+struct AttnWs {
+  float* o_part;   // [nseq][Hkv][nsplit][rows][D] unnormalised partial outputs
+  float2* ml;      // [nseq][Hkv][nsplit][rows] (max, sum)
+  int nsplit;
+  int keys_per_split;  // multiple of kAttnKeyBlock
+};
+
+// select
+hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);
+hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st);
+hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st);
+hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipStream_t st);
+hipError_t launch_emit_candidates(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score,
+                                  hipStream_t st);
+// refine
+hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, const int32_t* cand,
+                               const RefineWs& ws, hipStream_t st);
+hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, const int32_t* cand,
+                                const RefineWs& ws, hipStream_t st);
+hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
+                             hipStream_t st);
+hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
+                                float* topk_score, hipStream_t st);
+// gather
+hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
+                         hipStream_t st);
+hipError_t launch_layout_packed(const Shape& s, const void* packed_k, const void* packed_v, void* k_sel, void* v_sel,
+                                hipStream_t st);
+// attention
+int attn_splits(const Shape& s, int* keys_per_split);
+int attn_rpad(const Shape& s);
+hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void* vb, const void* k_sel,
+                       const void* v_sel, void* out, const AttnWs& ws, hipStream_t st);
+hipError_t launch_attn_combine(const Shape& s, const AttnWs& ws, void* out, hipStream_t st);
+
+inline int64_t vsel_ld(int topk) { return ((int64_t)topk + 63) / 64 * 64; }
+
+}  // namespace herald

@@ -1,0 +1,371 @@
+// Stage two of the two-stage selection: refine the C candidates with the B real
+// queries into the final top-K subset (HERALD, arXiv 2606.21633 v3, abstract).
+//
+// Refine score of candidate c of KV head g (the per-row softmax is over the C
+// candidates only, summed over the B queries and the G heads of the group):
+//   R_g[c] = sum_{b, h in g} 2^(x[b,h,c] - M[b,h]) / Z[b,h],
+//   x = scale * log2(e) * <q[b][h], K[cand_c][g]>.
+//
+// bf16 path, two launches over the same (sequence, KV head, 256-candidate tile)
+// grid; both compute x with identical MFMA code, so the logits agree bit for bit:
+//   refine_stats_kernel   per row (b,h): (max, sum 2^(x-max)) over the tile.
+//   refine_scores_kernel  per row: normalisers from all tiles; per candidate: the
+//                         sum over rows, in a fixed order.
+// Each wave owns 64 candidates (four 16-candidate MFMA tiles). The candidate key
+// rows are the A operand, loaded once from the cache by index into registers;
+// the group's B*G query rows sit in LDS and are the B operand
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// fp32 path: refine_f32_kernel, one workgroup per (sequence, KV head).
+// refine_select_kernel: exact top-K of R in LDS (three radix digits on the fp32
+// bit pattern, R >= 0), ties to the lower cache index, ascending output.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace herald {
+
+template <int D>
+__device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[4][D / 32], const bf16* qs, int ldq, int rt,
+                                                   int lane, f32x4_t (&acc)[4]) {
+  uint4 bq[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    bq[ks] = *reinterpret_cast<const uint4*>(qs + (rt * 16 + (lane & 15)) * ldq + ks * 32 + (lane >> 4) * 8);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) acc[mt] = mfma16x16x32(a[mt][ks], bq[ks], acc[mt]);
+  }
+}
+
+// Shared prologue of both refine kernels: stage the group's query rows in LDS and
+// load this wave's 64 candidate key rows into registers.
+template <int D>
+__device__ __forceinline__ void refine_prologue(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                const int32_t* __restrict__ cand, int64_t j0, int s, int g, int B,
+                                                int Hq, int Hkv, int G, int C, int R, int RT, int cbase, bf16* qs,
+                                                int ldq, uint4 (&a)[4][D / 32]) {
+  const int lane = threadIdx.x & 63;
+  // query rows r = b*G + hh -> q[s][b][g*G+hh][:]; rows past R are zero
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  for (int c = threadIdx.x; c < RT * 16 * CPR; c += 256) {
+    const int r = c / CPR, ch = c % CPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R) {
+      const int b = r / G, hh = r % G;
+      v = ld16(q + (((int64_t)s * B + b) * Hq + g * G + hh) * D + ch * 8);
+    }
+    *reinterpret_cast<uint4*>(qs + r * ldq + ch * 8) = v;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int c = cbase + mt * 16 + (lane & 15);
+    const bf16* row = nullptr;
+    if (c < C) row = k + ((j0 + cand[((int64_t)s * Hkv + g) * C + c]) * Hkv + g) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      a[mt][ks] = row ? ld16(row + ks * 32 + (lane >> 4) * 8) : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void refine_stats_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                           const int32_t* __restrict__ cand,
+                                                           const int64_t* __restrict__ seq_start, int B, int Hq,
+                                                           int Hkv, int G, int C, float scale2, int ntile,
+                                                           float2* __restrict__ row_stats) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G, RT = (R + 15) / 16, ldq = D + 8;
+  bf16* qs = reinterpret_cast<bf16*>(smem);
+  float2* wstat = reinterpret_cast<float2*>(smem + RT * 16 * ldq * sizeof(bf16));  // [4][RT*16]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cbase = tile * kRefineTile + w * 64;
+  uint4 a[4][D / 32];
+  refine_prologue<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, cbase, qs, ldq, a);
+
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4_t acc[4];
+    refine_tile_logits<D>(a, qs, ldq, rt, lane, acc);
+    float x[4][4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = cbase + mt * 16 + (lane >> 4) * 4 + i;
+        x[mt][i] = c < C ? acc[mt][i] * scale2 : -INFINITY;
+        m = fmaxf(m, x[mt][i]);
+      }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float l = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l += fast_exp2(x[mt][i] - m);
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (lane < 16) wstat[w * RT * 16 + rt * 16 + lane] = make_float2(m, l);
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += 256) {
+    float M = -INFINITY, Z = 0.f;
+    for (int ww = 0; ww < 4; ++ww) {
+      const float2 p = wstat[ww * RT * 16 + r];
+      ms_merge(M, Z, p.x, p.y);
+    }
+    row_stats[(((int64_t)s * Hkv + g) * ntile + tile) * R + r] = make_float2(M, Z);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void refine_scores_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                            const int32_t* __restrict__ cand,
+                                                            const int64_t* __restrict__ seq_start, int B, int Hq,
+                                                            int Hkv, int G, int C, float scale2, int ntile,
+                                                            const float2* __restrict__ row_stats,
+                                                            float* __restrict__ rscore) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G, RT = (R + 15) / 16, ldq = D + 8;
+  bf16* qs = reinterpret_cast<bf16*>(smem);
+  float* rowM = reinterpret_cast<float*>(smem + RT * 16 * ldq * sizeof(bf16));  // [RT*16]
+  float* rowIZ = rowM + RT * 16;                                                // [RT*16]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cbase = tile * kRefineTile + w * 64;
+  for (int r = threadIdx.x; r < RT * 16; r += 256) {
+    float M = -INFINITY, Z = 0.f;
+    if (r < R)
+      for (int t = 0; t < ntile; ++t) {
+        const float2 p = row_stats[(((int64_t)s * Hkv + g) * ntile + t) * R + r];
+        ms_merge(M, Z, p.x, p.y);
+      }
+    rowM[r] = M;
+    rowIZ[r] = r < R ? 1.f / Z : 0.f;
+  }
+  uint4 a[4][D / 32];
+  refine_prologue<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, cbase, qs, ldq, a);
+
+  float rs[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[mt][i] = 0.f;
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4_t acc[4];
+    refine_tile_logits<D>(a, qs, ldq, rt, lane, acc);
+    const int r = rt * 16 + (lane & 15);
+    const float M = rowM[r], iz = rowIZ[r];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = r < R ? fast_exp2(acc[mt][i] * scale2 - M) * iz : 0.f;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o);
+        rs[mt][i] += p;
+      }
+  }
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = cbase + mt * 16 + (lane >> 4) * 4 + i;
+        if (c < C) rscore[((int64_t)s * Hkv + g) * C + c] = rs[mt][i];
+      }
+  }
+}
+
+// fp32 path: one workgroup per (sequence, KV head); rows first, then candidates.
+template <int D>
+__device__ __forceinline__ float dot_rows_f32(const float* __restrict__ a, const float* __restrict__ b) {
+  float acc = 0.f;
+#pragma unroll 8
+  for (int e = 0; e < D; ++e) acc = fmaf(a[e], b[e], acc);
+  return acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void refine_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                         const int32_t* __restrict__ cand,
+                                                         const int64_t* __restrict__ seq_start, int B, int Hq,
+                                                         int Hkv, int G, int C, float scale2,
+                                                         float* __restrict__ rscore) {
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int R = B * G;
+  const int64_t j0 = seq_start[s];
+  __shared__ float rowM[256], rowIZ[256];
+  const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
+  auto qrow = [&](int r) { return q + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D; };
+  auto krow = [&](int c) { return k + ((j0 + cd[c]) * Hkv + g) * D; };
+  for (int r = threadIdx.x; r < R; r += 256) {
+    float m = -INFINITY, z = 0.f;
+    for (int c = 0; c < C; ++c) {
+      const float x = dot_rows_f32<D>(qrow(r), krow(c)) * scale2;
+      if (x > m) {
+        z = z * fast_exp2(m - x) + 1.f;
+        m = x;
+      } else {
+        z += fast_exp2(x - m);
+      }
+    }
+    rowM[r] = m;
+    rowIZ[r] = 1.f / z;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += 256) {
+    float acc = 0.f;
+    for (int r = 0; r < R; ++r) acc += fast_exp2(dot_rows_f32<D>(qrow(r), krow(c)) * scale2 - rowM[r]) * rowIZ[r];
+    rscore[((int64_t)s * Hkv + g) * C + c] = acc;
+  }
+}
+
+// Exact top-K of the refine scores of one (sequence, KV head), in LDS.
+__global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __restrict__ cand,
+                                                            const float* __restrict__ rscore, int Hkv, int C,
+                                                            int topk, int32_t* __restrict__ topk_idx,
+                                                            float* __restrict__ topk_score) {
+  const int g = blockIdx.x, s = blockIdx.y;
+  extern __shared__ uint32_t u[];  // [C]
+  __shared__ uint32_t h[kRadixBins];
+  __shared__ uint32_t lds[32];
+  const int64_t base = ((int64_t)s * Hkv + g) * C;
+  for (int c = threadIdx.x; c < C; c += 1024) u[c] = __float_as_uint(rscore[base + c]);
+
+  uint32_t want = (uint32_t)topk;
+  uint32_t prefix = 0;  // digits found so far
+  int shift[3] = {21, 10, 0};
+  int width[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int i = threadIdx.x; i < kRadixBins; i += 1024) h[i] = 0u;
+    __syncthreads();
+    const int hi_shift = shift[pass] + width[pass];
+    const uint32_t mask = (1u << width[pass]) - 1u;
+    for (int c = threadIdx.x; c < C; c += 1024) {
+      const uint32_t v = u[c];
+      const bool match = pass == 0 || (v >> hi_shift) == prefix;
+      if (match) atomicAdd(&h[(v >> shift[pass]) & mask], 1u);
+    }
+    __syncthreads();
+    int d;
+    uint32_t above;
+    find_digit<1024>(h, kRadixBins, want, lds, &d, &above);
+    want -= above;
+    prefix = (prefix << width[pass]) | (uint32_t)d;
+  }
+  const uint32_t thr = prefix;  // bit pattern of the topk-th largest score
+  const uint32_t ties_wanted = want;
+
+  const int cpt = (C + 1023) / 1024;
+  const int c0 = threadIdx.x * cpt, c1 = min(C, c0 + cpt);
+  uint32_t my_ties = 0;
+  for (int c = c0; c < c1; ++c) my_ties += u[c] == thr;
+  uint32_t tot;
+  uint32_t tie_rank = block_exclusive_scan<1024>(my_ties, lds, &tot);
+  // count selected with the tie quota, in candidate (= cache index) order
+  uint32_t my_sel = 0;
+  {
+    uint32_t tr = tie_rank;
+    for (int c = c0; c < c1; ++c) {
+      if (u[c] > thr) ++my_sel;
+      else if (u[c] == thr) {
+        if (tr < ties_wanted) ++my_sel;
+        ++tr;
+      }
+    }
+  }
+  uint32_t pos = block_exclusive_scan<1024>(my_sel, lds, &tot);
+  const int32_t* cd = cand + base;
+  int32_t* out = topk_idx + ((int64_t)s * Hkv + g) * topk;
+  float* outs = topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr;
+  uint32_t tr = tie_rank;
+  for (int c = c0; c < c1; ++c) {
+    bool take = false;
+    if (u[c] > thr) take = true;
+    else if (u[c] == thr) {
+      take = tr < ties_wanted;
+      ++tr;
+    }
+    if (take) {
+      if (pos < (uint32_t)topk) {
+        out[pos] = cd[c];
+        if (outs) outs[pos] = __uint_as_float(u[c]);
+      }
+      ++pos;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+static size_t refine_smem(const Shape& s, bool stats) {
+  const int RT = (s.B * s.G + 15) / 16;
+  const size_t q = (size_t)RT * 16 * (s.D + 8) * sizeof(bf16);
+  return q + (stats ? (size_t)4 * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
+}
+
+hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
+                               hipStream_t st) {
+  dim3 grid(ws.ntile, s.Hkv, s.nseq);
+  const float scale2 = s.scale * kLog2e;
+  const size_t smem = refine_smem(s, true);
+  hipError_t e = allow_smem(s.D == 128 ? (const void*)refine_stats_kernel<128> : (const void*)refine_stats_kernel<64>,
+                            smem);
+  if (e != hipSuccess) return e;
+  if (s.D == 128)
+    refine_stats_kernel<128><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
+                                                      s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
+  else
+    refine_stats_kernel<64><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
+                                                     s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, const int32_t* cand,
+                                const RefineWs& ws, hipStream_t st) {
+  dim3 grid(ws.ntile, s.Hkv, s.nseq);
+  const float scale2 = s.scale * kLog2e;
+  const size_t smem = refine_smem(s, false);
+  hipError_t e = allow_smem(
+      s.D == 128 ? (const void*)refine_scores_kernel<128> : (const void*)refine_scores_kernel<64>, smem);
+  if (e != hipSuccess) return e;
+  if (s.D == 128)
+    refine_scores_kernel<128><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
+                                                       s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
+                                                       ws.rscore);
+  else
+    refine_scores_kernel<64><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
+                                                      s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
+                                                      ws.rscore);
+  return hipGetLastError();
+}
+
+hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
+                             hipStream_t st) {
+  dim3 grid(s.Hkv, s.nseq);
+  const float scale2 = s.scale * kLog2e;
+  if (s.D == 128)
+    refine_f32_kernel<128><<<grid, 256, 0, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
+                                                 s.Hkv, s.G, s.C, scale2, ws.rscore);
+  else
+    refine_f32_kernel<64><<<grid, 256, 0, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
+                                                s.Hkv, s.G, s.C, scale2, ws.rscore);
+  return hipGetLastError();
+}
+
+hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
+                                float* topk_score, hipStream_t st) {
+  const size_t smem = (size_t)s.C * sizeof(uint32_t);
+  hipError_t e = allow_smem((const void*)refine_select_kernel, smem);
+  if (e != hipSuccess) return e;
+  refine_select_kernel<<<dim3(s.Hkv, s.nseq), 1024, smem, st>>>(cand, ws.rscore, s.Hkv, s.C, s.topk, topk_idx,
+                                                                topk_score);
+  return hipGetLastError();
+}
+
+}  // namespace herald

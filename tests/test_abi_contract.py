@@ -1,0 +1,183 @@
+"""C-ABI contract on the CPU: the library loads, exports every declared symbol, and
+rejects every invalid argument with the documented status before any HIP call.
+No kernel is launched here (validation happens on the host first)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_diffusion_sparse_herald_amd import herald as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "herald.h")
+
+# a fake device address: validation never dereferences seq_start_dev or tensor pointers
+FAKE = 0x10000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(herald_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return H.load()
+
+
+def prob(**kw):
+    base = dict(seq_start=[0, 4096, 9000], B=32, Hq=8, Hkv=2, head_dim=128, C=512, topk=128, dtype=H.HERALD_BF16)
+    base.update(kw)
+    return H.make_problem(base.pop("seq_start"), seq_start_dev=FAKE, **base)
+
+
+def status_of(fn, *args):
+    with pytest.raises(H.HeraldError) as e:
+        fn(*args)
+    assert H.herald_last_error(), "error message must not be empty"
+    return e.value.status
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(H.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", H.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (herald_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_load_fails_loudly_when_missing():
+    saved = H._lib
+    H._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            H.load("/nonexistent/libherald.so")
+    finally:
+        H._lib = saved
+
+
+def test_workspace_sizes(lib):
+    p = prob()
+    for op in (H.HERALD_OP_SELECT, H.HERALD_OP_REFINE, H.HERALD_OP_GATHER_HOST):
+        assert H.herald_workspace_size(p, op) > 0
+    assert H.herald_workspace_size(p, H.HERALD_OP_ATTN) >= 0
+    big = prob(seq_start=[0, 8192, 20000])
+    assert H.herald_workspace_size(big, H.HERALD_OP_SELECT) > H.herald_workspace_size(p, H.HERALD_OP_SELECT)
+    assert H.herald_workspace_size(prob(seq_start=[0]), H.HERALD_OP_SELECT) == 0
+    assert status_of(H.herald_workspace_size, p, 99) == H.HERALD_ERR_INVALID_ARG
+
+
+def test_vsel_ld(lib):
+    assert H.herald_vsel_ld(1) == 64
+    assert H.herald_vsel_ld(64) == 64
+    assert H.herald_vsel_ld(65) == 128
+    assert H.herald_vsel_ld(1024) == 1024
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=9, Hkv=2), H.HERALD_ERR_INVALID_ARG),            # Hq % Hkv != 0
+    (dict(Hq=1, Hkv=2), H.HERALD_ERR_INVALID_ARG),            # Hq < Hkv
+    (dict(Hkv=0), H.HERALD_ERR_INVALID_ARG),
+    (dict(Hq=18, Hkv=2), H.HERALD_ERR_UNSUPPORTED),           # G = 9 > 8
+    (dict(B=64, Hq=16, Hkv=2), H.HERALD_ERR_UNSUPPORTED),     # B*G = 512 > 256
+    (dict(B=0), H.HERALD_ERR_INVALID_ARG),
+    (dict(B=65), H.HERALD_ERR_UNSUPPORTED),
+    (dict(head_dim=96), H.HERALD_ERR_UNSUPPORTED),
+    (dict(topk=513), H.HERALD_ERR_INVALID_ARG),               # topk > C
+    (dict(topk=0), H.HERALD_ERR_INVALID_ARG),
+    (dict(C=0, topk=0), H.HERALD_ERR_INVALID_ARG),
+    (dict(C=5000, topk=10), H.HERALD_ERR_INVALID_ARG),        # C > L_0 = 4096
+    (dict(C=20000, topk=10, seq_start=[0, 30000]), H.HERALD_ERR_UNSUPPORTED),  # C > 16384
+    (dict(dtype=7), H.HERALD_ERR_INVALID_ARG),
+    (dict(seq_start=[1, 5000]), H.HERALD_ERR_INVALID_ARG),    # seq_start[0] != 0
+    (dict(seq_start=[0, 5000, 4000]), H.HERALD_ERR_INVALID_ARG),  # negative length
+    (dict(softmax_scale=-1.0), H.HERALD_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), H.HERALD_ERR_INVALID_ARG),
+])
+def test_invalid_problem(lib, kw, status):
+    p = prob(**kw)
+    assert status_of(H.herald_workspace_size, p, H.HERALD_OP_SELECT) == status
+    assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
+    assert status_of(H.herald_refine_topk, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
+    assert status_of(H.herald_block_attn, p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == status
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, None, 0, 0, None) == status
+
+
+def test_negative_nseq_and_reserved(lib):
+    p = prob()
+    p.c.nseq = -1
+    assert status_of(H.herald_workspace_size, p, H.HERALD_OP_SELECT) == H.HERALD_ERR_INVALID_ARG
+    p = prob()
+    p.c.reserved = 1
+    assert status_of(H.herald_workspace_size, p, H.HERALD_OP_SELECT) == H.HERALD_ERR_INVALID_ARG
+    p = prob()
+    p.c.seq_start_dev = None
+    assert status_of(H.herald_workspace_size, p, H.HERALD_OP_SELECT) == H.HERALD_ERR_INVALID_ARG
+    with pytest.raises(H.HeraldError):
+        H._check(H.load().herald_workspace_size(None, 0, ctypes.byref(ctypes.c_size_t())), "x")
+
+
+def test_pointer_checks(lib):
+    p = prob()
+    ws = H.herald_workspace_size(p, H.HERALD_OP_SELECT)
+    # NULL and misaligned operands
+    assert status_of(H.herald_select_merged, p, None, FAKE, FAKE, None, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_merged, p, FAKE + 8, FAKE, FAKE, None, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, FAKE + 4, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
+    # workspace too small / missing
+    assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, FAKE, ws - 1, 0) == H.HERALD_ERR_WORKSPACE
+    assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, None, ws, 0) == H.HERALD_ERR_WORKSPACE
+    rws = H.herald_workspace_size(p, H.HERALD_OP_REFINE)
+    assert status_of(H.herald_refine_topk, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, rws - 1, 0) == H.HERALD_ERR_WORKSPACE
+    assert status_of(H.herald_refine_topk, p, FAKE, FAKE, None, FAKE, None, FAKE, rws, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_block_attn, p, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0) == \
+        H.HERALD_ERR_INVALID_ARG
+    # gather: bad flag, host path without staging / event / workspace
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, None, None, 0, 0, None) == \
+        H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, 0, FAKE) == \
+        H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 0, None) == \
+        H.HERALD_ERR_INVALID_ARG
+    gws = H.herald_workspace_size(p, H.HERALD_OP_GATHER_HOST)
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gws - 1, 0, FAKE) == \
+        H.HERALD_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop(lib):
+    p = prob(seq_start=[0])
+    H.herald_select_merged(p, None, None, None, None, None, 0, 0)
+    H.herald_refine_topk(p, None, None, None, None, None, None, 0, 0)
+    H.herald_gather_kv(p, None, None, 0, None, None, None, None, None, None, 0, 0, None)
+    H.herald_block_attn(p, None, None, None, None, None, None, None, 0, 0)
+    assert H.herald_last_error() == ""
+
+
+def test_kernel_events_argument_checks(lib):
+    assert status_of(H.herald_set_kernel_events, 10, None, None) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_set_kernel_events, -1, None, None) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_set_kernel_events, 0, FAKE, None) == H.HERALD_ERR_INVALID_ARG
+    H.herald_set_kernel_events(0, None, None)
+
+
+def test_attn_splits_reported(lib):
+    assert H.herald_attn_splits(prob()) >= 1
+    assert H.herald_attn_splits(prob(dtype=H.HERALD_F32)) == 1
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "block_diffusion_sparse_herald_amd")
+    pat = re.compile(r"^\s*(import\s+oracle|from\s+oracle|from\s+\.+\s*import\s+oracle)|herald_oracle|#include.*oracle",
+                     re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), f

@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Stage by stage, on seeded inputs that span several tiles and ragged tails:
+  P1 candidates: band test against the oracle selection scores;
+  P2 final subset: band test against the oracle refine scores, both with the
+     oracle's candidates fed to the GPU (stage-isolated) and with the GPU's own
+     candidates (end to end);
+  P3 gather: bit-exact;
+  P4 attention: oracle attention on the GPU's own subset, max abs error within
+     2e-2 (bf16) / 1e-4 (fp32);
+  P5 planted keys are selected; P6 strict ties; P7 bit-identical reruns.
+Full-size workloads run in the launch configuration the benchmark times and are
+checked on sampled sequences and steps.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.herald_oracle as orc
+from block_diffusion_sparse_herald_amd import herald as H
+from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, Workload, bf16_bits_to_f32, make_batch
+from block_diffusion_sparse_herald_amd.runner import BlockRunner, batch_to_device, device_tensor
+from parity import ATOL, band_check, max_abs
+
+pytestmark = pytest.mark.gpu
+
+BASE = WORKLOADS["gqa32x8_L32768_b1"]
+SMALL = {
+    "tiny_f32_L4096": WORKLOADS["tiny_f32_L4096"],
+    "gqa32x8_L5000_b2": BASE.with_(name="gqa32x8_L5000_b2", L=5000, nseq=2, C=1000, topk=300, T=2),
+    "drift_L9000": WORKLOADS["gqa32x8_L131072_b4_drift"].with_(name="drift_L9000", L=9000, nseq=1, C=2048,
+                                                                topk=700, T=2),
+    "ragged_g7_L1500-6000": WORKLOADS["gqa28x4_ragged16k-64k_b8"].with_(name="ragged_g7", L=6000, L_min=1500,
+                                                                        nseq=3, C=1024, topk=333, T=2),
+    "bf16_d64_g4": Workload("bf16_d64_g4", nseq=2, L=3000, Hq=8, Hkv=2, d=64, dtype="bf16", B=16, C=600, topk=130,
+                            T=2, planted=8, seed_base=7100),
+    "f32_d128_g2": Workload("f32_d128_g2", nseq=2, L=2100, Hq=4, Hkv=2, d=128, dtype="f32", B=8, C=300, topk=77,
+                            T=2, planted=4, seed_base=7200),
+    "g1_b1": Workload("g1_b1", nseq=2, L=2500, Hq=2, Hkv=2, d=128, dtype="bf16", B=1, C=700, topk=64, T=2,
+                      seed_base=7300),
+    "g8_b32": Workload("g8_b32", nseq=1, L=4000, Hq=16, Hkv=2, d=128, dtype="bf16", B=32, C=512, topk=200, T=2,
+                       planted=8, seed_base=7400),
+    "select_all": Workload("select_all", nseq=2, L=700, Hq=4, Hkv=1, d=128, dtype="bf16", B=4, C=700, topk=700,
+                           T=1, seed_base=7500),
+    "topk1": Workload("topk1", nseq=1, L=1000, Hq=4, Hkv=2, d=64, dtype="bf16", B=2, C=1, topk=1, T=1,
+                      seed_base=7600),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    return (bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class Run:
+    """One batch on the GPU: all per-block outputs, attention for the requested steps."""
+
+    def __init__(self, wl: Workload, steps=None):
+        self.wl = wl
+        self.batch = make_batch(wl)
+        self.dev = batch_to_device(self.batch)
+        self.runner = BlockRunner(self.batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
+        r, d = self.runner, self.dev
+        self.steps = list(range(wl.T)) if steps is None else steps
+        r.select(d["q0"], d["k_cache"])
+        r.refine(d["q0"], d["k_cache"])
+        r.gather(d["k_cache"], d["v_cache"])
+        self.outs = {}
+        for t in self.steps:
+            out = torch.empty_like(r.out)
+            r.attn(d["q_steps"][t], d["kb_steps"][t], d["vb_steps"][t], out=out)
+            self.outs[t] = out
+        torch.cuda.synchronize()
+        self.cand = to_np(r.cand).astype(np.int64)
+        self.cand_score = to_np(r.cand_score)
+        self.sel = to_np(r.sel).astype(np.int64)
+        self.sel_score = to_np(r.sel_score)
+        self.k_sel = to_np(r.k_sel)
+        self.v_sel = to_np(r.v_sel)
+        self.out = {t: to_np(o) for t, o in self.outs.items()}
+
+    def seq(self, s):
+        b = self.batch
+        a, e = int(b.seq_start[s]), int(b.seq_start[s + 1])
+        return widen(b.q0[s]), widen(b.k_cache[a:e]), widen(b.v_cache[a:e])
+
+
+def check_sequence(run: Run, s: int, steps, stage_isolated: bool = True):
+    wl = run.wl
+    scale = orc.default_scale(wl.d)
+    q0, k, v = run.seq(s)
+    cand_o, S = orc.select_merged(q0, k, wl.C, scale)
+    band = 0
+    for g in range(wl.Hkv):
+        band += band_check(run.cand[s, g], S[g], wl.C, what=f"{wl.name} s{s} g{g} candidates")
+        got = run.cand_score[s, g]
+        want = S[g][run.cand[s, g]]
+        np.testing.assert_allclose(got, want, rtol=1e-4, atol=1e-30, err_msg=f"{wl.name} s{s} g{g} scores")
+    # end to end: oracle refine on the GPU's candidates
+    R_e2e = orc.refine_scores(q0, k, run.cand[s], scale)
+    for g in range(wl.Hkv):
+        band_check(run.sel[s, g], R_e2e[g], wl.topk, domain=run.cand[s, g], what=f"{wl.name} s{s} g{g} refine e2e")
+        np.testing.assert_allclose(run.sel_score[s, g], R_e2e[g][np.searchsorted(run.cand[s, g], run.sel[s, g])],
+                                   rtol=1e-4, atol=1e-30)
+    # planted keys
+    if wl.planted:
+        for g in range(wl.Hkv):
+            planted = set(run.batch.planted[s][g].tolist())
+            assert planted <= set(run.cand[s, g].tolist()), f"{wl.name} s{s} g{g}: planted key not a candidate"
+            assert planted <= set(run.sel[s, g].tolist()), f"{wl.name} s{s} g{g}: planted key not selected"
+    # gather: bit-exact
+    a = int(run.batch.seq_start[s])
+    ldv = run.v_sel.shape[-1]
+    for g in range(wl.Hkv):
+        rows = run.batch.k_cache[a + run.sel[s, g], g, :]
+        assert np.array_equal(run.k_sel[s, g], rows), f"{wl.name} s{s} g{g}: k_sel differs"
+        vrows = run.batch.v_cache[a + run.sel[s, g], g, :]
+        assert np.array_equal(run.v_sel[s, g, :, :wl.topk], vrows.T), f"{wl.name} s{s} g{g}: v_sel differs"
+        assert not run.v_sel[s, g, :, wl.topk:ldv].any(), "v_sel padding must be zero"
+    # attention on the GPU's own subset
+    ks, vs = orc.gather_kv(k, v, run.sel[s])
+    worst = 0.0
+    for t in steps:
+        want = orc.block_attention(widen(run.batch.q_steps[t, s]), widen(run.batch.kb_steps[t, s]),
+                                   widen(run.batch.vb_steps[t, s]), ks, vs, scale)
+        err = max_abs(widen(run.out[t][s]), want)
+        worst = max(worst, err)
+        assert err <= ATOL[wl.dtype], f"{wl.name} s{s} t{t}: attention max abs error {err}"
+    log(f"  {wl.name} s{s}: band {band}, attention max abs err {worst:.3g}")
+    return cand_o
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(gpu_lib):
+    yield
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workload_parity(name):
+    wl = SMALL[name]
+    log(f"[parity] {name}: {wl}")
+    run = Run(wl)
+    for s in range(wl.nseq):
+        cand_o = check_sequence(run, s, run.steps)
+        # stage-isolated refine: the oracle's candidates through the GPU refine
+        if s == 0:
+            cand_dev = torch.from_numpy(np.stack([cand_o if i == 0 else run.cand[i] for i in range(wl.nseq)])
+                                        .astype(np.int32)).cuda()
+            r = run.runner
+            r.refine(run.dev["q0"], run.dev["k_cache"], cand=cand_dev)
+            torch.cuda.synchronize()
+            sel = to_np(r.sel).astype(np.int64)
+            q0, k, _ = run.seq(0)
+            R = orc.refine_scores(q0, k, cand_o, orc.default_scale(wl.d))
+            for g in range(wl.Hkv):
+                band_check(sel[0, g], R[g], wl.topk, domain=cand_o[g], what=f"{name} refine stage-isolated g{g}")
+    if name == "select_all":
+        assert (run.cand == np.arange(wl.C)).all() and (run.sel == np.arange(wl.C)).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strict_ties(dtype):
+    """All keys identical within each KV head: candidates are [0, C) and the subset [0, topk)."""
+    wl = Workload("ties", nseq=2, L=3000, Hq=8, Hkv=2, d=128 if dtype == "bf16" else 64, dtype=dtype, B=8, C=700,
+                  topk=150, T=1, seed_base=7700)
+    batch = make_batch(wl)
+    batch.k_cache[:] = batch.k_cache[:1]
+    dev = batch_to_device(batch)
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, dtype)
+    r.select(dev["q0"], dev["k_cache"])
+    r.refine(dev["q0"], dev["k_cache"])
+    torch.cuda.synchronize()
+    assert (to_np(r.cand) == np.arange(wl.C)).all()
+    assert (to_np(r.sel) == np.arange(wl.topk)).all()
+
+
+def test_rerun_is_bit_identical():
+    wl = SMALL["gqa32x8_L5000_b2"]
+    a, b = Run(wl), Run(wl)
+    assert np.array_equal(a.cand, b.cand) and np.array_equal(a.cand_score.view(np.uint32), b.cand_score.view(np.uint32))
+    assert np.array_equal(a.sel, b.sel) and np.array_equal(a.sel_score.view(np.uint32), b.sel_score.view(np.uint32))
+    for t in a.out:
+        assert np.array_equal(a.out[t], b.out[t])
+
+
+def test_host_pool_gather_matches_device_gather():
+    wl = SMALL["ragged_g7_L1500-6000"]
+    run = Run(wl, steps=[])
+    r = run.runner
+    kh = torch.empty(run.dev["k_cache"].shape, dtype=run.dev["k_cache"].dtype, pin_memory=True)
+    vh = torch.empty(run.dev["v_cache"].shape, dtype=run.dev["v_cache"].dtype, pin_memory=True)
+    kh.copy_(run.dev["k_cache"].cpu())
+    vh.copy_(run.dev["v_cache"].cpu())
+    n = wl.nseq * wl.Hkv * wl.topk
+    staging = torch.empty(2 * n * wl.d, dtype=kh.dtype, pin_memory=True)
+    host_idx = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    ws = torch.empty(H.herald_workspace_size(r.problem, H.HERALD_OP_GATHER_HOST), dtype=torch.uint8, device="cuda")
+    k_sel = torch.zeros_like(r.k_sel)
+    v_sel = torch.full_like(r.v_sel, 7.0)
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    done.record(side)  # creates the event
+    side.wait_stream(torch.cuda.current_stream())
+    H.herald_gather_kv(r.problem, kh, vh, 1, r.sel, k_sel, v_sel, staging, host_idx, ws, stream=side, done=done)
+    torch.cuda.current_stream().wait_event(done)
+    torch.cuda.synchronize()
+    assert torch.equal(k_sel.view(torch.int16), r.k_sel.view(torch.int16))
+    assert torch.equal(v_sel.view(torch.int16), r.v_sel.view(torch.int16))
+
+
+def test_kernel_events_time_the_scan():
+    wl = SMALL["gqa32x8_L5000_b2"]
+    batch = make_batch(wl)
+    dev = batch_to_device(batch)
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
+    st, sp = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    sp.record()
+    H.herald_set_kernel_events("scan", st, sp)
+    try:
+        r.select(dev["q0"], dev["k_cache"])
+    finally:
+        H.herald_set_kernel_events("scan", None, None)
+    torch.cuda.synchronize()
+    assert st.elapsed_time(sp) > 0
+
+
+FULL = ["tiny_f32_L4096", "gqa32x8_L32768_b1", "gqa32x8_L32768_b16", "gqa32x8_L131072_b4_drift",
+        "gqa28x4_ragged16k-64k_b8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """Full-size workload, bench launch configuration; oracle on the first and last sequence and step."""
+    wl = WORKLOADS[name]
+    log(f"[full] {name}: generating")
+    steps = sorted({0, wl.T - 1})
+    run = Run(wl, steps=steps)
+    seqs = sorted({0, wl.nseq - 1})
+    if name == "gqa28x4_ragged16k-64k_b8":
+        L = run.batch.lengths
+        seqs = sorted({int(np.argmin(L)), int(np.argmax(L))})
+    for s in seqs:
+        log(f"[full] {name}: oracle on sequence {s}")
+        check_sequence(run, s, steps)
+    del run
+    torch.cuda.empty_cache()
