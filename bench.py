@@ -89,6 +89,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="gqa32x8_L32768_b1")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every step directly instead of replaying graphs")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the per-block path needs no "
@@ -96,40 +97,63 @@ def main(argv=None):
         return 2
 
     import numpy as np
-    import torch
 
     from block_diffusion_sparse_herald_amd import herald as H
+    from block_diffusion_sparse_herald_amd.hiprt import DevArray, Hip
     from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, make_batch
-    from block_diffusion_sparse_herald_amd.runner import BlockRunner, batch_to_device, device_tensor
+    from block_diffusion_sparse_herald_amd.runner import BlockRunner
 
+    # Device memory, streams, events and graphs come straight from the HIP runtime the
+    # library links (no PyTorch in this process).
+    hip = Hip()
     H.load()
     wl = WORKLOADS[args.workload]
     log(f"[bench] workload {wl.name}: generating inputs")
     batch = make_batch(wl)
-    dev = batch_to_device(batch)
-    cache_bytes = 2 * dev["k_cache"].numel() * dev["k_cache"].element_size()
+    dev = {n: DevArray.from_host(hip, getattr(batch, n))
+           for n in ["q0", "k_cache", "v_cache", "q_steps", "kb_steps", "vb_steps"]}
+    cache_bytes = dev["k_cache"].nbytes + dev["v_cache"].nbytes
     replicas = max(1, math.ceil(512 * 2**20 / cache_bytes))
     kv = [(dev["k_cache"], dev["v_cache"])] + [(dev["k_cache"].clone(), dev["v_cache"].clone())
                                               for _ in range(replicas - 1)]
-    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
-    q0, qs, kbs, vbs = dev["q0"], dev["q_steps"], dev["kb_steps"], dev["vb_steps"]
+    seq_dev = DevArray.from_host(hip, batch.seq_start)
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype,
+                    alloc=lambda shape, dt: DevArray(hip, shape, dt), seq_start_dev=seq_dev)
+    q0 = dev["q0"]
+    qs, kbs, vbs = ([dev[n].offset(t) for t in range(wl.T)] for n in ("q_steps", "kb_steps", "vb_steps"))
+    stream = hip.stream()
 
-    def step(i):
+    call_of = {"scan": "select", "score_hist": "select", "radix": "select", "emit": "select",
+               "refine_stats": "refine", "refine_scores": "refine", "refine_select": "refine",
+               "gather": "gather", "attn": "attn", "attn_combine": "attn"}
+
+    def step(i, timed=None, events=None):
+        """One block per sequence. With `timed`, the events bracket that kernel in exactly one
+        launch of the step (the last attention call for the per-step kernels)."""
         k, v = kv[i % replicas]
-        r.run_block(q0, k, v, qs, kbs, vbs)
 
-    def new_event():
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record()  # instantiates the underlying HIP event
-        return ev
+        def run(call, fn, last=True):
+            on = timed is not None and call_of[timed] == call and last
+            if on:
+                H.herald_set_kernel_events(timed, *events)
+            try:
+                fn()
+            finally:
+                if on:
+                    H.herald_set_kernel_events(timed, None, None)
 
-    # warm-up; then one instrumented step per kernel to find the one that dominates a step
+        run("select", lambda: r.select(q0, k, stream=stream))
+        run("refine", lambda: r.refine(q0, k, stream=stream))
+        run("gather", lambda: r.gather(k, v, stream=stream))
+        for t in range(wl.T):
+            run("attn", lambda: r.attn(qs[t], kbs[t], vbs[t], stream=stream), last=t == wl.T - 1)
+
     log(f"[bench] {replicas} K/V replica(s); warm-up {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    hip.sync()
     launches = {"scan": 1, "score_hist": 1, "radix": 2, "emit": 1, "refine_stats": 1 if wl.dtype == "bf16" else 0,
-                "refine_scores": 1, "refine_select": 1, "gather": 1, "attn": wl.T,
+                "refine_scores": 1, "refine_select": 1 if wl.dtype == "bf16" else 0, "gather": 1, "attn": wl.T,
                 "attn_combine": wl.T if r.attn_splits > 1 else 0}
     per_launch_us = {}
     for name, n in launches.items():
@@ -137,36 +161,54 @@ def main(argv=None):
             continue
         times = []
         for rep in range(3):
-            st, sp = new_event(), new_event()
-            H.herald_set_kernel_events(name, st, sp)
-            step(rep)
-            H.herald_set_kernel_events(name, None, None)
-            torch.cuda.synchronize()
-            times.append(st.elapsed_time(sp) * 1e3)
+            st, sp = hip.event(), hip.event()
+            step(rep, name, (st, sp))
+            hip.sync()
+            times.append(hip.elapsed_ms(st, sp) * 1e3)
         per_launch_us[name] = float(np.median(times))
     per_step_us = {k: per_launch_us[k] * launches[k] for k in per_launch_us}
     dominant = max((k for k in per_step_us if k in ("scan", "refine_stats", "refine_scores", "gather", "attn")),
                    key=lambda k: per_step_us[k])
-    log(f"[bench] per-launch us: {json.dumps({k: round(v, 2) for k, v in per_launch_us.items()})}; "
+    log(f"[bench] per-launch us (eager): {json.dumps({k: round(v, 2) for k, v in per_launch_us.items()})}; "
         f"dominant: {dominant}")
 
-    # timed region: K steps, the dominant kernel bracketed by fresh events every step
-    evs = [(new_event(), new_event()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start, t_end = new_event(), new_event()
-    torch.cuda.synchronize()
+    # Timed region: K steps, the dominant kernel bracketed by fresh events in every step. By
+    # default each step is replayed from a HIP graph captured from the same calls (one graph per
+    # step, so each holds its own event pair), which takes the host out of the loop.
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    graphs = []
+    if not args.eager:
+        log(f"[bench] capturing {args.steps} step graphs")
+        for i in range(args.steps):
+            graphs.append(hip.capture(stream, lambda: step(i, dominant, evs[i])))
+        # replays must reproduce the eager result bit for bit, with eager work in between
+        outs = (r.cand, r.sel, r.k_sel, r.out)
+        for i in sorted({0, 1 % args.steps, min(replicas, args.steps - 1)}):
+            step(i)
+            hip.sync()
+            want = [o.numpy() for o in outs]
+            for _ in range(2):
+                hip.launch(graphs[i], stream)
+                hip.sync()
+                assert all(np.array_equal(w, o.numpy()) for w, o in zip(want, outs)), f"graph replay {i} differs"
+                step(i + 1)
+                hip.sync()
+        log("[bench] graph replays match eager steps")
+    t_start, t_end = hip.event(), hip.event()
+    hip.sync()
     w0 = time.perf_counter()
-    t_start.record()
+    hip.record(t_start, stream)
     for i in range(args.steps):
-        H.herald_set_kernel_events(dominant, *evs[i])
-        step(i)
-    H.herald_set_kernel_events(dominant, None, None)
-    t_end.record()
-    torch.cuda.synchronize()
+        if graphs:
+            hip.launch(graphs[i], stream)
+        else:
+            step(i, dominant, evs[i])
+    hip.record(t_end, stream)
+    hip.sync()
     wall = time.perf_counter() - w0
-    ms = t_start.elapsed_time(t_end)
+    ms = hip.elapsed_ms(t_start, t_end)
     ms_per_step = ms / args.steps
-    dom_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    dom_us = float(np.mean([hip.elapsed_ms(a, b) * 1e3 for a, b in evs]))
     blocks_per_s = wl.nseq * args.steps / (ms / 1e3)
     log(f"[bench] {args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); {ms_per_step * 1e3:.1f} us/step")
 
@@ -197,7 +239,8 @@ def main(argv=None):
                    "head_dim": wl.d, "B": wl.B, "C": wl.C, "topk": wl.topk, "T": wl.T, "kv_replicas": replicas,
                    "attn_splits": r.attn_splits},
         "tokens_per_s": round(blocks_per_s * wl.B, 1),
-        "per_launch_us": {k: round(v, 2) for k, v in per_launch_us.items()},
+        "launch": "eager" if args.eager else "hip_graph_per_step",
+        "per_launch_us_eager": {k: round(v, 2) for k, v in per_launch_us.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

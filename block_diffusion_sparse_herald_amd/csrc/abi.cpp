@@ -49,12 +49,22 @@ herald_status ok() {
   } while (0)
 
 // Launch `call` (returns hipError_t) as kernel `id`, bracketed by its events if set.
-#define HERALD_LAUNCH(id, stream, call)                                                 \
-  do {                                                                                  \
-    if (g_events[id].start) HERALD_HIP(hipEventRecord(g_events[id].start, stream));     \
-    HERALD_HIP(call);                                                                   \
-    if (g_events[id].stop) HERALD_HIP(hipEventRecord(g_events[id].stop, stream));       \
+// The events are recorded as external nodes when the stream is being captured into
+// a graph, so they time the kernel on every replay.
+#define HERALD_LAUNCH(id, stream, call)                                  \
+  do {                                                                   \
+    if (g_events[id].start) HERALD_HIP(record_event(g_events[id].start, stream)); \
+    HERALD_HIP(call);                                                    \
+    if (g_events[id].stop) HERALD_HIP(record_event(g_events[id].stop, stream));   \
   } while (0)
+
+hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return e;
+  if (st == hipStreamCaptureStatusActive) return hipEventRecordWithFlags(ev, stream, hipEventRecordExternal);
+  return hipEventRecord(ev, stream);
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -146,7 +156,8 @@ struct Carver {
 SelectWs carve_select(const Shape& s, void* ws, size_t* bytes) {
   Carver c{static_cast<char*>(ws)};
   SelectWs w;
-  w.nchunk = (int)((s.max_len + kScanTok - 1) / kScanTok);
+  w.tpc = kScanTok;
+  w.nchunk = (int)((s.max_len + w.tpc - 1) / w.tpc);
   w.nwords = (int)((s.max_len + 63) / 64);
   w.qbar = c.take<float>((size_t)s.nseq * s.Hq * s.D);
   w.logits = c.take<float>((size_t)s.Hq * s.total);
@@ -257,10 +268,10 @@ herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, 
   if (s.bf16) {
     HERALD_LAUNCH(4, stream, launch_refine_stats(s, q_refine, k_cache, cand_idx, w, stream));
     HERALD_LAUNCH(5, stream, launch_refine_scores(s, q_refine, k_cache, cand_idx, w, stream));
+    HERALD_LAUNCH(6, stream, launch_refine_select(s, cand_idx, w, topk_idx, topk_score, stream));
   } else {
-    HERALD_LAUNCH(5, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, stream));
+    HERALD_LAUNCH(5, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, topk_idx, topk_score, stream));
   }
-  HERALD_LAUNCH(6, stream, launch_refine_select(s, cand_idx, w, topk_idx, topk_score, stream));
   return ok();
 }
 

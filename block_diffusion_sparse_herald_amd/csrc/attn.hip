@@ -67,25 +67,51 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16* __restrict__ q, c
   const bf16* ksrc = k_sel + (int64_t)unit * topk * D;
   const bf16* vsrc = v_sel + (int64_t)unit * D * ldv;
 
+  // Blocks that lie wholly inside the selected subset are prefetched into
+  // registers one block ahead (16-byte loads of K rows and of V^T rows); the block
+  // that reaches the in-block keys is staged element by element.
+  constexpr int CPR = D / 8;                  // 16-byte chunks per K row
+  constexpr int KCH = KB * CPR / 256;         // K chunks per thread
+  constexpr int VCH = D * (KB / 8) / 256;     // V^T chunks per thread
+  uint4 kreg[KCH], vreg[VCH];
+  auto prefetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = threadIdx.x + i * 256;
+      kreg[i] = ld16(ksrc + (int64_t)(k0 + c / CPR) * D + (c % CPR) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = threadIdx.x + i * 256;
+      vreg[i] = ld16(vsrc + (int64_t)(c / (KB / 8)) * ldv + k0 + (c % (KB / 8)) * 8);
+    }
+  };
+  if (kbeg + KB <= topk) prefetch(kbeg);
+
   for (int k0 = kbeg; k0 < kend; k0 += KB) {
     // ---- stage K rows and V^T for keys [k0, k0+KB)
-    constexpr int CPR = D / 8;
-    for (int c = threadIdx.x; c < KB * CPR; c += 256) {
-      const int r = c / CPR, ch = c % CPR;
-      const int kk = k0 + r;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (kk < kend) {
-        if (kk < topk) val = ld16(ksrc + (int64_t)kk * D + ch * 8);
-        else val = ld16(kb + (((int64_t)s * B + (kk - topk)) * Hkv + g) * D + ch * 8);
-      }
-      *reinterpret_cast<uint4*>(&Ks[r * LDK + ch * 8]) = val;
-    }
     if (k0 + KB <= topk) {
-      for (int c = threadIdx.x; c < D * (KB / 8); c += 256) {
-        const int e = c / (KB / 8), kc = c % (KB / 8);
-        *reinterpret_cast<uint4*>(&Vt[e * LDV + kc * 8]) = ld16(vsrc + (int64_t)e * ldv + k0 + kc * 8);
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int c = threadIdx.x + i * 256;
+        *reinterpret_cast<uint4*>(&Ks[(c / CPR) * LDK + (c % CPR) * 8]) = kreg[i];
+      }
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int c = threadIdx.x + i * 256;
+        *reinterpret_cast<uint4*>(&Vt[(c / (KB / 8)) * LDV + (c % (KB / 8)) * 8]) = vreg[i];
       }
     } else {
+      for (int c = threadIdx.x; c < KB * CPR; c += 256) {
+        const int r = c / CPR, ch = c % CPR;
+        const int kk = k0 + r;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (kk < kend) {
+          if (kk < topk) val = ld16(ksrc + (int64_t)kk * D + ch * 8);
+          else val = ld16(kb + (((int64_t)s * B + (kk - topk)) * Hkv + g) * D + ch * 8);
+        }
+        *reinterpret_cast<uint4*>(&Ks[r * LDK + ch * 8]) = val;
+      }
       for (int c = threadIdx.x; c < D * KB; c += 256) {
         const int e = c % D, r = c / D;
         const int kk = k0 + r;
@@ -96,6 +122,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16* __restrict__ q, c
       }
     }
     __syncthreads();
+    if (k0 + KB < kend && k0 + 2 * KB <= topk) prefetch(k0 + KB);
 
     // ---- S^T = K Q^T: lane holds keys mt*16 + 4*(lane/16) + i of query row lane%16
     f32x4_t sacc[4][RT];
@@ -200,26 +227,47 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16* __restrict__ q, c
   }
 }
 
-template <typename T>
+// Merges the key splits of one (sequence, KV head): 4 output dimensions per thread.
+// All split partials are loaded before any is used (nsplit <= kAttnMaxSplits).
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ o_part,
                                                            const float2* __restrict__ ml, int B, int Hq, int Hkv,
-                                                           int G, int D, int nsplit, int rpad, T* __restrict__ out) {
+                                                           int G, int D, int nsplit, int rpad,
+                                                           bf16* __restrict__ out) {
   const int unit = blockIdx.y;
   const int s = unit / Hkv, g = unit % Hkv;
   const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int r = idx / D, e = idx % D;
+  const int r = idx / (D / 4), e = (idx % (D / 4)) * 4;
   if (r >= B * G) return;
-  const int64_t base = (int64_t)unit * nsplit * rpad;
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ml[base + (int64_t)sp * rpad + r].x);
-  float Lsum = 0.f, acc = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float2 p = ml[base + (int64_t)sp * rpad + r];
-    const float wgt = fast_exp2(p.x - M);
-    Lsum += wgt * p.y;
-    acc += wgt * o_part[(base + (int64_t)sp * rpad + r) * D + e];
+  const int64_t base = (int64_t)unit * nsplit * rpad + r;
+  float2 p[kAttnMaxSplits];
+  float4 o[kAttnMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kAttnMaxSplits; ++sp) {
+    if (sp < nsplit) {
+      p[sp] = ml[base + (int64_t)sp * rpad];
+      o[sp] = *reinterpret_cast<const float4*>(o_part + (base + (int64_t)sp * rpad) * D + e);
+    }
   }
-  out[(((int64_t)s * B + r / G) * Hq + g * G + r % G) * D + e] = from_f32<T>(acc / Lsum);
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kAttnMaxSplits; ++sp)
+    if (sp < nsplit) M = fmaxf(M, p[sp].x);
+  float Lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int sp = 0; sp < kAttnMaxSplits; ++sp) {
+    if (sp < nsplit) {
+      const float wgt = fast_exp2(p[sp].x - M);
+      Lsum += wgt * p[sp].y;
+      acc.x += wgt * o[sp].x;
+      acc.y += wgt * o[sp].y;
+      acc.z += wgt * o[sp].z;
+      acc.w += wgt * o[sp].w;
+    }
+  }
+  const float inv = 1.f / Lsum;
+  *reinterpret_cast<uint2*>(out + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D + e) =
+      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
 // fp32 path: one workgroup per query row; keys in chunks of 1024 with an online softmax.
@@ -289,17 +337,19 @@ static int attn_row_groups(const Shape& s) {
 
 int attn_splits(const Shape& s, int* keys_per_split) {
   const int NK = s.topk + s.B;
+  const int nblk = (NK + kAttnKeyBlock - 1) / kAttnKeyBlock;
   if (!s.bf16) {
-    *keys_per_split = ((NK + kAttnKeyBlock - 1) / kAttnKeyBlock) * kAttnKeyBlock;
+    *keys_per_split = nblk * kAttnKeyBlock;
     return 1;
   }
   const int64_t units = (int64_t)s.nseq * s.Hkv * attn_row_groups(s);
-  const int64_t target = 256;
-  const int64_t want = std::max<int64_t>(1, (target + units - 1) / std::max<int64_t>(units, 1));
-  int kps = (int)((NK + want - 1) / want);
-  kps = std::max(kAttnKeyBlock, (kps + kAttnKeyBlock - 1) / kAttnKeyBlock * kAttnKeyBlock);
-  *keys_per_split = kps;
-  return (NK + kps - 1) / kps;
+  const int64_t want = std::max<int64_t>(1, (kAttnTargetWorkgroups + units - 1) / units);
+  int bps = (int)std::max<int64_t>(kAttnMinBlocksPerSplit, (nblk + want - 1) / want);
+  bps = std::max(bps, (nblk + kAttnMaxSplits - 1) / kAttnMaxSplits);
+  const int nsplit = (nblk + bps - 1) / bps;
+  bps = (nblk + nsplit - 1) / nsplit;  // even out the splits
+  *keys_per_split = bps * kAttnKeyBlock;
+  return (NK + *keys_per_split - 1) / *keys_per_split;
 }
 
 int attn_rpad(const Shape& s) { return attn_row_groups(s) * 64 * attn_rt(s); }
@@ -338,9 +388,9 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
 }
 
 hipError_t launch_attn_combine(const Shape& s, const AttnWs& ws, void* out, hipStream_t st) {
-  dim3 grid((s.B * s.G * s.D + 255) / 256, s.nseq * s.Hkv);
-  attn_combine_kernel<bf16><<<grid, 256, 0, st>>>(ws.o_part, ws.ml, s.B, s.Hq, s.Hkv, s.G, s.D, ws.nsplit,
-                                                  attn_rpad(s), (bf16*)out);
+  dim3 grid((s.B * s.G * (s.D / 4) + 255) / 256, s.nseq * s.Hkv);
+  attn_combine_kernel<<<grid, 256, 0, st>>>(ws.o_part, ws.ml, s.B, s.Hq, s.Hkv, s.G, s.D, ws.nsplit, attn_rpad(s),
+                                            (bf16*)out);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace herald {
 
 typedef uint16_t bf16;  // storage type of bf16 tensors (bit pattern)
@@ -163,6 +165,76 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
   __syncthreads();
 }
 
+// Radix-select step run by wave 0 alone on a histogram in LDS: finds the largest
+// digit b whose suffix count reaches k and the count strictly above it. Each lane
+// holds PER = nbins/64 consecutive bins in registers (16-byte LDS reads), lane 0
+// the top ones. Only wave 0 may call it; the result is returned in every lane.
+template <int PER>
+__device__ __forceinline__ void wave_find_digit_t(const uint32_t* hist, uint32_t k, int* digit, uint32_t* above) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lo = (kWave - 1 - lane) * PER;  // first bin of this lane
+  uint32_t v[PER];
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    const uint4 t = *reinterpret_cast<const uint4*>(hist + lo + 4 * q);
+    v[4 * q] = t.x;
+    v[4 * q + 1] = t.y;
+    v[4 * q + 2] = t.z;
+    v[4 * q + 3] = t.w;
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int b = 0; b < PER; ++b) sum += v[b];
+  uint32_t incl = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  const uint32_t before = incl - sum;
+  const bool mine = before < k && incl >= k;
+  int d = 0;
+  uint32_t ab = 0;
+  {
+    uint32_t acc = before;
+    bool found = false;
+#pragma unroll
+    for (int b = PER - 1; b >= 0; --b) {
+      if (!found && acc + v[b] >= k) {
+        d = lo + b;
+        ab = acc;
+        found = true;
+      }
+      acc += v[b];
+    }
+  }
+  const uint64_t who = __ballot(mine);
+  const int src = who ? __builtin_ctzll(who) : 0;
+  *digit = __shfl(d, src);
+  *above = __shfl(ab, src);
+}
+
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, int nbins, uint32_t k, int* digit,
+                                                uint32_t* above) {
+  if (nbins == 2048) wave_find_digit_t<32>(hist, k, digit, above);
+  else wave_find_digit_t<16>(hist, k, digit, above);
+}
+
+// The three radix digits (11, 11, 10 bits) of the k-th largest key from its three
+// histograms hist[0..2048), hist[2048..4096), hist[4096..5120) in LDS. Wave 0 only.
+// Returns the threshold bit pattern and how many keys equal to it are wanted.
+__device__ __forceinline__ void wave_threshold(const uint32_t* hist, uint32_t k, uint32_t* thr, uint32_t* ties) {
+  int d1, d2, d3;
+  uint32_t a1, a2, a3;
+  wave_find_digit(hist, 2048, k, &d1, &a1);
+  const uint32_t k1 = k - a1;
+  wave_find_digit(hist + 2048, 2048, k1, &d2, &a2);
+  const uint32_t k2 = k1 - a2;
+  wave_find_digit(hist + 4096, 1024, k2, &d3, &a3);
+  *thr = ((uint32_t)d1 << 21) | ((uint32_t)d2 << 10) | (uint32_t)d3;
+  *ties = k2 - a3;
+}
+
 // ---------------------------------------------------------------- MFMA
 
 // D[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate (v_mfma_f32_16x16x32_bf16).
@@ -173,11 +245,22 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
                                                   c, 0, 0, 0);
 }
 
-// Raise a kernel's dynamic LDS limit when a launch needs more than 64 KiB (gfx950
-// has 160 KiB per CU). Host side.
+// Lets `kernel` take up to the full 160 KiB of LDS of a gfx950 CU when a launch needs
+// more than the default 64 KiB. Host side; the attribute is set once per kernel, so
+// the call is cheap and safe to repeat (also while a stream is being captured).
 inline hipError_t allow_smem(const void* kernel, size_t bytes) {
+  constexpr int kMaxLds = 160 * 1024;
   if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (bytes > (size_t)kMaxLds) return hipErrorInvalidValue;
+  static std::mutex mu;
+  static const void* done[64];
+  static int ndone = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < ndone; ++i)
+    if (done[i] == kernel) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  if (e == hipSuccess && ndone < 64) done[ndone++] = kernel;
+  return e;
 }
 
 }  // namespace herald

@@ -7,7 +7,8 @@
 
 namespace herald {
 
-// Tokens one scan workgroup covers, and tokens one score / radix workgroup covers.
+// Tokens one scan workgroup covers (one KV head), and tokens one score / radix
+// workgroup covers.
 constexpr int kScanTok = 256;
 constexpr int kScoreTok = 4096;
 constexpr int kRadixBins = 2048;
@@ -33,13 +34,15 @@ struct SelectWs {
   float* scores;     // [Hkv][total] selection score S
   uint32_t* hist;    // [nseq][Hkv][3][kRadixBins]
   uint64_t* bits;    // [nseq][Hkv][2][nwords] (above-prefix, equal-prefix) bitmaps
+  int tpc;           // tokens per scan chunk
   int nchunk;        // scan chunks per sequence (max over sequences)
   int nwords;        // bitmap words per (sequence, KV head)
 };
 
+
 struct RefineWs {
-  float2* row_stats;  // [nseq][Hkv][ntile][rows] (max, sum) per refine tile
-  float* rscore;      // [nseq][Hkv][C]
+  float2* row_stats;   // [nseq][Hkv][ntile][rows] (max, sum) per refine tile
+  float* rscore;       // [nseq][Hkv][C]
   int ntile;
 };
 
@@ -49,6 +52,11 @@ struct AttnWs {
   int nsplit;
   int keys_per_split;  // multiple of kAttnKeyBlock
 };
+
+// Key blocks per attention split: at least 4, enough splits to reach ~256 workgroups.
+constexpr int kAttnMinBlocksPerSplit = 4;
+constexpr int kAttnMaxSplits = 16;
+constexpr int kAttnTargetWorkgroups = 256;
 
 // select
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);
@@ -62,10 +70,10 @@ hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, con
                                const RefineWs& ws, hipStream_t st);
 hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, const int32_t* cand,
                                 const RefineWs& ws, hipStream_t st);
-hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
-                             hipStream_t st);
 hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
                                 float* topk_score, hipStream_t st);
+hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
+                             int32_t* topk_idx, float* topk_score, hipStream_t st);
 // gather
 hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
                          hipStream_t st);

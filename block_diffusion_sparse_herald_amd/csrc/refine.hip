@@ -15,13 +15,87 @@
 // rows are the A operand, loaded once from the cache by index into registers;
 // the group's B*G query rows sit in LDS and are the B operand
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
-// fp32 path: refine_f32_kernel, one workgroup per (sequence, KV head).
-// refine_select_kernel: exact top-K of R in LDS (three radix digits on the fp32
-// bit pattern, R >= 0), ties to the lower cache index, ascending output.
+// refine_select_kernel then takes, per (sequence, KV head), the exact top-K of R
+// in LDS (three radix digits on the fp32 bit pattern, R >= 0), ties to the lower
+// cache index, ascending output.
+// fp32 path: refine_f32_kernel, one workgroup per (sequence, KV head), same top-K.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace herald {
+
+// Exact top-k of u[0..n) (fp32 bit patterns of non-negative scores, in LDS), ties
+// to the lower position; writes cand[pos] (or pos when cand is NULL) and the score
+// of each pick in ascending position order. h: kRadixBins LDS words; lds: NT/64+3.
+template <int NT>
+__device__ void lds_topk(const uint32_t* u, int n, int k, uint32_t* h, uint32_t* lds, const int32_t* cand,
+                         int32_t* out, float* outs) {
+  uint32_t want = (uint32_t)k;
+  uint32_t prefix = 0;  // digits found so far
+  const int shift[3] = {21, 10, 0};
+  const int width[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int i = threadIdx.x; i < kRadixBins; i += NT) h[i] = 0u;
+    __syncthreads();
+    const int hi_shift = shift[pass] + width[pass];
+    const uint32_t mask = (1u << width[pass]) - 1u;
+    for (int c = threadIdx.x; c < n; c += NT) {
+      const uint32_t v = u[c];
+      if (pass == 0 || (v >> hi_shift) == prefix) atomicAdd(&h[(v >> shift[pass]) & mask], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      int d;
+      uint32_t above;
+      wave_find_digit(h, width[pass] == 11 ? kRadixBins : 1024, want, &d, &above);
+      if (threadIdx.x == 0) {
+        lds[NT / 64 + 1] = (uint32_t)d;
+        lds[NT / 64 + 2] = above;
+      }
+    }
+    __syncthreads();
+    want -= lds[NT / 64 + 2];
+    prefix = (prefix << width[pass]) | lds[NT / 64 + 1];
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;  // bit pattern of the k-th largest score
+  const uint32_t ties_wanted = want;
+
+  const int cpt = (n + NT - 1) / NT;
+  const int c0 = threadIdx.x * cpt, c1 = min(n, c0 + cpt);
+  uint32_t my_ties = 0;
+  for (int c = c0; c < c1; ++c) my_ties += u[c] == thr;
+  uint32_t tot;
+  const uint32_t tie_rank = block_exclusive_scan<NT>(my_ties, lds, &tot);
+  uint32_t my_sel = 0;
+  {
+    uint32_t tr = tie_rank;
+    for (int c = c0; c < c1; ++c) {
+      if (u[c] > thr) ++my_sel;
+      else if (u[c] == thr) {
+        if (tr < ties_wanted) ++my_sel;
+        ++tr;
+      }
+    }
+  }
+  uint32_t pos = block_exclusive_scan<NT>(my_sel, lds, &tot);
+  uint32_t tr = tie_rank;
+  for (int c = c0; c < c1; ++c) {
+    bool take = false;
+    if (u[c] > thr) take = true;
+    else if (u[c] == thr) {
+      take = tr < ties_wanted;
+      ++tr;
+    }
+    if (take) {
+      if (pos < (uint32_t)k) {
+        out[pos] = cand ? cand[c] : c;
+        if (outs) outs[pos] = __uint_as_float(u[c]);
+      }
+      ++pos;
+    }
+  }
+}
 
 template <int D>
 __device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[4][D / 32], const bf16* qs, int ldq, int rt,
@@ -137,13 +211,19 @@ __global__ __launch_bounds__(256) void refine_scores_kernel(const bf16* __restri
   float* rowIZ = rowM + RT * 16;                                                // [RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cbase = tile * kRefineTile + w * 64;
+  // per-row normalisers over all tiles (loads issued 8 at a time, merged in tile order)
   for (int r = threadIdx.x; r < RT * 16; r += 256) {
     float M = -INFINITY, Z = 0.f;
-    if (r < R)
-      for (int t = 0; t < ntile; ++t) {
-        const float2 p = row_stats[(((int64_t)s * Hkv + g) * ntile + t) * R + r];
-        ms_merge(M, Z, p.x, p.y);
+    if (r < R) {
+      const float2* rs = row_stats + ((int64_t)s * Hkv + g) * ntile * R + r;
+      for (int t0 = 0; t0 < ntile; t0 += 8) {
+        float2 p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] = t0 + u < ntile ? rs[(int64_t)(t0 + u) * R] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ms_merge(M, Z, p[u].x, p[u].y);
       }
+    }
     rowM[r] = M;
     rowIZ[r] = r < R ? 1.f / Z : 0.f;
   }
@@ -179,6 +259,23 @@ __global__ __launch_bounds__(256) void refine_scores_kernel(const bf16* __restri
         if (c < C) rscore[((int64_t)s * Hkv + g) * C + c] = rs[mt][i];
       }
   }
+
+}
+
+// Exact top-K of the refine scores of one (sequence, KV head), in LDS.
+__global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __restrict__ cand,
+                                                            const float* __restrict__ rscore, int Hkv, int C,
+                                                            int topk, int32_t* __restrict__ topk_idx,
+                                                            float* __restrict__ topk_score) {
+  const int g = blockIdx.x, s = blockIdx.y;
+  extern __shared__ uint32_t u[];  // [C]
+  __shared__ uint32_t h[kRadixBins];
+  __shared__ uint32_t lds[1024 / 64 + 4];
+  const int64_t base = ((int64_t)s * Hkv + g) * C;
+  for (int c = threadIdx.x; c < C; c += 1024) u[c] = __float_as_uint(rscore[base + c]);
+  __syncthreads();
+  lds_topk<1024>(u, C, topk, h, lds, cand + base, topk_idx + ((int64_t)s * Hkv + g) * topk,
+                 topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr);
 }
 
 // fp32 path: one workgroup per (sequence, KV head); rows first, then candidates.
@@ -194,12 +291,16 @@ template <int D>
 __global__ __launch_bounds__(256) void refine_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                          const int32_t* __restrict__ cand,
                                                          const int64_t* __restrict__ seq_start, int B, int Hq,
-                                                         int Hkv, int G, int C, float scale2,
-                                                         float* __restrict__ rscore) {
+                                                         int Hkv, int G, int C, float scale2, int topk,
+                                                         float* __restrict__ rscore, int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_score) {
   const int g = blockIdx.x, s = blockIdx.y;
   const int R = B * G;
   const int64_t j0 = seq_start[s];
   __shared__ float rowM[256], rowIZ[256];
+  __shared__ uint32_t h[kRadixBins];
+  __shared__ uint32_t lds[256 / 64 + 4];
+  extern __shared__ uint32_t u[];  // [C]
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
   auto qrow = [&](int r) { return q + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D; };
   auto krow = [&](int c) { return k + ((j0 + cd[c]) * Hkv + g) * D; };
@@ -222,83 +323,11 @@ __global__ __launch_bounds__(256) void refine_f32_kernel(const float* __restrict
     float acc = 0.f;
     for (int r = 0; r < R; ++r) acc += fast_exp2(dot_rows_f32<D>(qrow(r), krow(c)) * scale2 - rowM[r]) * rowIZ[r];
     rscore[((int64_t)s * Hkv + g) * C + c] = acc;
+    u[c] = __float_as_uint(acc);
   }
-}
-
-// Exact top-K of the refine scores of one (sequence, KV head), in LDS.
-__global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __restrict__ cand,
-                                                            const float* __restrict__ rscore, int Hkv, int C,
-                                                            int topk, int32_t* __restrict__ topk_idx,
-                                                            float* __restrict__ topk_score) {
-  const int g = blockIdx.x, s = blockIdx.y;
-  extern __shared__ uint32_t u[];  // [C]
-  __shared__ uint32_t h[kRadixBins];
-  __shared__ uint32_t lds[32];
-  const int64_t base = ((int64_t)s * Hkv + g) * C;
-  for (int c = threadIdx.x; c < C; c += 1024) u[c] = __float_as_uint(rscore[base + c]);
-
-  uint32_t want = (uint32_t)topk;
-  uint32_t prefix = 0;  // digits found so far
-  int shift[3] = {21, 10, 0};
-  int width[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    for (int i = threadIdx.x; i < kRadixBins; i += 1024) h[i] = 0u;
-    __syncthreads();
-    const int hi_shift = shift[pass] + width[pass];
-    const uint32_t mask = (1u << width[pass]) - 1u;
-    for (int c = threadIdx.x; c < C; c += 1024) {
-      const uint32_t v = u[c];
-      const bool match = pass == 0 || (v >> hi_shift) == prefix;
-      if (match) atomicAdd(&h[(v >> shift[pass]) & mask], 1u);
-    }
-    __syncthreads();
-    int d;
-    uint32_t above;
-    find_digit<1024>(h, kRadixBins, want, lds, &d, &above);
-    want -= above;
-    prefix = (prefix << width[pass]) | (uint32_t)d;
-  }
-  const uint32_t thr = prefix;  // bit pattern of the topk-th largest score
-  const uint32_t ties_wanted = want;
-
-  const int cpt = (C + 1023) / 1024;
-  const int c0 = threadIdx.x * cpt, c1 = min(C, c0 + cpt);
-  uint32_t my_ties = 0;
-  for (int c = c0; c < c1; ++c) my_ties += u[c] == thr;
-  uint32_t tot;
-  uint32_t tie_rank = block_exclusive_scan<1024>(my_ties, lds, &tot);
-  // count selected with the tie quota, in candidate (= cache index) order
-  uint32_t my_sel = 0;
-  {
-    uint32_t tr = tie_rank;
-    for (int c = c0; c < c1; ++c) {
-      if (u[c] > thr) ++my_sel;
-      else if (u[c] == thr) {
-        if (tr < ties_wanted) ++my_sel;
-        ++tr;
-      }
-    }
-  }
-  uint32_t pos = block_exclusive_scan<1024>(my_sel, lds, &tot);
-  const int32_t* cd = cand + base;
-  int32_t* out = topk_idx + ((int64_t)s * Hkv + g) * topk;
-  float* outs = topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr;
-  uint32_t tr = tie_rank;
-  for (int c = c0; c < c1; ++c) {
-    bool take = false;
-    if (u[c] > thr) take = true;
-    else if (u[c] == thr) {
-      take = tr < ties_wanted;
-      ++tr;
-    }
-    if (take) {
-      if (pos < (uint32_t)topk) {
-        out[pos] = cd[c];
-        if (outs) outs[pos] = __uint_as_float(u[c]);
-      }
-      ++pos;
-    }
-  }
+  __syncthreads();
+  lds_topk<256>(u, C, topk, h, lds, cd, topk_idx + ((int64_t)s * Hkv + g) * topk,
+                topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -314,8 +343,8 @@ hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, con
   dim3 grid(ws.ntile, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
   const size_t smem = refine_smem(s, true);
-  hipError_t e = allow_smem(s.D == 128 ? (const void*)refine_stats_kernel<128> : (const void*)refine_stats_kernel<64>,
-                            smem);
+  const void* kern = s.D == 128 ? (const void*)refine_stats_kernel<128> : (const void*)refine_stats_kernel<64>;
+  hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (s.D == 128)
     refine_stats_kernel<128><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
@@ -331,8 +360,8 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
   dim3 grid(ws.ntile, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
   const size_t smem = refine_smem(s, false);
-  hipError_t e = allow_smem(
-      s.D == 128 ? (const void*)refine_scores_kernel<128> : (const void*)refine_scores_kernel<64>, smem);
+  const void* kern = s.D == 128 ? (const void*)refine_scores_kernel<128> : (const void*)refine_scores_kernel<64>;
+  hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (s.D == 128)
     refine_scores_kernel<128><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
@@ -345,19 +374,6 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
   return hipGetLastError();
 }
 
-hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
-                             hipStream_t st) {
-  dim3 grid(s.Hkv, s.nseq);
-  const float scale2 = s.scale * kLog2e;
-  if (s.D == 128)
-    refine_f32_kernel<128><<<grid, 256, 0, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
-                                                 s.Hkv, s.G, s.C, scale2, ws.rscore);
-  else
-    refine_f32_kernel<64><<<grid, 256, 0, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
-                                                s.Hkv, s.G, s.C, scale2, ws.rscore);
-  return hipGetLastError();
-}
-
 hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
                                 float* topk_score, hipStream_t st) {
   const size_t smem = (size_t)s.C * sizeof(uint32_t);
@@ -365,6 +381,23 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
   if (e != hipSuccess) return e;
   refine_select_kernel<<<dim3(s.Hkv, s.nseq), 1024, smem, st>>>(cand, ws.rscore, s.Hkv, s.C, s.topk, topk_idx,
                                                                 topk_score);
+  return hipGetLastError();
+}
+
+hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
+                             int32_t* topk_idx, float* topk_score, hipStream_t st) {
+  dim3 grid(s.Hkv, s.nseq);
+  const float scale2 = s.scale * kLog2e;
+  const size_t smem = (size_t)s.C * sizeof(uint32_t);
+  const void* kern = s.D == 128 ? (const void*)refine_f32_kernel<128> : (const void*)refine_f32_kernel<64>;
+  hipError_t e = allow_smem(kern, smem);
+  if (e != hipSuccess) return e;
+  if (s.D == 128)
+    refine_f32_kernel<128><<<grid, 256, smem, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
+                                                    s.Hkv, s.G, s.C, scale2, s.topk, ws.rscore, topk_idx, topk_score);
+  else
+    refine_f32_kernel<64><<<grid, 256, smem, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
+                                                   s.Hkv, s.G, s.C, scale2, s.topk, ws.rscore, topk_idx, topk_score);
   return hipGetLastError();
 }
 

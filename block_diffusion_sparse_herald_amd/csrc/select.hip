@@ -9,16 +9,16 @@
 // Kernels, in launch order:
 //   merge_kernel      qbar = mean_b q * scale * log2(e) (fp32); also zeroes the
 //                     radix histograms.
-//   scan_kernel       one pass over K: base-2 logits of every (query head, token)
-//                     and per-chunk (max, sum 2^(x-max)) pairs. HBM-bound GEMV:
-//                     8 lanes share a 256-byte key row (two 128-byte coalesced
-//                     loads), G query heads per row, 3-step xor reduction.
+//   scan_*_kernel     one pass over K: base-2 logits of every (query head, token)
+//                     and per-chunk (max, sum 2^(x-max)) pairs. HBM-bound: on
+//                     MFMA for bf16 caches, on the VALU for fp32 caches.
 //   score_hist_kernel per-head normalisers from the pairs, S = sum_h 2^(x-M_h)/Z_h,
 //                     first 11-bit radix histogram of the fp32 bit pattern of S.
 //   radix_kernel<2>   second 11-bit digit among keys matching the first.
 //   radix_kernel<3>   last 10-bit digit; bitmaps of keys above / equal to the
 //                     22-bit prefix (wave ballots).
-//   emit_kernel       exact threshold, ties to the lowest indices, ascending
+//   emit_kernel       one workgroup per (sequence, KV head): exact threshold from
+//                     the three histograms, ties to the lowest indices, ascending
 //                     indices from the bitmaps (block-wide prefix counts).
 // S >= 0, so its IEEE bit pattern orders like its value and radix select is exact.
 #include "common.hpp"
@@ -35,11 +35,21 @@ __global__ __launch_bounds__(128) void merge_kernel(const T* __restrict__ q, int
   const int blk = blockIdx.x;
   if (blk < nmerge) {
     const int s = blk / Hq, h = blk % Hq;
-    for (int e = threadIdx.x; e < D; e += blockDim.x) {
-      float acc = 0.f;
-      for (int b = 0; b < B; ++b) acc += to_f32(q[(((int64_t)s * B + b) * Hq + h) * D + e]);
-      qbar[(int64_t)blk * D + e] = acc * mul;
+    const int e = threadIdx.x;
+    if (e >= D) return;
+    const T* p = q + ((int64_t)s * B * Hq + h) * D + e;
+    const int64_t step = (int64_t)Hq * D;
+    float acc = 0.f;
+    int b = 0;
+    for (; b + 8 <= B; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = to_f32(p[(b + u) * step]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
     }
+    for (; b < B; ++b) acc += to_f32(p[b * step]);
+    qbar[(int64_t)blk * D + e] = acc * mul;
   } else {
     const int64_t nz = (int64_t)(gridDim.x - nmerge) * blockDim.x;
     for (int64_t i = (int64_t)(blk - nmerge) * blockDim.x + threadIdx.x; i < zero_words; i += nz) zero[i] = 0u;
@@ -48,16 +58,131 @@ __global__ __launch_bounds__(128) void merge_kernel(const T* __restrict__ q, int
 
 // ------------------------------------------------------------------ scan
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, const float* __restrict__ qbar,
-                                                   const int64_t* __restrict__ seq_start, int Hq, int Hkv,
-                                                   int64_t total, int nchunk, float* __restrict__ logits,
-                                                   float2* __restrict__ partials) {
-  constexpr int EPL = Vec16<T>::N;   // elements per 16-byte load
+// bf16 caches: the merged-query logits as a skinny matrix product on MFMA, so the
+// scan stays bound by HBM. Per 16 keys of one KV head and 32 dimensions, one
+// v_mfma_f32_16x16x32_bf16 takes the group's query heads as A rows (the fp32
+// merged query split into a bf16 high part and a bf16 residual, two MFMAs into
+// one fp32 accumulator, relative error ~2^-18) and the keys as B columns, loaded
+// straight from the token-major cache (each lane 16 bytes of one key row).
+// A workgroup covers kScanTok tokens of one (sequence, KV head); each wave takes
+// 64 of them, 16 per MFMA column block, all 16-byte loads issued up front.
+template <int D>
+__global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__ k, const float* __restrict__ qbar,
+                                                        const int64_t* __restrict__ seq_start, int Hq, int Hkv, int G,
+                                                        int64_t total, int nchunk, float* __restrict__ logits,
+                                                        float2* __restrict__ partials) {
+  constexpr int KS = D / 32;                 // MFMA contraction steps per key row
+  constexpr int NB = kScanTok / (4 * 16);    // 16-key column blocks per wave
+  __shared__ float2 red[4][16];
+  const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int64_t j0 = seq_start[s];
+  const int64_t L = seq_start[s + 1] - j0;
+  const int64_t tok0 = (int64_t)chunk * kScanTok;
+  if (tok0 >= L) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, kq = lane >> 4;  // MFMA column (key) and contraction quarter of this lane
+
+  // A operand: query head n of the group (rows >= G are zero), dims ks*32 + 8*kq .. +8, hi and lo parts
+  uint4 ahi[KS], alo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float x[8];
+    if (n < G) {
+      const float* qp = qbar + ((int64_t)s * Hq + g * G + n) * D + ks * 32 + kq * 8;
+      const float4 x0 = *reinterpret_cast<const float4*>(qp);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
+      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    uint32_t h[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = x[2 * e], a1 = x[2 * e + 1];
+      h[e] = pack_bf16x2(a0, a1);
+      const float r0 = a0 - __uint_as_float(h[e] << 16), r1 = a1 - __uint_as_float(h[e] & 0xffff0000u);
+      lo[e] = pack_bf16x2(r0, r1);
+    }
+    ahi[ks] = make_uint4(h[0], h[1], h[2], h[3]);
+    alo[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+
+  // B operand: key rows, all loads of this wave in flight at once
+  const int64_t row_stride = (int64_t)Hkv * D;
+  const bf16* kbase = k + (j0 * Hkv + g) * D + kq * 8;
+  const int64_t wtok0 = tok0 + w * (NB * 16);
+  uint4 kb[NB][KS];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t j = wtok0 + b * 16 + n;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[b][ks] = j < L ? ld16(kbase + j * row_stride + ks * 32) : make_uint4(0, 0, 0, 0);
+  }
+
+  // lane holds logits of query heads 4*kq + i (i = 0..3) for key n of each column block
+  float m[4], z[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    z[i] = 0.f;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = mfma16x16x32(ahi[ks], kb[b][ks], acc);
+      acc = mfma16x16x32(alo[ks], kb[b][ks], acc);
+    }
+    const int64_t j = wtok0 + b * 16 + n;
+    if (j < L) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = kq * 4 + i;
+        if (hh < G) {
+          const float x = acc[i];
+          logits[(int64_t)(g * G + hh) * total + j0 + j] = x;
+          if (x > m[i]) {
+            z[i] = z[i] * fast_exp2(m[i] - x) + 1.f;
+            m[i] = x;
+          } else {
+            z[i] += fast_exp2(x - m[i]);
+          }
+        }
+      }
+    }
+  }
+  // (max, sum) per head: over the 16 keys of the lane group, then over the 4 waves in order
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float m2 = __shfl_xor(m[i], o), z2 = __shfl_xor(z[i], o);
+      ms_merge(m[i], z[i], m2, z2);
+    }
+    if (n == 0) red[w][kq * 4 + i] = make_float2(m[i], z[i]);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float M = -INFINITY, Z = 0.f;
+    for (int ww = 0; ww < 4; ++ww) ms_merge(M, Z, red[ww][threadIdx.x].x, red[ww][threadIdx.x].y);
+    partials[((int64_t)s * Hq + g * G + threadIdx.x) * nchunk + chunk] = make_float2(M, Z);
+  }
+}
+
+// fp32 caches: VALU GEMV. 8 lanes share a key row (16-byte loads), the G query
+// heads of the row's group are reduced with 3 xor steps.
+template <int D, int MAXG>
+__global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict__ k, const float* __restrict__ qbar,
+                                                        const int64_t* __restrict__ seq_start, int Hq, int Hkv, int G,
+                                                        int64_t total, int nchunk, float* __restrict__ logits,
+                                                        float2* __restrict__ partials) {
+  constexpr int EPL = 4;             // fp32 elements per 16-byte load
   constexpr int NL = D / (8 * EPL);  // loads per lane per key row
   constexpr int PER = D / 8;         // elements per lane per key row
   constexpr int U = 4;               // key rows in flight per lane
-  static_assert(NL >= 1 && PER == NL * EPL, "row split");
+  __shared__ float2 red[32][8];
   const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
@@ -65,19 +190,18 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
   if (tok0 >= L) return;
   const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
 
-  float qr[G][PER];
+  float qr[MAXG][PER];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int hh = 0; hh < MAXG; ++hh)
 #pragma unroll
     for (int i = 0; i < NL; ++i)
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
-        qr[hh][i * EPL + e] = qbar[((int64_t)s * Hq + g * G + hh) * D + (i * 8 + sub) * EPL + e];
+        qr[hh][i * EPL + e] = hh < G ? qbar[((int64_t)s * Hq + g * G + hh) * D + (i * 8 + sub) * EPL + e] : 0.f;
 
   const int64_t row_stride = (int64_t)Hkv * D;
-  const T* kbase = k + (j0 * Hkv + g) * D;
+  const float* kbase = k + (j0 * Hkv + g) * D;
   float m = -INFINITY, ssum = 0.f;
-
   for (int it = 0; it < kScanTok / 32; it += U) {
     uint4 v[U][NL];
     int64_t jj[U];
@@ -90,25 +214,25 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float acc[G];
+      float acc[MAXG];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
+      for (int hh = 0; hh < MAXG; ++hh) acc[hh] = 0.f;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         float f[EPL];
-        Vec16<T>::unpack(v[u][i], f);
+        Vec16<float>::unpack(v[u][i], f);
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
 #pragma unroll
-          for (int hh = 0; hh < G; ++hh) acc[hh] = fmaf(qr[hh][i * EPL + e], f[e], acc[hh]);
+          for (int hh = 0; hh < MAXG; ++hh) acc[hh] = fmaf(qr[hh][i * EPL + e], f[e], acc[hh]);
       }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1)
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) acc[hh] += __shfl_xor(acc[hh], o);
+        for (int hh = 0; hh < MAXG; ++hh) acc[hh] += __shfl_xor(acc[hh], o);
       float x = acc[0];
 #pragma unroll
-      for (int hh = 1; hh < G; ++hh)
+      for (int hh = 1; hh < MAXG; ++hh)
         if (sub == hh) x = acc[hh];
       if (sub < G && jj[u] < L) {
         logits[(int64_t)(g * G + sub) * total + j0 + jj[u]] = x;
@@ -121,8 +245,6 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
       }
     }
   }
-
-  __shared__ float2 red[32][8];
   red[slot][sub] = make_float2(m, ssum);
   __syncthreads();
   if (threadIdx.x < G) {
@@ -134,38 +256,40 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
 
 // ------------------------------------------------------------------ score + first radix digit
 
-template <int G>
+template <int MAXG>
 __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict__ logits,
                                                          const float2* __restrict__ partials,
                                                          const int64_t* __restrict__ seq_start, int Hq, int Hkv,
-                                                         int64_t total, int nchunk, float* __restrict__ scores,
-                                                         uint32_t* __restrict__ hist) {
+                                                         int G, int64_t total, int nchunk, int tpc,
+                                                         float* __restrict__ scores, uint32_t* __restrict__ hist) {
   const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
   const int64_t tok0 = (int64_t)chunk * kScoreTok;
   if (tok0 >= L) return;
   __shared__ uint32_t h[kRadixBins];
-  __shared__ float2 red[4][G];
-  __shared__ float Msh[G], invZ[G];
+  __shared__ float2 red[4][MAXG];
+  __shared__ float Msh[MAXG], invZ[MAXG];
   for (int i = threadIdx.x; i < kRadixBins; i += 256) h[i] = 0u;
 
   // per-head normalisers over the whole sequence, same order in every workgroup
-  const int nc = (int)((L + kScanTok - 1) / kScanTok);
-  float m[G], z[G];
+  const int nc = (int)((L + tpc - 1) / tpc);
+  float m[MAXG], z[MAXG];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
+  for (int hh = 0; hh < MAXG; ++hh) {
     m[hh] = -INFINITY;
     z[hh] = 0.f;
   }
-  for (int c = threadIdx.x; c < nc; c += 256)
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float2 p[MAXG];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float2 p = partials[((int64_t)s * Hq + g * G + hh) * nchunk + c];
-      ms_merge(m[hh], z[hh], p.x, p.y);
-    }
+    for (int hh = 0; hh < MAXG; ++hh)
+      p[hh] = hh < G ? partials[((int64_t)s * Hq + g * G + hh) * nchunk + c] : make_float2(-INFINITY, 0.f);
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
+    for (int hh = 0; hh < MAXG; ++hh) ms_merge(m[hh], z[hh], p[hh].x, p[hh].y);
+  }
+#pragma unroll
+  for (int hh = 0; hh < MAXG; ++hh) {
     ms_wave_merge(m[hh], z[hh]);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][hh] = make_float2(m[hh], z[hh]);
   }
@@ -178,15 +302,27 @@ __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict
   }
   __syncthreads();
 
-  for (int it = 0; it < kScoreTok / 256; ++it) {
-    const int64_t j = tok0 + it * 256 + threadIdx.x;
-    if (j < L) {
-      float S = 0.f;
+  constexpr int IT = kScoreTok / 256, UB = 4;
+  for (int it = 0; it < IT; it += UB) {
+    float lv[UB][MAXG];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-        S += fast_exp2(logits[(int64_t)(g * G + hh) * total + j0 + j] - Msh[hh]) * invZ[hh];
-      scores[(int64_t)g * total + j0 + j] = S;
-      atomicAdd(&h[__float_as_uint(S) >> 21], 1u);
+    for (int u = 0; u < UB; ++u) {
+      const int64_t j = tok0 + (it + u) * 256 + threadIdx.x;
+#pragma unroll
+      for (int hh = 0; hh < MAXG; ++hh)
+        lv[u][hh] = (j < L && hh < G) ? logits[(int64_t)(g * G + hh) * total + j0 + j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int64_t j = tok0 + (it + u) * 256 + threadIdx.x;
+      if (j < L) {
+        float S = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < MAXG; ++hh)
+          if (hh < G) S += fast_exp2(lv[u][hh] - Msh[hh]) * invZ[hh];
+        scores[(int64_t)g * total + j0 + j] = S;
+        atomicAdd(&h[__float_as_uint(S) >> 21], 1u);
+      }
     }
   }
   __syncthreads();
@@ -207,30 +343,52 @@ __global__ __launch_bounds__(256) void radix_kernel(const float* __restrict__ sc
   const int64_t L = seq_start[s + 1] - j0;
   const int64_t tok0 = (int64_t)chunk * kScoreTok;
   if (tok0 >= L) return;
-  __shared__ uint32_t h[kRadixBins];
-  __shared__ uint32_t lds[16];
-  for (int i = threadIdx.x; i < kRadixBins; i += 256) h[i] = 0u;
+  __shared__ uint32_t h[kRadixBins];                // this pass
+  __shared__ uint32_t prev[(PASS - 1) * kRadixBins];  // the finished histograms of the earlier passes
+  __shared__ uint32_t dig[2];
   uint32_t* gh = hist + (int64_t)(s * Hkv + g) * 3 * kRadixBins;
-  int d1, d2 = 0;
-  uint32_t a1, a2;
-  find_digit<256>(gh, kRadixBins, (uint32_t)C, lds, &d1, &a1);
-  if (PASS == 3) find_digit<256>(gh + kRadixBins, kRadixBins, (uint32_t)C - a1, lds, &d2, &a2);
-  const uint32_t prefix = ((uint32_t)d1 << 11) | (uint32_t)d2;
+  const float* sc = scores + (int64_t)g * total + j0;
+
+  // issue the score loads first; they do not depend on the digits
+  constexpr int IT = kScoreTok / 256;
+  uint32_t u[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t j = tok0 + it * 256 + threadIdx.x;
+    u[it] = j < L ? __float_as_uint(sc[j]) : 0u;
+  }
+  for (int i = threadIdx.x; i < kRadixBins; i += 256) h[i] = 0u;
+  for (int i = threadIdx.x; i < (PASS - 1) * kRadixBins / 4; i += 256)
+    reinterpret_cast<uint4*>(prev)[i] = reinterpret_cast<const uint4*>(gh)[i];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int d1, d2 = 0;
+    uint32_t a1, a2;
+    wave_find_digit(prev, kRadixBins, (uint32_t)C, &d1, &a1);
+    if (PASS == 3) wave_find_digit(prev + kRadixBins, kRadixBins, (uint32_t)C - a1, &d2, &a2);
+    if (threadIdx.x == 0) {
+      dig[0] = (uint32_t)d1;
+      dig[1] = (uint32_t)d2;
+    }
+  }
+  __syncthreads();
+  const uint32_t d1 = dig[0];
+  const uint32_t prefix = (dig[0] << 11) | dig[1];
   uint64_t* gt_bits = bits + (int64_t)(s * Hkv + g) * 2 * nwords;
   uint64_t* eq_bits = gt_bits + nwords;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 
-  for (int it = 0; it < kScoreTok / 256; ++it) {
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
     const int64_t j = tok0 + it * 256 + threadIdx.x;
     const bool valid = j < L;
-    const uint32_t u = valid ? __float_as_uint(scores[(int64_t)g * total + j0 + j]) : 0u;
     if (PASS == 2) {
-      if (valid && (u >> 21) == (uint32_t)d1) atomicAdd(&h[(u >> 10) & 2047u], 1u);
+      if (valid && (u[it] >> 21) == d1) atomicAdd(&h[(u[it] >> 10) & 2047u], 1u);
     } else {
-      const uint32_t top = u >> 10;
+      const uint32_t top = u[it] >> 10;
       const bool eq = valid && top == prefix;
       const bool gt = valid && top > prefix;
-      if (eq) atomicAdd(&h[u & 1023u], 1u);
+      if (eq) atomicAdd(&h[u[it] & 1023u], 1u);
       const uint64_t bg = __ballot(gt), be = __ballot(eq);
       const int64_t w0 = tok0 + it * 256 + wid * 64;
       if (lane == 0 && w0 < L) {
@@ -247,81 +405,97 @@ __global__ __launch_bounds__(256) void radix_kernel(const float* __restrict__ sc
 
 // ------------------------------------------------------------------ emit
 
+// One workgroup per (sequence, KV head). Words of the prefix bitmaps are handled in
+// rounds of 4 per thread; ties (keys equal to the threshold) are kept lowest index
+// first, and the final indices come out in ascending order.
 __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ scores,
                                                    const int64_t* __restrict__ seq_start, int Hkv, int64_t total,
                                                    int C, int nwords, const uint32_t* __restrict__ hist,
-                                                   uint64_t* __restrict__ bits, int32_t* __restrict__ cand,
+                                                   const uint64_t* __restrict__ bits, int32_t* __restrict__ cand,
                                                    float* __restrict__ cand_score) {
+  constexpr int NT = 1024, WPT = 4;
   const int g = blockIdx.x, s = blockIdx.y;
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
-  __shared__ uint32_t lds[32];
+  __shared__ uint32_t hs[3 * kRadixBins];
+  __shared__ uint32_t lds[NT / 64 + 4];
   const uint32_t* gh = hist + (int64_t)(s * Hkv + g) * 3 * kRadixBins;
-  int d1, d2, d3;
-  uint32_t a1, a2, a3;
-  find_digit<1024>(gh, kRadixBins, (uint32_t)C, lds, &d1, &a1);
-  const uint32_t k1 = (uint32_t)C - a1;
-  find_digit<1024>(gh + kRadixBins, kRadixBins, k1, lds, &d2, &a2);
-  const uint32_t k2 = k1 - a2;
-  find_digit<1024>(gh + 2 * kRadixBins, 1024, k2, lds, &d3, &a3);
-  const uint32_t ties_wanted = k2 - a3;  // keys equal to the threshold to keep, lowest indices first
+  for (int i = threadIdx.x; i < 3 * kRadixBins / 4; i += NT)
+    reinterpret_cast<uint4*>(hs)[i] = reinterpret_cast<const uint4*>(gh)[i];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    uint32_t thr, ties;
+    wave_threshold(hs, (uint32_t)C, &thr, &ties);
+    if (threadIdx.x == 0) {
+      lds[NT / 64 + 1] = thr & 1023u;
+      lds[NT / 64 + 2] = ties;
+    }
+  }
+  __syncthreads();
+  const uint32_t d3 = lds[NT / 64 + 1];
+  const uint32_t ties_wanted = lds[NT / 64 + 2];
 
-  uint64_t* gt_bits = bits + (int64_t)(s * Hkv + g) * 2 * nwords;
+  const uint64_t* gt_bits = bits + (int64_t)(s * Hkv + g) * 2 * nwords;
   const uint64_t* eq_bits = gt_bits + nwords;
   const float* sc = scores + (int64_t)g * total + j0;
-  const int64_t nw = (L + 63) >> 6;
-  const int64_t wpt = (nw + 1023) / 1024;
-  const int64_t w0 = (int64_t)threadIdx.x * wpt;
-  const int64_t w1 = min(nw, w0 + wpt);
-
-  // pass A: ties owned by this thread (keys on the 22-bit prefix whose last digit is d3)
-  uint32_t my_ties = 0;
-  for (int64_t w = w0; w < w1; ++w) {
-    uint64_t x = eq_bits[w];
-    while (x) {
-      const int b = __builtin_ctzll(x);
-      x &= x - 1;
-      if ((__float_as_uint(sc[(w << 6) + b]) & 1023u) == (uint32_t)d3) ++my_ties;
-    }
-  }
-  uint32_t tot;
-  uint32_t tie_rank = block_exclusive_scan<1024>(my_ties, lds, &tot);
-
-  // pass B: final membership word by word (written over the above-prefix bitmap)
-  uint32_t my_sel = 0;
-  for (int64_t w = w0; w < w1; ++w) {
-    uint64_t sel = gt_bits[w];
-    uint64_t x = eq_bits[w];
-    while (x) {
-      const int b = __builtin_ctzll(x);
-      x &= x - 1;
-      const uint32_t low = __float_as_uint(sc[(w << 6) + b]) & 1023u;
-      if (low > (uint32_t)d3) {
-        sel |= 1ull << b;
-      } else if (low == (uint32_t)d3) {
-        if (tie_rank < ties_wanted) sel |= 1ull << b;
-        ++tie_rank;
-      }
-    }
-    gt_bits[w] = sel;
-    my_sel += (uint32_t)__builtin_popcountll(sel);
-  }
-  uint32_t pos = block_exclusive_scan<1024>(my_sel, lds, &tot);
-
-  // pass C: ascending indices
   int32_t* out = cand + (int64_t)(s * Hkv + g) * C;
   float* outs = cand_score ? cand_score + (int64_t)(s * Hkv + g) * C : nullptr;
-  for (int64_t w = w0; w < w1; ++w) {
-    uint64_t x = gt_bits[w];
-    while (x) {
-      const int b = __builtin_ctzll(x);
-      x &= x - 1;
-      if (pos < (uint32_t)C) {
-        const int64_t j = (w << 6) + b;
-        out[pos] = (int32_t)j;
-        if (outs) outs[pos] = sc[j];
+  const int64_t nw = (L + 63) >> 6;
+  uint32_t tie_base = 0, pos_base = 0;
+  for (int64_t r0 = 0; r0 < nw; r0 += (int64_t)NT * WPT) {
+    const int64_t w0 = r0 + (int64_t)threadIdx.x * WPT;
+    uint64_t gt[WPT], eq[WPT];
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      gt[i] = w0 + i < nw ? gt_bits[w0 + i] : 0ull;
+      eq[i] = w0 + i < nw ? eq_bits[w0 + i] : 0ull;
+    }
+    // keys on the 22-bit prefix: above the threshold's last digit go in, equal ones are ties
+    uint64_t tie[WPT];
+    uint32_t my_ties = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      tie[i] = 0ull;
+      uint64_t x = eq[i];
+      while (x) {
+        const int b = __builtin_ctzll(x);
+        x &= x - 1;
+        const uint32_t low = __float_as_uint(sc[((w0 + i) << 6) + b]) & 1023u;
+        if (low > d3) gt[i] |= 1ull << b;
+        else if (low == d3) tie[i] |= 1ull << b;
       }
-      ++pos;
+      my_ties += (uint32_t)__builtin_popcountll(tie[i]);
+    }
+    uint32_t tot;
+    uint32_t tie_rank = tie_base + block_exclusive_scan<NT>(my_ties, lds, &tot);
+    tie_base += tot;
+    uint32_t my_sel = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      uint64_t x = tie[i];
+      while (x) {
+        const int b = __builtin_ctzll(x);
+        x &= x - 1;
+        if (tie_rank < ties_wanted) gt[i] |= 1ull << b;
+        ++tie_rank;
+      }
+      my_sel += (uint32_t)__builtin_popcountll(gt[i]);
+    }
+    uint32_t pos = pos_base + block_exclusive_scan<NT>(my_sel, lds, &tot);
+    pos_base += tot;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      uint64_t x = gt[i];
+      while (x) {
+        const int b = __builtin_ctzll(x);
+        x &= x - 1;
+        if (pos < (uint32_t)C) {
+          const int64_t j = ((w0 + i) << 6) + b;
+          out[pos] = (int32_t)j;
+          if (outs) outs[pos] = sc[j];
+        }
+        ++pos;
+      }
     }
   }
 }
@@ -342,35 +516,35 @@ hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipSt
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static void scan_dispatch_g(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st) {
+static int maxg_of(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
+
+hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st) {
   dim3 grid(ws.nchunk, s.Hkv, s.nseq);
-#define HERALD_SCAN_CASE(GG)                                                                                  \
-  case GG:                                                                                                    \
-    scan_kernel<T, D, GG><<<grid, 256, 0, st>>>((const T*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.total,      \
-                                                ws.nchunk, ws.logits, ws.partials);                           \
+  if (s.bf16) {
+    if (s.D == 128)
+      scan_mfma_kernel<128><<<grid, 256, 0, st>>>((const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
+                                                  ws.nchunk, ws.logits, ws.partials);
+    else
+      scan_mfma_kernel<64><<<grid, 256, 0, st>>>((const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
+                                                 ws.nchunk, ws.logits, ws.partials);
+    return hipGetLastError();
+  }
+#define HERALD_SCAN_CASE(GG)                                                                                        \
+  case GG:                                                                                                          \
+    if (s.D == 128)                                                                                                 \
+      scan_valu_kernel<128, GG><<<grid, 256, 0, st>>>((const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,      \
+                                                      s.total, ws.nchunk, ws.logits, ws.partials);                  \
+    else                                                                                                            \
+      scan_valu_kernel<64, GG><<<grid, 256, 0, st>>>((const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,       \
+                                                     s.total, ws.nchunk, ws.logits, ws.partials);                   \
     break;
-  switch (s.G) {
+  switch (maxg_of(s.G)) {
     HERALD_SCAN_CASE(1)
     HERALD_SCAN_CASE(2)
-    HERALD_SCAN_CASE(3)
     HERALD_SCAN_CASE(4)
-    HERALD_SCAN_CASE(5)
-    HERALD_SCAN_CASE(6)
-    HERALD_SCAN_CASE(7)
     HERALD_SCAN_CASE(8)
   }
 #undef HERALD_SCAN_CASE
-}
-
-hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st) {
-  if (s.bf16) {
-    if (s.D == 128) scan_dispatch_g<bf16, 128>(s, k, ws, st);
-    else scan_dispatch_g<bf16, 64>(s, k, ws, st);
-  } else {
-    if (s.D == 128) scan_dispatch_g<float, 128>(s, k, ws, st);
-    else scan_dispatch_g<float, 64>(s, k, ws, st);
-  }
   return hipGetLastError();
 }
 
@@ -378,19 +552,15 @@ static int score_chunks(const Shape& s) { return (int)((s.max_len + kScoreTok - 
 
 hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st) {
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
-#define HERALD_SCORE_CASE(GG)                                                                                    \
-  case GG:                                                                                                       \
-    score_hist_kernel<GG><<<grid, 256, 0, st>>>(ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.total,      \
-                                                ws.nchunk, ws.scores, ws.hist);                                  \
+#define HERALD_SCORE_CASE(GG)                                                                                   \
+  case GG:                                                                                                      \
+    score_hist_kernel<GG><<<grid, 256, 0, st>>>(ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total, \
+                                                ws.nchunk, ws.tpc, ws.scores, ws.hist);                         \
     break;
-  switch (s.G) {
+  switch (maxg_of(s.G)) {
     HERALD_SCORE_CASE(1)
     HERALD_SCORE_CASE(2)
-    HERALD_SCORE_CASE(3)
     HERALD_SCORE_CASE(4)
-    HERALD_SCORE_CASE(5)
-    HERALD_SCORE_CASE(6)
-    HERALD_SCORE_CASE(7)
     HERALD_SCORE_CASE(8)
   }
 #undef HERALD_SCORE_CASE

@@ -114,12 +114,10 @@ def _ptr(x) -> Optional[int]:
 
 
 def _nbytes(x) -> int:
-    if x is None:
+    if x is None or isinstance(x, int):
         return 0
-    if hasattr(x, "untyped_storage"):
-        return x.numel() * x.element_size()
-    if isinstance(x, np.ndarray):
-        return x.nbytes
+    if hasattr(x, "nbytes"):
+        return int(x.nbytes)
     raise TypeError(f"pass workspace sizes explicitly for {type(x)}")
 
 

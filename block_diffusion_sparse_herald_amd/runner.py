@@ -1,23 +1,25 @@
 """Device buffers and the per-block call sequence, on top of the C ABI.
 
-PyTorch provides device memory and streams only; all compute happens in
-libherald.so. ``BlockRunner`` owns the outputs and workspaces of one batch shape
-and issues, per block: herald_select_merged, herald_refine_topk,
-herald_gather_kv, then herald_block_attn once per denoising step.
+The caller's allocator provides device memory (PyTorch by default, or the plain
+HIP runtime of ``hiprt``); all compute happens in libherald.so. ``BlockRunner``
+owns the outputs and workspaces of one batch shape and issues, per block:
+herald_select_merged, herald_refine_topk, herald_gather_kv, then
+herald_block_attn once per denoising step.
 """
 
 from __future__ import annotations
 
-from typing import Optional
+from typing import Callable, Optional
 
 import numpy as np
-import torch
 
 from . import herald as H
 
 
-def device_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
+def device_tensor(a: np.ndarray, device="cuda"):
     """numpy input (uint16 bf16 bits or float32) -> torch device tensor of the same bits."""
+    import torch
+
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
@@ -28,29 +30,46 @@ def batch_to_device(batch, device="cuda") -> dict:
             for n in ["q0", "k_cache", "v_cache", "q_steps", "kb_steps", "vb_steps"]}
 
 
-class BlockRunner:
-    """Outputs and workspaces for one (workload shape, sequence offsets)."""
+def torch_alloc(device="cuda") -> Callable:
+    import torch
 
-    def __init__(self, seq_start, B, Hq, Hkv, d, C, topk, dtype: str, softmax_scale: float = 0.0, device="cuda"):
+    def alloc(shape, dtype):
+        dt = {np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32,
+              np.dtype(np.uint16): torch.bfloat16, np.dtype(np.uint8): torch.uint8}[np.dtype(dtype)]
+        return torch.empty(tuple(shape), dtype=dt, device=device)
+
+    return alloc
+
+
+class BlockRunner:
+    """Outputs and workspaces for one (workload shape, sequence offsets).
+
+    `alloc(shape, numpy_dtype)` returns device memory exposing data_ptr() and nbytes
+    (uint16 stands for bf16); `seq_start_dev` is the device copy of the offsets
+    (made with the allocator's framework when omitted).
+    """
+
+    def __init__(self, seq_start, B, Hq, Hkv, d, C, topk, dtype: str, softmax_scale: float = 0.0, device="cuda",
+                 alloc: Optional[Callable] = None, seq_start_dev=None):
         self.dtype = H.HERALD_BF16 if dtype == "bf16" else H.HERALD_F32
-        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        alloc = torch_alloc(device) if alloc is None else alloc
         self.problem = H.make_problem(seq_start, B, Hq, Hkv, d, C, topk, self.dtype, softmax_scale=softmax_scale,
-                                      device=device)
+                                      device=device, seq_start_dev=seq_start_dev)
         nseq = len(seq_start) - 1
         self.nseq, self.B, self.Hq, self.Hkv, self.d, self.C, self.topk = nseq, B, Hq, Hkv, d, C, topk
-        dev = device
-        self.cand = torch.empty((nseq, Hkv, C), dtype=torch.int32, device=dev)
-        self.cand_score = torch.empty((nseq, Hkv, C), dtype=torch.float32, device=dev)
-        self.sel = torch.empty((nseq, Hkv, topk), dtype=torch.int32, device=dev)
-        self.sel_score = torch.empty((nseq, Hkv, topk), dtype=torch.float32, device=dev)
+        el = np.uint16 if dtype == "bf16" else np.float32
+        self.cand = alloc((nseq, Hkv, C), np.int32)
+        self.cand_score = alloc((nseq, Hkv, C), np.float32)
+        self.sel = alloc((nseq, Hkv, topk), np.int32)
+        self.sel_score = alloc((nseq, Hkv, topk), np.float32)
         self.ldv = H.herald_vsel_ld(topk)
-        self.k_sel = torch.empty((nseq, Hkv, topk, d), dtype=self.tdtype, device=dev)
-        self.v_sel = torch.empty((nseq, Hkv, d, self.ldv), dtype=self.tdtype, device=dev)
-        self.out = torch.empty((nseq, B, Hq, d), dtype=self.tdtype, device=dev)
+        self.k_sel = alloc((nseq, Hkv, topk, d), el)
+        self.v_sel = alloc((nseq, Hkv, d, self.ldv), el)
+        self.out = alloc((nseq, B, Hq, d), el)
         self.ws = {}
         for name, op in [("select", H.HERALD_OP_SELECT), ("refine", H.HERALD_OP_REFINE), ("attn", H.HERALD_OP_ATTN)]:
             n = H.herald_workspace_size(self.problem, op)
-            self.ws[name] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+            self.ws[name] = alloc((max(n, 256),), np.uint8)
         self.attn_splits = H.herald_attn_splits(self.problem)
 
     def select(self, q_merge, k_cache, stream=None):
@@ -65,7 +84,7 @@ class BlockRunner:
         H.herald_gather_kv(self.problem, k_cache, v_cache, 0, self.sel if sel is None else sel, self.k_sel,
                            self.v_sel, stream=stream)
 
-    def attn(self, q, k_blk, v_blk, out: Optional[torch.Tensor] = None, stream=None):
+    def attn(self, q, k_blk, v_blk, out=None, stream=None):
         H.herald_block_attn(self.problem, q, k_blk, v_blk, self.k_sel, self.v_sel, self.out if out is None else out,
                             self.ws["attn"], stream=stream)
 

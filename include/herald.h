@@ -175,12 +175,13 @@ herald_status herald_block_attn(const herald_problem* p, const void* q, const vo
 const char* herald_last_error(void);
 
 /*
- * Instrumentation. Kernel ids: 0 scan, 1 score + first radix pass, 2 radix
- * passes, 3 candidate emit, 4 refine statistics, 5 refine scores, 6 refine top-k,
- * 7 gather, 8 attention, 9 attention combine. While set (non-NULL), every launch of
- * that kernel on a call's stream is bracketed by hipEventRecord(start) and
- * hipEventRecord(stop) on the same stream; the last launch wins. Pass NULL events
- * to clear. Thread-local setting.
+ * Instrumentation. Kernel ids: 0 merged-query scan, 1 selection scores + first
+ * radix digit, 2 second and third radix digits, 3 candidate emission, 4 refine
+ * statistics, 5 refine scores, 6 final top-K, 7 gather, 8 block attention,
+ * 9 attention split combine. While set (non-NULL), every launch of
+ * that kernel on a call's stream is bracketed by records of start and stop on the
+ * same stream (external event nodes when the stream is being captured into a
+ * graph); the last launch wins. Pass NULL events to clear. Thread-local setting.
  */
 herald_status herald_set_kernel_events(int32_t kernel_id, hipEvent_t start, hipEvent_t stop);
 

@@ -117,12 +117,24 @@ def check_sequence(run: Run, s: int, steps, stage_isolated: bool = True):
         band_check(run.sel[s, g], R_e2e[g], wl.topk, domain=run.cand[s, g], what=f"{wl.name} s{s} g{g} refine e2e")
         np.testing.assert_allclose(run.sel_score[s, g], R_e2e[g][np.searchsorted(run.cand[s, g], run.sel[s, g])],
                                    rtol=1e-4, atol=1e-30)
-    # planted keys
+    # planted keys: always candidates (they are built along the merged-query direction); the final subset
+    # must keep them too unless the oracle's own refine drops them (the drifting-key workload: the walk grows
+    # to ~3.6 per channel at 128K, so some drifted keys outscore needles for individual real queries). Those
+    # cases are reported with the seed; the band test above already ties the GPU to the oracle there.
     if wl.planted:
         for g in range(wl.Hkv):
             planted = set(run.batch.planted[s][g].tolist())
+            assert planted <= set(cand_o[g].tolist()), f"{wl.name} s{s} g{g}: oracle misses a planted candidate"
             assert planted <= set(run.cand[s, g].tolist()), f"{wl.name} s{s} g{g}: planted key not a candidate"
-            assert planted <= set(run.sel[s, g].tolist()), f"{wl.name} s{s} g{g}: planted key not selected"
+            sel_o = set(run.cand[s, g][orc.top_k_ascending(R_e2e[g], wl.topk, tiebreak=run.cand[s, g])].tolist())
+            dropped = planted - sel_o
+            if wl.law == "drift":
+                if dropped:
+                    log(f"  {wl.name} seed {wl.seed_base + s} g{g}: oracle final subset keeps "
+                        f"{len(planted) - len(dropped)}/{len(planted)} needles")
+            else:
+                assert not dropped, f"{wl.name} s{s} g{g}: oracle drops planted keys {sorted(dropped)[:5]}"
+                assert planted <= set(run.sel[s, g].tolist()), f"{wl.name} s{s} g{g}: planted key not selected"
     # gather: bit-exact
     a = int(run.batch.seq_start[s])
     ldv = run.v_sel.shape[-1]
@@ -260,3 +272,31 @@ def test_full_size_sampled(name):
         check_sequence(run, s, steps)
     del run
     torch.cuda.empty_cache()
+
+
+def test_graph_replay_matches_eager():
+    """A whole block captured into a HIP graph: every replay equals the eager run, with eager work between."""
+    wl = SMALL["gqa32x8_L5000_b2"]
+    batch = make_batch(wl)
+    dev = batch_to_device(batch)
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
+    other = dev["k_cache"].flip(0).contiguous()  # different data for the eager runs in between
+
+    def block(k):
+        r.run_block(dev["q0"], k, dev["v_cache"], dev["q_steps"], dev["kb_steps"], dev["vb_steps"])
+
+    block(dev["k_cache"])
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (r.cand, r.cand_score, r.sel, r.k_sel, r.v_sel, r.out)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        block(dev["k_cache"])
+    for rep in range(4):
+        block(other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (r.cand, r.cand_score, r.sel, r.k_sel, r.v_sel, r.out)
+        for a, b in zip(want, got):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"replay {rep} differs"
