@@ -19,8 +19,10 @@ LIB = os.path.join(HERE, "libherald.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops stay off: hipcc would otherwise form v_pk_{add,mul,fma}_f32 on its own.
+# MFMA accumulators stay in ordinary VGPRs (no AGPR copies around the softmax).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-         "-packed-fp32-ops", "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+         "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-unused-command-line-argument",
+         "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 SOURCES = ["select.hip", "refine.hip", "gather.hip", "attn.hip", "abi.cpp"]
 

@@ -26,14 +26,22 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16* __restrict__ q, c
                                                    const bf16* __restrict__ vb, const bf16* __restrict__ k_sel,
                                                    const bf16* __restrict__ v_sel, int B, int Hq, int Hkv, int G,
                                                    int topk, int64_t ldv, float scale2, int nsplit, int kps,
-                                                   int rpad, bf16* __restrict__ out, float* __restrict__ o_part,
-                                                   float2* __restrict__ ml) {
+                                                   int rpad, int nunits, int nrg, bf16* __restrict__ out,
+                                                   float* __restrict__ o_part, float2* __restrict__ ml) {
   constexpr int KB = kAttnKeyBlock;
   constexpr int LDK = D + 8;   // K tile row stride (elements)
   constexpr int LDV = KB + 8;  // V^T tile row stride (elements)
   __shared__ __align__(16) bf16 Ks[KB * LDK];
   __shared__ __align__(16) bf16 Vt[D * LDV];
-  const int sp = blockIdx.x, rg = blockIdx.y, unit = blockIdx.z;
+  // 1-D grid, XCD-aware: workgroups are dispatched round-robin over the 8 XCDs, so
+  // workgroup x runs on XCD x % 8. The row groups of one (unit, key split) item are
+  // placed on the same XCD one after the other and share its L2 for the K/V blocks.
+  const int x = blockIdx.x;
+  const int kx = x >> 3;
+  const int item = (kx / nrg) * 8 + (x & 7);
+  const int rg = kx % nrg;
+  if (item >= nunits * nsplit) return;
+  const int sp = item % nsplit, unit = item / nsplit;
   const int s = unit / Hkv, g = unit % Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int R = B * G;
@@ -139,37 +147,41 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16* __restrict__ q, c
         for (int rt = 0; rt < RT; ++rt) sacc[mt][rt] = mfma16x16x32(a, qf[rt][ks], sacc[mt][rt]);
       }
 
-    // ---- online softmax (base 2) and P^T fragments
+    // ---- online softmax (base 2) and P^T fragments. The scale is folded into one FMA;
+    //      the output is rescaled only when some row's running max grows (otherwise
+    //      every factor is exactly 1); only the last block of a split can hold masked keys.
+    const bool partial = k0 + KB > kend;
     uint4 bp[2][RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float x[4][4];
       float bm = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kk = k0 + mt * 16 + (lane >> 4) * 4 + i;
-          x[mt][i] = kk < kend ? sacc[mt][rt][i] * scale2 : -INFINITY;
-          bm = fmaxf(bm, x[mt][i]);
+          if (partial && k0 + mt * 16 + (lane >> 4) * 4 + i >= kend) sacc[mt][rt][i] = -INFINITY;
+          bm = fmaxf(bm, sacc[mt][rt][i]);
         }
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m[rt], bm);
-      const float alpha = fast_exp2(m[rt] - mn);
+      const float mn = fmaxf(m[rt], bm * scale2);
+      if (__ballot(mn > m[rt])) {
+        const float alpha = fast_exp2(m[rt] - mn);
+        l[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt][rt] *= alpha;
+      }
+      m[rt] = mn;
       float p[4][4];
       float ps = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[mt][i] = fast_exp2(x[mt][i] - mn);
+          p[mt][i] = fast_exp2(fmaf(sacc[mt][rt][i], scale2, -mn));
           ps += p[mt][i];
         }
-      l[rt] = l[rt] * alpha + ps;
-      m[rt] = mn;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[dt][rt] *= alpha;
+      l[rt] += ps;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
         bp[h2][rt] = make_uint4(pack_bf16x2(p[2 * h2][0], p[2 * h2][1]), pack_bf16x2(p[2 * h2][2], p[2 * h2][3]),
@@ -328,7 +340,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------ host side
 
-static int attn_rt(const Shape& s) { return s.B * s.G <= 64 ? 1 : 2; }
+// 16-row MFMA tiles per wave: one, so that a workgroup takes 64 query rows and the
+// grid holds more workgroups per CU to hide latency.
+static int attn_rt(const Shape&) { return 1; }
 
 static int attn_row_groups(const Shape& s) {
   const int rows = 64 * attn_rt(s);
@@ -370,12 +384,15 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
                                                 s.topk, ldv, scale2, (float*)out);
     return hipGetLastError();
   }
-  dim3 grid(ws.nsplit, attn_row_groups(s), s.nseq * s.Hkv);
+  const int nunits = s.nseq * s.Hkv, nrg = attn_row_groups(s);
+  const int nitems = nunits * ws.nsplit;
+  // items padded to a multiple of 8, times the row groups
+  dim3 grid((unsigned)(((nitems + 7) / 8) * 8 * nrg), 1, 1);
   const int rpad = attn_rpad(s);
 #define HERALD_ATTN(DD, RR)                                                                                         \
   attn_kernel<DD, RR><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)kb, (const bf16*)vb, (const bf16*)k_sel,  \
                                             (const bf16*)v_sel, s.B, s.Hq, s.Hkv, s.G, s.topk, ldv, scale2,         \
-                                            ws.nsplit, ws.keys_per_split, rpad, (bf16*)out, ws.o_part, ws.ml)
+                                            ws.nsplit, ws.keys_per_split, rpad, nunits, nrg, (bf16*)out, ws.o_part, ws.ml)
   if (s.D == 128) {
     if (attn_rt(s) == 1) HERALD_ATTN(128, 1);
     else HERALD_ATTN(128, 2);

@@ -53,10 +53,10 @@ struct AttnWs {
   int keys_per_split;  // multiple of kAttnKeyBlock
 };
 
-// Key blocks per attention split: at least 4, enough splits to reach ~256 workgroups.
-constexpr int kAttnMinBlocksPerSplit = 4;
+// Key blocks per attention split: at least 2, enough splits to reach ~512 workgroups.
+constexpr int kAttnMinBlocksPerSplit = 2;
 constexpr int kAttnMaxSplits = 16;
-constexpr int kAttnTargetWorkgroups = 256;
+constexpr int kAttnTargetWorkgroups = 512;
 
 // select
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);
