@@ -53,6 +53,37 @@ def kernel_work(wl, lengths):
     }
 
 
+# kernel name in the roofline -> the sources its code comes from (traffic figures are void once they change)
+KERNEL_SOURCES = {
+    "attn_kernel+attn_combine_kernel": ["attn.hip", "common.hpp"],
+    "scan": ["select.hip", "common.hpp"],
+    "refine_stats": ["refine.hip", "common.hpp"],
+    "refine_scores": ["refine.hip", "common.hpp"],
+    "gather": ["gather.hip", "common.hpp"],
+}
+
+
+def sources_digest(files) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "block_diffusion_sparse_herald_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter runs, if the kernel is unchanged since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    for e in json.load(open(path)).get("entries", []):
+        if e["kernel"] == kernel and e["workload"] == workload:
+            if e["sources_sha256"] == sources_digest(KERNEL_SOURCES[kernel]):
+                return e["bytes_per_launch"]
+    return None
+
+
 def cpu_baseline(wl, batch, budget_s: float):
     """The CPU oracle, one BLAS thread, whole blocks of sequence 0 until the time budget is used."""
     import numpy as np
@@ -127,13 +158,14 @@ def main(argv=None):
                "refine_stats": "refine", "refine_scores": "refine", "refine_select": "refine",
                "gather": "gather", "attn": "attn", "attn_combine": "attn"}
 
-    def step(i, timed=None, events=None):
-        """One block per sequence. With `timed`, the events bracket that kernel in exactly one
-        launch of the step (the last attention call for the per-step kernels)."""
+    def step(i, timed=None, events=None, capturing=False):
+        """One block per sequence. With `timed`, `events` bracket that kernel in one launch of
+        the step; with timed == "attn_op" they bracket the whole T-step attention phase
+        (attention + split combine, T times)."""
         k, v = kv[i % replicas]
 
         def run(call, fn, last=True):
-            on = timed is not None and call_of[timed] == call and last
+            on = timed is not None and timed != "attn_op" and call_of[timed] == call and last
             if on:
                 H.herald_set_kernel_events(timed, *events)
             try:
@@ -145,8 +177,12 @@ def main(argv=None):
         run("select", lambda: r.select(q0, k, stream=stream))
         run("refine", lambda: r.refine(q0, k, stream=stream))
         run("gather", lambda: r.gather(k, v, stream=stream))
+        if timed == "attn_op":
+            hip.record(events[0], stream, external=capturing)
         for t in range(wl.T):
             run("attn", lambda: r.attn(qs[t], kbs[t], vbs[t], stream=stream), last=t == wl.T - 1)
+        if timed == "attn_op":
+            hip.record(events[1], stream, external=capturing)
 
     log(f"[bench] {replicas} K/V replica(s); warm-up {args.warmup} steps")
     for i in range(args.warmup):
@@ -169,18 +205,22 @@ def main(argv=None):
     per_step_us = {k: per_launch_us[k] * launches[k] for k in per_launch_us}
     dominant = max((k for k in per_step_us if k in ("scan", "refine_stats", "refine_scores", "gather", "attn")),
                    key=lambda k: per_step_us[k])
-    log(f"[bench] per-launch us (eager): {json.dumps({k: round(v, 2) for k, v in per_launch_us.items()})}; "
+    log(f"[bench] per-launch us: {json.dumps({k: round(v, 2) for k, v in per_launch_us.items()})}; "
         f"dominant: {dominant}")
 
-    # Timed region: K steps, the dominant kernel bracketed by fresh events in every step. By
-    # default each step is replayed from a HIP graph captured from the same calls (one graph per
-    # step, so each holds its own event pair), which takes the host out of the loop.
+    # Timed region: K steps, each replayed from a HIP graph captured from the same calls, which
+    # takes the host out of the loop (--eager launches directly). Every step carries its own
+    # event pair around the dominant operation: for attention, the whole phase of T calls
+    # (attention kernel + split combine each), divided by T; otherwise the one launch of
+    # the dominant kernel.
+    timed = "attn_op" if dominant in ("attn", "attn_combine") else dominant
+    nper = wl.T if timed == "attn_op" else 1
     evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
     graphs = []
     if not args.eager:
         log(f"[bench] capturing {args.steps} step graphs")
         for i in range(args.steps):
-            graphs.append(hip.capture(stream, lambda: step(i, dominant, evs[i])))
+            graphs.append(hip.capture(stream, lambda: step(i, timed, evs[i], capturing=True)))
         # replays must reproduce the eager result bit for bit, with eager work in between
         outs = (r.cand, r.sel, r.k_sel, r.out)
         for i in sorted({0, 1 % args.steps, min(replicas, args.steps - 1)}):
@@ -202,15 +242,16 @@ def main(argv=None):
         if graphs:
             hip.launch(graphs[i], stream)
         else:
-            step(i, dominant, evs[i])
+            step(i, timed, evs[i])
     hip.record(t_end, stream)
     hip.sync()
     wall = time.perf_counter() - w0
     ms = hip.elapsed_ms(t_start, t_end)
     ms_per_step = ms / args.steps
-    dom_us = float(np.mean([hip.elapsed_ms(a, b) * 1e3 for a, b in evs]))
     blocks_per_s = wl.nseq * args.steps / (ms / 1e3)
-    log(f"[bench] {args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); {ms_per_step * 1e3:.1f} us/step")
+    dom_us = float(np.mean([hip.elapsed_ms(a, b) * 1e3 for a, b in evs])) / nper
+    log(f"[bench] {args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); {ms_per_step * 1e3:.1f} us/step; "
+        f"{timed}: {dom_us:.2f} us per launch")
 
     bound, work = kernel_work(wl, batch.lengths)[dominant]
     if bound == "hbm":
@@ -219,8 +260,10 @@ def main(argv=None):
         achieved = work / (dom_us * 1e-6) / 1e12
         peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
         unit = "TFLOP/s"
-    roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "avg_launch_us": round(dom_us, 3)}
+    rkernel = "attn_kernel+attn_combine_kernel" if timed == "attn_op" else dominant
+    roofline = {"kernel": rkernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(rkernel, wl.name),
+                "avg_launch_us": round(dom_us, 3)}
 
     result = {
         "metric": METRIC,
@@ -240,7 +283,7 @@ def main(argv=None):
                    "attn_splits": r.attn_splits},
         "tokens_per_s": round(blocks_per_s * wl.B, 1),
         "launch": "eager" if args.eager else "hip_graph_per_step",
-        "per_launch_us_eager": {k: round(v, 2) for k, v in per_launch_us.items()},
+        "per_launch_us": {k: round(v, 2) for k, v in per_launch_us.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

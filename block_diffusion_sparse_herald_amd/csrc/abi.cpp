@@ -51,11 +51,14 @@ herald_status ok() {
 // Launch `call` (returns hipError_t) as kernel `id`, bracketed by its events if set.
 // The events are recorded as external nodes when the stream is being captured into
 // a graph, so they time the kernel on every replay.
-#define HERALD_LAUNCH(id, stream, call)                                  \
-  do {                                                                   \
-    if (g_events[id].start) HERALD_HIP(record_event(g_events[id].start, stream)); \
-    HERALD_HIP(call);                                                    \
-    if (g_events[id].stop) HERALD_HIP(record_event(g_events[id].stop, stream));   \
+// The events are recorded right before and after the kernel on its stream; while the
+// stream is being captured into a graph they become external event nodes, so they time
+// the kernel on every replay.
+#define HERALD_LAUNCH(id, stream, call)                                                     \
+  do {                                                                                      \
+    if (g_events[id].start) HERALD_HIP(record_event(g_events[id].start, stream));           \
+    HERALD_HIP(call);                                                                       \
+    if (g_events[id].stop) HERALD_HIP(record_event(g_events[id].stop, stream));             \
   } while (0)
 
 hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
@@ -241,7 +244,7 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
   carve_select(s, nullptr, &need);
   HERALD_TRY(check_ws(ws, ws_bytes, need));
   const SelectWs w = carve_select(s, ws, &need);
-  HERALD_LAUNCH(0, stream, launch_merge(s, q_merge, w, stream));
+  HERALD_HIP(launch_merge(s, q_merge, w, stream));
   HERALD_LAUNCH(0, stream, launch_scan(s, k_cache, w, stream));
   HERALD_LAUNCH(1, stream, launch_score_hist(s, w, stream));
   HERALD_LAUNCH(2, stream, launch_radix_pass(s, w, 2, stream));

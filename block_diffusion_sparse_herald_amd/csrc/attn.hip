@@ -375,11 +375,11 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
   if (!s.bf16) {
     dim3 grid(s.B * s.Hq, s.nseq);
     if (s.D == 128)
-      attn_f32_kernel<128><<<grid, 256, 0, st>>>((const float*)q, (const float*)kb, (const float*)vb,
+      klaunch(attn_f32_kernel<128>, grid, 256, 0, st, (const float*)q, (const float*)kb, (const float*)vb,
                                                  (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G,
                                                  s.topk, ldv, scale2, (float*)out);
     else
-      attn_f32_kernel<64><<<grid, 256, 0, st>>>((const float*)q, (const float*)kb, (const float*)vb,
+      klaunch(attn_f32_kernel<64>, grid, 256, 0, st, (const float*)q, (const float*)kb, (const float*)vb,
                                                 (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G,
                                                 s.topk, ldv, scale2, (float*)out);
     return hipGetLastError();
@@ -390,7 +390,7 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
   dim3 grid((unsigned)(((nitems + 7) / 8) * 8 * nrg), 1, 1);
   const int rpad = attn_rpad(s);
 #define HERALD_ATTN(DD, RR)                                                                                         \
-  attn_kernel<DD, RR><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)kb, (const bf16*)vb, (const bf16*)k_sel,  \
+  klaunch(attn_kernel<DD, RR>, grid, 256, 0, st, (const bf16*)q, (const bf16*)kb, (const bf16*)vb, (const bf16*)k_sel,  \
                                             (const bf16*)v_sel, s.B, s.Hq, s.Hkv, s.G, s.topk, ldv, scale2,         \
                                             ws.nsplit, ws.keys_per_split, rpad, nunits, nrg, (bf16*)out, ws.o_part, ws.ml)
   if (s.D == 128) {
@@ -406,7 +406,7 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
 
 hipError_t launch_attn_combine(const Shape& s, const AttnWs& ws, void* out, hipStream_t st) {
   dim3 grid((s.B * s.G * (s.D / 4) + 255) / 256, s.nseq * s.Hkv);
-  attn_combine_kernel<<<grid, 256, 0, st>>>(ws.o_part, ws.ml, s.B, s.Hq, s.Hkv, s.G, s.D, ws.nsplit, attn_rpad(s),
+  klaunch(attn_combine_kernel, grid, 256, 0, st, ws.o_part, ws.ml, s.B, s.Hq, s.Hkv, s.G, s.D, ws.nsplit, attn_rpad(s),
                                             (bf16*)out);
   return hipGetLastError();
 }

@@ -69,17 +69,17 @@ static hipError_t gather_dispatch(const Shape& s, const void* k, const void* v, 
   const int64_t ldv = vsel_ld(s.topk);
   if (s.bf16) {
     if (s.D == 128)
-      gather_kernel<bf16, 128, PACKED><<<grid, 256, 0, st>>>((const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
+      klaunch(gather_kernel<bf16, 128, PACKED>, grid, 256, 0, st, (const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
                                                              s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel);
     else
-      gather_kernel<bf16, 64, PACKED><<<grid, 256, 0, st>>>((const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
+      klaunch(gather_kernel<bf16, 64, PACKED>, grid, 256, 0, st, (const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
                                                             s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel);
   } else {
     if (s.D == 128)
-      gather_kernel<float, 128, PACKED><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, idx, s.seq_start,
+      klaunch(gather_kernel<float, 128, PACKED>, grid, 256, 0, st, (const float*)k, (const float*)v, idx, s.seq_start,
                                                               s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel);
     else
-      gather_kernel<float, 64, PACKED><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, idx, s.seq_start,
+      klaunch(gather_kernel<float, 64, PACKED>, grid, 256, 0, st, (const float*)k, (const float*)v, idx, s.seq_start,
                                                              s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel);
   }
   return hipGetLastError();

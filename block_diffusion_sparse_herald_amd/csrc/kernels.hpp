@@ -7,6 +7,12 @@
 
 namespace herald {
 
+// Every kernel launch of the library goes through here.
+template <typename F, typename... Args>
+inline void klaunch(F kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st, Args... args) {
+  hipLaunchKernelGGL(kernel, grid, block, smem, st, args...);
+}
+
 // Tokens one scan workgroup covers (one KV head), and tokens one score / radix
 // workgroup covers.
 constexpr int kScanTok = 256;

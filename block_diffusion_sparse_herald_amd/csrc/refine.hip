@@ -347,10 +347,10 @@ hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, con
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (s.D == 128)
-    refine_stats_kernel<128><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
+    klaunch(refine_stats_kernel<128>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
                                                       s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
   else
-    refine_stats_kernel<64><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
+    klaunch(refine_stats_kernel<64>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
                                                      s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
   return hipGetLastError();
 }
@@ -364,11 +364,11 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (s.D == 128)
-    refine_scores_kernel<128><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
+    klaunch(refine_scores_kernel<128>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
                                                        s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
                                                        ws.rscore);
   else
-    refine_scores_kernel<64><<<grid, 256, smem, st>>>((const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
+    klaunch(refine_scores_kernel<64>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
                                                       s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
                                                       ws.rscore);
   return hipGetLastError();
@@ -379,7 +379,7 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
   const size_t smem = (size_t)s.C * sizeof(uint32_t);
   hipError_t e = allow_smem((const void*)refine_select_kernel, smem);
   if (e != hipSuccess) return e;
-  refine_select_kernel<<<dim3(s.Hkv, s.nseq), 1024, smem, st>>>(cand, ws.rscore, s.Hkv, s.C, s.topk, topk_idx,
+  klaunch(refine_select_kernel, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, s.Hkv, s.C, s.topk, topk_idx,
                                                                 topk_score);
   return hipGetLastError();
 }
@@ -393,10 +393,10 @@ hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (s.D == 128)
-    refine_f32_kernel<128><<<grid, 256, smem, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
+    klaunch(refine_f32_kernel<128>, grid, 256, smem, st, (const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
                                                     s.Hkv, s.G, s.C, scale2, s.topk, ws.rscore, topk_idx, topk_score);
   else
-    refine_f32_kernel<64><<<grid, 256, smem, st>>>((const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
+    klaunch(refine_f32_kernel<64>, grid, 256, smem, st, (const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
                                                    s.Hkv, s.G, s.C, scale2, s.topk, ws.rscore, topk_idx, topk_score);
   return hipGetLastError();
 }

@@ -508,10 +508,10 @@ hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipSt
   const int nz = (int)std::min<int64_t>(256, (zero_words + 127) / 128);
   const float mul = s.scale * kLog2e / (float)s.B;
   if (s.bf16)
-    merge_kernel<bf16><<<nmerge + nz, 128, 0, st>>>((const bf16*)q, s.B, s.Hq, s.D, mul, ws.qbar, nmerge, ws.hist,
+    klaunch(merge_kernel<bf16>, nmerge + nz, 128, 0, st, (const bf16*)q, s.B, s.Hq, s.D, mul, ws.qbar, nmerge, ws.hist,
                                                     zero_words);
   else
-    merge_kernel<float><<<nmerge + nz, 128, 0, st>>>((const float*)q, s.B, s.Hq, s.D, mul, ws.qbar, nmerge, ws.hist,
+    klaunch(merge_kernel<float>, nmerge + nz, 128, 0, st, (const float*)q, s.B, s.Hq, s.D, mul, ws.qbar, nmerge, ws.hist,
                                                      zero_words);
   return hipGetLastError();
 }
@@ -522,20 +522,20 @@ hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStr
   dim3 grid(ws.nchunk, s.Hkv, s.nseq);
   if (s.bf16) {
     if (s.D == 128)
-      scan_mfma_kernel<128><<<grid, 256, 0, st>>>((const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
+      klaunch(scan_mfma_kernel<128>, grid, 256, 0, st, (const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
                                                   ws.nchunk, ws.logits, ws.partials);
     else
-      scan_mfma_kernel<64><<<grid, 256, 0, st>>>((const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
+      klaunch(scan_mfma_kernel<64>, grid, 256, 0, st, (const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
                                                  ws.nchunk, ws.logits, ws.partials);
     return hipGetLastError();
   }
 #define HERALD_SCAN_CASE(GG)                                                                                        \
   case GG:                                                                                                          \
     if (s.D == 128)                                                                                                 \
-      scan_valu_kernel<128, GG><<<grid, 256, 0, st>>>((const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,      \
+      klaunch(scan_valu_kernel<128, GG>, grid, 256, 0, st, (const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,      \
                                                       s.total, ws.nchunk, ws.logits, ws.partials);                  \
     else                                                                                                            \
-      scan_valu_kernel<64, GG><<<grid, 256, 0, st>>>((const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,       \
+      klaunch(scan_valu_kernel<64, GG>, grid, 256, 0, st, (const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,       \
                                                      s.total, ws.nchunk, ws.logits, ws.partials);                   \
     break;
   switch (maxg_of(s.G)) {
@@ -554,7 +554,7 @@ hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st)
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
 #define HERALD_SCORE_CASE(GG)                                                                                   \
   case GG:                                                                                                      \
-    score_hist_kernel<GG><<<grid, 256, 0, st>>>(ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total, \
+    klaunch(score_hist_kernel<GG>, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total, \
                                                 ws.nchunk, ws.tpc, ws.scores, ws.hist);                         \
     break;
   switch (maxg_of(s.G)) {
@@ -570,15 +570,15 @@ hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st)
 hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipStream_t st) {
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
   if (pass == 2)
-    radix_kernel<2><<<grid, 256, 0, st>>>(ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
+    klaunch(radix_kernel<2>, grid, 256, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
   else
-    radix_kernel<3><<<grid, 256, 0, st>>>(ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
+    klaunch(radix_kernel<3>, grid, 256, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
   return hipGetLastError();
 }
 
 hipError_t launch_emit_candidates(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score,
                                   hipStream_t st) {
-  emit_kernel<<<dim3(s.Hkv, s.nseq), 1024, 0, st>>>(ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist,
+  klaunch(emit_kernel, dim3(s.Hkv, s.nseq), 1024, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist,
                                                     ws.bits, cand, cand_score);
   return hipGetLastError();
 }

@@ -33,7 +33,9 @@ class Hip:
             "hipStreamCreate": [ctypes.POINTER(_vp)],
             "hipStreamSynchronize": [_vp],
             "hipEventCreate": [ctypes.POINTER(_vp)],
+            "hipEventCreateWithFlags": [ctypes.POINTER(_vp), ctypes.c_uint],
             "hipEventRecord": [_vp, _vp],
+            "hipEventRecordWithFlags": [_vp, _vp, ctypes.c_uint],
             "hipEventSynchronize": [_vp],
             "hipEventElapsedTime": [ctypes.POINTER(ctypes.c_float), _vp, _vp],
             "hipStreamBeginCapture": [_vp, ctypes.c_int],
@@ -90,13 +92,22 @@ class Hip:
         else:
             self.check(self.lib.hipStreamSynchronize(stream), "hipStreamSynchronize")
 
-    def event(self) -> int:
+    def event(self, light: bool = False) -> int:
+        """A timing event; `light` ones skip the system-scope cache release on record
+        (hipEventDisableSystemFence), so bracketing a kernel adds little to it."""
         e = _vp()
-        self.check(self.lib.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
+        if light:
+            self.check(self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000), "hipEventCreateWithFlags")
+        else:
+            self.check(self.lib.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
         return e.value
 
-    def record(self, event: int, stream: int) -> None:
-        self.check(self.lib.hipEventRecord(event, stream), "hipEventRecord")
+    def record(self, event: int, stream: int, external: bool = False) -> None:
+        """Record `event` on `stream`; `external` makes it an event node of a graph being captured."""
+        if external:
+            self.check(self.lib.hipEventRecordWithFlags(event, stream, 1), "hipEventRecordWithFlags")
+        else:
+            self.check(self.lib.hipEventRecord(event, stream), "hipEventRecord")
 
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = ctypes.c_float()

@@ -178,10 +178,10 @@ const char* herald_last_error(void);
  * Instrumentation. Kernel ids: 0 merged-query scan, 1 selection scores + first
  * radix digit, 2 second and third radix digits, 3 candidate emission, 4 refine
  * statistics, 5 refine scores, 6 final top-K, 7 gather, 8 block attention,
- * 9 attention split combine. While set (non-NULL), every launch of
- * that kernel on a call's stream is bracketed by records of start and stop on the
- * same stream (external event nodes when the stream is being captured into a
- * graph); the last launch wins. Pass NULL events to clear. Thread-local setting.
+ * 9 attention split combine. While set (non-NULL), every launch of that kernel on a
+ * call's stream is bracketed by records of start and stop on the same stream
+ * (external event nodes when the stream is being captured into a graph); the last
+ * launch wins. Pass NULL events to clear. Thread-local setting.
  */
 herald_status herald_set_kernel_events(int32_t kernel_id, hipEvent_t start, hipEvent_t stop);
 
