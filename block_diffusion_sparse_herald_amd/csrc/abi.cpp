@@ -142,7 +142,6 @@ herald_status make_shape(const herald_problem* p, Shape* s) {
 }
 
 size_t elem_bytes(const Shape& s) { return s.bf16 ? 2 : 4; }
-size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Carves consecutive 256-byte-aligned regions out of a workspace.
 struct Carver {
@@ -182,21 +181,6 @@ RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
   return w;
 }
 
-AttnWs carve_attn(const Shape& s, void* ws, size_t* bytes) {
-  Carver c{static_cast<char*>(ws)};
-  AttnWs w;
-  w.nsplit = attn_splits(s, &w.keys_per_split);
-  w.o_part = nullptr;
-  w.ml = nullptr;
-  if (w.nsplit > 1) {
-    const size_t rows = (size_t)s.nseq * s.Hkv * w.nsplit * attn_rpad(s);
-    w.o_part = c.take<float>(rows * s.D);
-    w.ml = c.take<float2>(rows);
-  }
-  *bytes = c.off;
-  return w;
-}
-
 size_t gather_host_bytes(const Shape& s) { return align256(2 * (size_t)s.nseq * s.Hkv * s.topk * s.D * elem_bytes(s)); }
 
 herald_status check_ws(void* ws, size_t have, size_t need) {
@@ -219,7 +203,7 @@ herald_status herald_workspace_size(const herald_problem* p, int op, size_t* byt
   switch (op) {
     case HERALD_OP_SELECT: carve_select(s, nullptr, &n); break;
     case HERALD_OP_REFINE: carve_refine(s, nullptr, &n); break;
-    case HERALD_OP_ATTN: carve_attn(s, nullptr, &n); break;
+    case HERALD_OP_ATTN: n = attn_ws_bytes(s); break;
     case HERALD_OP_GATHER_HOST: n = gather_host_bytes(s); break;
     default: return fail(HERALD_ERR_INVALID_ARG, "unknown op %d", op);
   }
@@ -342,12 +326,9 @@ herald_status herald_block_attn(const herald_problem* p, const void* q, const vo
   HERALD_TRY(check_ptr(k_sel, "k_sel"));
   HERALD_TRY(check_ptr(v_sel, "v_sel"));
   HERALD_TRY(check_ptr(out, "out"));
-  size_t need;
-  carve_attn(s, nullptr, &need);
-  HERALD_TRY(check_ws(ws, ws_bytes, need));
-  const AttnWs w = carve_attn(s, ws, &need);
-  HERALD_LAUNCH(8, stream, launch_attn(s, q, k_blk, v_blk, k_sel, v_sel, out, w, stream));
-  if (w.nsplit > 1) HERALD_LAUNCH(9, stream, launch_attn_combine(s, w, out, stream));
+  HERALD_TRY(check_ws(ws, ws_bytes, attn_ws_bytes(s)));
+  HERALD_LAUNCH(8, stream, launch_attn(s, q, k_blk, v_blk, k_sel, v_sel, out, ws, stream));
+  if (attn_splits(s) > 1) HERALD_LAUNCH(9, stream, launch_attn_combine(s, ws, out, stream));
   return ok();
 }
 
@@ -365,8 +346,7 @@ herald_status herald_set_kernel_events(int32_t kernel_id, hipEvent_t start, hipE
 int32_t herald_attn_splits(const herald_problem* p) {
   Shape s;
   if (make_shape(p, &s) != HERALD_OK) return -1;
-  int kps;
-  return attn_splits(s, &kps);
+  return attn_splits(s);
 }
 
 }  // extern "C"

@@ -18,6 +18,9 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// low / high bf16 of a packed pair, widened
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 
 // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 f32_to_bf16(float f) {

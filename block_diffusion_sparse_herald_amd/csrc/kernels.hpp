@@ -52,17 +52,20 @@ struct RefineWs {
   int ntile;
 };
 
-struct AttnWs {
-  float* o_part;   // [nseq][Hkv][nsplit][rows][D] unnormalised partial outputs
-  float2* ml;      // [nseq][Hkv][nsplit][rows] (max, sum)
-  int nsplit;
-  int keys_per_split;  // multiple of kAttnKeyBlock
+// Attention work split (see attn_geom): query tiles per workgroup, key ranges.
+struct AttnGeom {
+  int B, G, Hq, Hkv, topk;
+  int64_t ldv;
+  int nunits;  // nseq * Hkv
+  int tpw;     // 16-row query tiles per workgroup (one per wave)
+  int nrs;     // row splits: workgroups per key range
+  int rpad;    // rows rounded up to whole tiles
+  int nks;     // key ranges per unit
+  int bps;     // 64-key blocks per key range
+  int nitems;  // workgroups
 };
-
-// Key blocks per attention split: at least 2, enough splits to reach ~512 workgroups.
-constexpr int kAttnMinBlocksPerSplit = 2;
-constexpr int kAttnMaxSplits = 16;
 constexpr int kAttnTargetWorkgroups = 512;
+constexpr int kAttnMaxSplits = 32;
 
 // select
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);
@@ -86,12 +89,14 @@ hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int
 hipError_t launch_layout_packed(const Shape& s, const void* packed_k, const void* packed_v, void* k_sel, void* v_sel,
                                 hipStream_t st);
 // attention
-int attn_splits(const Shape& s, int* keys_per_split);
-int attn_rpad(const Shape& s);
+AttnGeom attn_geom(const Shape& s);
+int attn_splits(const Shape& s);
+size_t attn_ws_bytes(const Shape& s);
 hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void* vb, const void* k_sel,
-                       const void* v_sel, void* out, const AttnWs& ws, hipStream_t st);
-hipError_t launch_attn_combine(const Shape& s, const AttnWs& ws, void* out, hipStream_t st);
+                       const void* v_sel, void* out, void* ws, hipStream_t st);
+hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t st);
 
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 inline int64_t vsel_ld(int topk) { return ((int64_t)topk + 63) / 64 * 64; }
 
 }  // namespace herald

@@ -161,14 +161,16 @@ def test_empty_batch_is_a_noop(lib):
 
 
 def test_kernel_events_argument_checks(lib):
-    assert status_of(H.herald_set_kernel_events, 10, None, None) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_set_kernel_events, len(H.KERNEL_IDS), None, None) == H.HERALD_ERR_INVALID_ARG
+    for kid in H.KERNEL_IDS.values():
+        H.herald_set_kernel_events(kid, None, None)
     assert status_of(H.herald_set_kernel_events, -1, None, None) == H.HERALD_ERR_INVALID_ARG
     assert status_of(H.herald_set_kernel_events, 0, FAKE, None) == H.HERALD_ERR_INVALID_ARG
     H.herald_set_kernel_events(0, None, None)
 
 
 def test_attn_splits_reported(lib):
-    assert H.herald_attn_splits(prob()) >= 1
+    assert 1 <= H.herald_attn_splits(prob()) <= 32
     assert H.herald_attn_splits(prob(dtype=H.HERALD_F32)) == 1
 
 

@@ -49,6 +49,12 @@ SMALL = {
                            T=1, seed_base=7500),
     "topk1": Workload("topk1", nseq=1, L=1000, Hq=4, Hkv=2, d=64, dtype="bf16", B=2, C=1, topk=1, T=1,
                       seed_base=7600),
+    # a full 64-key block of in-block keys and a subset of whole blocks; 192 rows
+    "b64_g3": Workload("b64_g3", nseq=1, L=1500, Hq=6, Hkv=2, d=128, dtype="bf16", B=64, C=400, topk=128, T=2,
+                       seed_base=7700),
+    # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
+    "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
+                           T=2, seed_base=7800),
 }
 
 
