@@ -162,7 +162,7 @@ SelectWs carve_select(const Shape& s, void* ws, size_t* bytes) {
   w.nchunk = (int)((s.max_len + w.tpc - 1) / w.tpc);
   w.nwords = (int)((s.max_len + 63) / 64);
   w.qbar = c.take<float>((size_t)s.nseq * s.Hq * s.D);
-  w.logits = c.take<float>((size_t)s.Hq * s.total);
+  w.logits = c.take<float>((size_t)s.Hkv * s.total * (s.G <= 4 ? 4 : 8));  // token-major, heads padded
   w.partials = c.take<float2>((size_t)s.nseq * s.Hq * w.nchunk);
   w.scores = c.take<float>((size_t)s.Hkv * s.total);
   w.hist = c.take<uint32_t>((size_t)s.nseq * s.Hkv * 3 * kRadixBins);

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 namespace herald {
@@ -251,19 +252,38 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
 // Lets `kernel` take up to the full 160 KiB of LDS of a gfx950 CU when a launch needs
 // more than the default 64 KiB. Host side; the attribute is set once per kernel, so
 // the call is cheap and safe to repeat (also while a stream is being captured).
-inline hipError_t allow_smem(const void* kernel, size_t bytes) {
-  constexpr int kMaxLds = 160 * 1024;
-  if (bytes <= 65536) return hipSuccess;
-  if (bytes > (size_t)kMaxLds) return hipErrorInvalidValue;
+// Lets `kernel` take `dynamic` bytes of dynamic LDS next to its static LDS (raises the
+// per-kernel limit once, to what the 160 KiB of a compute unit leave).
+inline hipError_t allow_smem(const void* kernel, size_t dynamic) {
+  constexpr size_t kMaxLds = 160 * 1024;
+  struct Entry {
+    const void* kernel;
+    size_t static_bytes;
+    bool raised;
+  };
   static std::mutex mu;
-  static const void* done[64];
-  static int ndone = 0;
+  static Entry seen[64];
+  static int nseen = 0;
   std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < ndone; ++i)
-    if (done[i] == kernel) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-  if (e == hipSuccess && ndone < 64) done[ndone++] = kernel;
-  return e;
+  Entry* e = nullptr;
+  for (int i = 0; i < nseen; ++i)
+    if (seen[i].kernel == kernel) e = &seen[i];
+  if (!e) {
+    hipFuncAttributes attr;
+    const hipError_t st = hipFuncGetAttributes(&attr, kernel);
+    if (st != hipSuccess) return st;
+    if (nseen == 64) return hipErrorUnknown;
+    seen[nseen] = Entry{kernel, attr.sharedSizeBytes, false};
+    e = &seen[nseen++];
+  }
+  const size_t room = kMaxLds - std::min(kMaxLds, e->static_bytes);
+  if (dynamic > room) return hipErrorInvalidValue;
+  if (dynamic + e->static_bytes > 65536 && !e->raised) {
+    const hipError_t st = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)room);
+    if (st != hipSuccess) return st;
+    e->raised = true;
+  }
+  return hipSuccess;
 }
 
 }  // namespace herald

@@ -16,7 +16,7 @@ inline void klaunch(F kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st
 // Tokens one scan workgroup covers (one KV head), and tokens one score / radix
 // workgroup covers.
 constexpr int kScanTok = 256;
-constexpr int kScoreTok = 4096;
+constexpr int kScoreTok = 1024;
 constexpr int kRadixBins = 2048;
 // Candidates one refine workgroup covers (bf16 MFMA path).
 constexpr int kRefineTile = 256;
@@ -35,7 +35,7 @@ struct Shape {
 
 struct SelectWs {
   float* qbar;       // [nseq][Hq][D] merged query * scale * log2(e)
-  float* logits;     // [Hq][total] base-2 logits of the merged query
+  float* logits;     // [Hkv][total][4 or 8] base-2 logits of the merged query (heads of the group, padded)
   float2* partials;  // [nseq][Hq][nchunk] (max, sum 2^(x-max)) per scan chunk
   float* scores;     // [Hkv][total] selection score S
   uint32_t* hist;    // [nseq][Hkv][3][kRadixBins]

@@ -9,7 +9,8 @@
 // Kernels, in launch order:
 //   merge_kernel      qbar = mean_b q * scale * log2(e) (fp32); also zeroes the
 //                     radix histograms.
-//   scan_*_kernel     one pass over K: base-2 logits of every (query head, token)
+//   scan_*_kernel     one pass over K: base-2 logits of every (query head, token),
+//                     stored token-major with the group's heads padded to 4 or 8,
 //                     and per-chunk (max, sum 2^(x-max)) pairs. HBM-bound: on
 //                     MFMA for bf16 caches, on the VALU for fp32 caches.
 //   score_hist_kernel per-head normalisers from the pairs, S = sum_h 2^(x-M_h)/Z_h,
@@ -120,7 +121,9 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
     for (int ks = 0; ks < KS; ++ks) kb[b][ks] = j < L ? ld16(kbase + j * row_stride + ks * 32) : make_uint4(0, 0, 0, 0);
   }
 
-  // lane holds logits of query heads 4*kq + i (i = 0..3) for key n of each column block
+  // lane holds logits of query heads 4*kq + i (i = 0..3) for key n of each column block;
+  // stored token-major, the group's heads padded to 4 or 8 per token
+  const int GP = G <= 4 ? 4 : 8;
   float m[4], z[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -137,12 +140,14 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
     }
     const int64_t j = wtok0 + b * 16 + n;
     if (j < L) {
+      if (4 * kq < GP)
+        *reinterpret_cast<float4*>(logits + ((int64_t)g * total + j0 + j) * GP + 4 * kq) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = kq * 4 + i;
         if (hh < G) {
           const float x = acc[i];
-          logits[(int64_t)(g * G + hh) * total + j0 + j] = x;
           if (x > m[i]) {
             z[i] = z[i] * fast_exp2(m[i] - x) + 1.f;
             m[i] = x;
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
       for (int hh = 1; hh < MAXG; ++hh)
         if (sub == hh) x = acc[hh];
       if (sub < G && jj[u] < L) {
-        logits[(int64_t)(g * G + sub) * total + j0 + jj[u]] = x;
+        logits[((int64_t)g * total + j0 + jj[u]) * (G <= 4 ? 4 : 8) + sub] = x;
         if (x > m) {
           ssum = ssum * fast_exp2(m - x) + 1.f;
           m = x;
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ score + first radix digit
 
-template <int MAXG>
+template <int GP>
 __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict__ logits,
                                                          const float2* __restrict__ partials,
                                                          const int64_t* __restrict__ seq_start, int Hq, int Hkv,
@@ -267,29 +272,40 @@ __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict
   const int64_t L = seq_start[s + 1] - j0;
   const int64_t tok0 = (int64_t)chunk * kScoreTok;
   if (tok0 >= L) return;
+  constexpr int IT = kScoreTok / 256;
   __shared__ uint32_t h[kRadixBins];
-  __shared__ float2 red[4][MAXG];
-  __shared__ float Msh[MAXG], invZ[MAXG];
+  __shared__ float2 red[4][GP];
+  __shared__ float Msh[GP], invZ[GP];
+
+  // this workgroup's logits: token-major, GP heads per token; loads first
+  float4 lv[IT][GP / 4];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t j = min(tok0 + it * 256 + threadIdx.x, L - 1);
+#pragma unroll
+    for (int c = 0; c < GP / 4; ++c)
+      lv[it][c] = *reinterpret_cast<const float4*>(logits + ((int64_t)g * total + j0 + j) * GP + 4 * c);
+  }
   for (int i = threadIdx.x; i < kRadixBins; i += 256) h[i] = 0u;
 
   // per-head normalisers over the whole sequence, same order in every workgroup
   const int nc = (int)((L + tpc - 1) / tpc);
-  float m[MAXG], z[MAXG];
+  float m[GP], z[GP];
 #pragma unroll
-  for (int hh = 0; hh < MAXG; ++hh) {
+  for (int hh = 0; hh < GP; ++hh) {
     m[hh] = -INFINITY;
     z[hh] = 0.f;
   }
   for (int c = threadIdx.x; c < nc; c += 256) {
-    float2 p[MAXG];
+    float2 p[GP];
 #pragma unroll
-    for (int hh = 0; hh < MAXG; ++hh)
+    for (int hh = 0; hh < GP; ++hh)
       p[hh] = hh < G ? partials[((int64_t)s * Hq + g * G + hh) * nchunk + c] : make_float2(-INFINITY, 0.f);
 #pragma unroll
-    for (int hh = 0; hh < MAXG; ++hh) ms_merge(m[hh], z[hh], p[hh].x, p[hh].y);
+    for (int hh = 0; hh < GP; ++hh) ms_merge(m[hh], z[hh], p[hh].x, p[hh].y);
   }
 #pragma unroll
-  for (int hh = 0; hh < MAXG; ++hh) {
+  for (int hh = 0; hh < GP; ++hh) {
     ms_wave_merge(m[hh], z[hh]);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][hh] = make_float2(m[hh], z[hh]);
   }
@@ -302,27 +318,17 @@ __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict
   }
   __syncthreads();
 
-  constexpr int IT = kScoreTok / 256, UB = 4;
-  for (int it = 0; it < IT; it += UB) {
-    float lv[UB][MAXG];
 #pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const int64_t j = tok0 + (it + u) * 256 + threadIdx.x;
+  for (int it = 0; it < IT; ++it) {
+    const int64_t j = tok0 + it * 256 + threadIdx.x;
+    if (j < L) {
+      const float* x = reinterpret_cast<const float*>(&lv[it][0]);
+      float S = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < MAXG; ++hh)
-        lv[u][hh] = (j < L && hh < G) ? logits[(int64_t)(g * G + hh) * total + j0 + j] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const int64_t j = tok0 + (it + u) * 256 + threadIdx.x;
-      if (j < L) {
-        float S = 0.f;
-#pragma unroll
-        for (int hh = 0; hh < MAXG; ++hh)
-          if (hh < G) S += fast_exp2(lv[u][hh] - Msh[hh]) * invZ[hh];
-        scores[(int64_t)g * total + j0 + j] = S;
-        atomicAdd(&h[__float_as_uint(S) >> 21], 1u);
-      }
+      for (int hh = 0; hh < GP; ++hh)
+        if (hh < G) S += fast_exp2(x[hh] - Msh[hh]) * invZ[hh];
+      scores[(int64_t)g * total + j0 + j] = S;
+      atomicAdd(&h[__float_as_uint(S) >> 21], 1u);
     }
   }
   __syncthreads();
@@ -407,7 +413,9 @@ __global__ __launch_bounds__(256) void radix_kernel(const float* __restrict__ sc
 
 // One workgroup per (sequence, KV head). Words of the prefix bitmaps are handled in
 // rounds of 4 per thread; ties (keys equal to the threshold) are kept lowest index
-// first, and the final indices come out in ascending order.
+// first, and the final indices come out in ascending order. The picks are collected
+// in LDS and written out (with their scores) by all threads at the end, so the
+// score gathers are independent loads.
 __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ scores,
                                                    const int64_t* __restrict__ seq_start, int Hkv, int64_t total,
                                                    int C, int nwords, const uint32_t* __restrict__ hist,
@@ -419,6 +427,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ sc
   const int64_t L = seq_start[s + 1] - j0;
   __shared__ uint32_t hs[3 * kRadixBins];
   __shared__ uint32_t lds[NT / 64 + 4];
+  extern __shared__ int32_t picks[];  // [C]
   const uint32_t* gh = hist + (int64_t)(s * Hkv + g) * 3 * kRadixBins;
   for (int i = threadIdx.x; i < 3 * kRadixBins / 4; i += NT)
     reinterpret_cast<uint4*>(hs)[i] = reinterpret_cast<const uint4*>(gh)[i];
@@ -489,12 +498,28 @@ __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ sc
       while (x) {
         const int b = __builtin_ctzll(x);
         x &= x - 1;
-        if (pos < (uint32_t)C) {
-          const int64_t j = ((w0 + i) << 6) + b;
-          out[pos] = (int32_t)j;
-          if (outs) outs[pos] = sc[j];
-        }
+        if (pos < (uint32_t)C) picks[pos] = (int32_t)(((w0 + i) << 6) + b);
         ++pos;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int U = 4;
+  for (int p0 = 0; p0 < C; p0 += NT * U) {
+    int32_t j[U];
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * NT + threadIdx.x;
+      j[u] = p < C ? picks[p] : 0;
+      v[u] = (outs && p < C) ? sc[j[u]] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * NT + threadIdx.x;
+      if (p < C) {
+        out[p] = j[u];
+        if (outs) outs[p] = v[u];
       }
     }
   }
@@ -552,18 +577,12 @@ static int score_chunks(const Shape& s) { return (int)((s.max_len + kScoreTok - 
 
 hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st) {
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
-#define HERALD_SCORE_CASE(GG)                                                                                   \
-  case GG:                                                                                                      \
-    klaunch(score_hist_kernel<GG>, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total, \
-                                                ws.nchunk, ws.tpc, ws.scores, ws.hist);                         \
-    break;
-  switch (maxg_of(s.G)) {
-    HERALD_SCORE_CASE(1)
-    HERALD_SCORE_CASE(2)
-    HERALD_SCORE_CASE(4)
-    HERALD_SCORE_CASE(8)
-  }
-#undef HERALD_SCORE_CASE
+  if (s.G <= 4)
+    klaunch(score_hist_kernel<4>, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
+            ws.nchunk, ws.tpc, ws.scores, ws.hist);
+  else
+    klaunch(score_hist_kernel<8>, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
+            ws.nchunk, ws.tpc, ws.scores, ws.hist);
   return hipGetLastError();
 }
 
@@ -578,8 +597,11 @@ hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipSt
 
 hipError_t launch_emit_candidates(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score,
                                   hipStream_t st) {
-  klaunch(emit_kernel, dim3(s.Hkv, s.nseq), 1024, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist,
-                                                    ws.bits, cand, cand_score);
+  const size_t smem = (size_t)s.C * sizeof(int32_t);
+  hipError_t e = allow_smem((const void*)emit_kernel, smem);
+  if (e != hipSuccess) return e;
+  klaunch(emit_kernel, dim3(s.Hkv, s.nseq), 1024, smem, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords,
+          ws.hist, ws.bits, cand, cand_score);
   return hipGetLastError();
 }
 

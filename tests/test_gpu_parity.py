@@ -52,6 +52,9 @@ SMALL = {
     # a full 64-key block of in-block keys and a subset of whole blocks; 192 rows
     "b64_g3": Workload("b64_g3", nseq=1, L=1500, Hq=6, Hkv=2, d=128, dtype="bf16", B=64, C=400, topk=128, T=2,
                        seed_base=7700),
+    # the largest candidate set (C = 16384: LDS beyond 64 KiB in the emit and top-K kernels)
+    "c16384": Workload("c16384", nseq=1, L=40000, Hq=8, Hkv=2, d=128, dtype="bf16", B=8, C=16384, topk=3000, T=1,
+                       seed_base=7900),
     # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
     "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
                            T=2, seed_base=7800),
