@@ -175,7 +175,7 @@ RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
   Carver c{static_cast<char*>(ws)};
   RefineWs w;
   w.ntile = (s.C + kRefineTile - 1) / kRefineTile;
-  w.row_stats = c.take<float2>((size_t)s.nseq * s.Hkv * w.ntile * s.B * s.G);
+  w.row_stats = c.take<float2>((size_t)s.nseq * s.Hkv * ((w.ntile + 1) & ~1) * s.B * s.G);
   w.rscore = c.take<float>((size_t)s.nseq * s.Hkv * s.C);
   *bytes = c.off;
   return w;

@@ -33,18 +33,23 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k, co
     return base + ((j0 + idx[unit * topk + i]) * Hkv + g) * D;
   };
 
-  // K: straight row copy
-  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
-    const int r = c / CPR, ch = c % CPR;
-    const int i = i0 + r;
-    if (i < topk) st16(k_sel + (unit * topk + i) * D + ch * EPL, ld16(src_row(k, i) + ch * EPL));
+  // K rows (copied straight through) and V rows (staged in LDS): all loads first
+  constexpr int NPT = 64 * CPR / 256;  // 16-byte chunks per thread, each of K and V
+  uint4 kv[NPT], vv[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int c = threadIdx.x + u * 256;
+    const int i = min(i0 + c / CPR, topk - 1), ch = c % CPR;
+    kv[u] = ld16(src_row(k, i) + ch * EPL);
+    vv[u] = ld16(src_row(v, i) + ch * EPL);
   }
-  // V: rows into LDS, then out d-major
-  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int c = threadIdx.x + u * 256;
     const int r = c / CPR, ch = c % CPR;
     const int i = i0 + r;
-    const uint4 val = i < topk ? ld16(src_row(v, i) + ch * EPL) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&tile[r * LDT + ch * EPL]) = val;
+    if (i < topk) st16(k_sel + (unit * topk + i) * D + ch * EPL, kv[u]);
+    *reinterpret_cast<uint4*>(&tile[r * LDT + ch * EPL]) = i < topk ? vv[u] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
   // each 16-byte output chunk holds EPL consecutive picks of one dimension

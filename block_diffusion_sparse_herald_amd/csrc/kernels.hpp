@@ -19,7 +19,7 @@ constexpr int kScanTok = 256;
 constexpr int kScoreTok = 1024;
 constexpr int kRadixBins = 2048;
 // Candidates one refine workgroup covers (bf16 MFMA path).
-constexpr int kRefineTile = 256;
+constexpr int kRefineTile = 128;
 // Keys per attention block and the largest supported candidate count.
 constexpr int kAttnKeyBlock = 64;
 constexpr int kMaxCandidates = 16384;
@@ -47,7 +47,7 @@ struct SelectWs {
 
 
 struct RefineWs {
-  float2* row_stats;   // [nseq][Hkv][ntile][rows] (max, sum) per refine tile
+  float2* row_stats;   // [nseq][Hkv][rows][ntile rounded up to even] (max, sum) per refine tile
   float* rscore;       // [nseq][Hkv][C]
   int ntile;
 };

@@ -8,12 +8,14 @@
 //
 // bf16 path, two launches over the same (sequence, KV head, 256-candidate tile)
 // grid; both compute x with identical MFMA code, so the logits agree bit for bit:
-//   refine_stats_kernel   per row (b,h): (max, sum 2^(x-max)) over the tile.
+//   refine_stats_kernel   per row (b,h): (max, sum 2^(x-max)) over the tile
+//                         (stored row-major: a row's tiles are contiguous).
 //   refine_scores_kernel  per row: normalisers from all tiles; per candidate: the
 //                         sum over rows, in a fixed order.
 // Each wave owns 64 candidates (four 16-candidate MFMA tiles). The candidate key
-// rows are the A operand, loaded once from the cache by index into registers;
-// the group's B*G query rows sit in LDS and are the B operand
+// rows (gathered from the cache by index) and the group's B*G query rows are
+// streamed into LDS with coalesced direct-to-LDS loads; the key rows are the A
+// operand (read once into registers), the query rows the B operand
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 // refine_select_kernel then takes, per (sequence, KV head), the exact top-K of R
 // in LDS (three radix digits on the fp32 bit pattern, R >= 0), ties to the lower
@@ -97,13 +99,21 @@ __device__ void lds_topk(const uint32_t* u, int n, int k, uint32_t* h, uint32_t*
   }
 }
 
+// 16-byte chunk c of an LDS row r (query row or candidate key row) is stored at chunk
+// c ^ refine_swz(r): the 16 rows one MFMA fragment read touches hit distinct banks.
 template <int D>
-__device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[4][D / 32], const bf16* qs, int ldq, int rt,
-                                                   int lane, f32x4_t (&acc)[4]) {
+__device__ __forceinline__ int refine_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int D>
+__device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[4][D / 32], const bf16* qs, int rt, int lane,
+                                                   f32x4_t (&acc)[4]) {
   uint4 bq[D / 32];
+  const int r = rt * 16 + (lane & 15);
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    bq[ks] = *reinterpret_cast<const uint4*>(qs + (rt * 16 + (lane & 15)) * ldq + ks * 32 + (lane >> 4) * 8);
+    bq[ks] = *reinterpret_cast<const uint4*>(qs + r * D + ((ks * 4 + (lane >> 4)) ^ refine_swz<D>(r)) * 8);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -112,56 +122,79 @@ __device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[4][D / 32], 
   }
 }
 
-// Shared prologue of both refine kernels: stage the group's query rows in LDS and
-// load this wave's 64 candidate key rows into registers.
+// Shared prologue of both refine kernels, in two parts. refine_issue_rows: the
+// group's query rows and this workgroup's kRefineTile candidate key rows go to LDS
+// with coalesced direct-to-LDS loads (rows past R re-read query row 0, candidates
+// past C re-read the last one; both are masked later). refine_key_frags: once the
+// loads have landed, each wave reads the key fragments of its 64 candidates into
+// registers.
 template <int D>
-__device__ __forceinline__ void refine_prologue(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                const int32_t* __restrict__ cand, int64_t j0, int s, int g, int B,
-                                                int Hq, int Hkv, int G, int C, int R, int RT, int cbase, bf16* qs,
-                                                int ldq, uint4 (&a)[4][D / 32]) {
-  const int lane = threadIdx.x & 63;
-  // query rows r = b*G + hh -> q[s][b][g*G+hh][:]; rows past R are zero
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  for (int c = threadIdx.x; c < RT * 16 * CPR; c += 256) {
-    const int r = c / CPR, ch = c % CPR;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < R) {
-      const int b = r / G, hh = r % G;
-      v = ld16(q + (((int64_t)s * B + b) * Hq + g * G + hh) * D + ch * 8);
-    }
-    *reinterpret_cast<uint4*>(qs + r * ldq + ch * 8) = v;
+__device__ __forceinline__ void refine_issue_rows(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                  const int32_t* __restrict__ cand, int64_t j0, int s, int g, int B,
+                                                  int Hq, int Hkv, int G, int C, int R, int RT, int ctile, bf16* qs,
+                                                  bf16* kls) {
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR; // rows per load instruction
+  constexpr int NW = kRefineTile / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rr = lane / CPR, p = lane % CPR;
+  // query rows: the waves take turns by instruction
+  for (int r0 = w * RPI; r0 < RT * 16; r0 += NW * RPI) {
+    const int r = r0 + rr;
+    const int rq = r < R ? r : 0;
+    const bf16* src = q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + (p ^ refine_swz<D>(r)) * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(qs + r0 * D), 16, 0, 0);
   }
+  // candidate key rows: wave w loads (and later uses) rows w*64 .. w*64+63 of the tile
+  const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int c = cbase + mt * 16 + (lane & 15);
-    const bf16* row = nullptr;
-    if (c < C) row = k + ((j0 + cand[((int64_t)s * Hkv + g) * C + c]) * Hkv + g) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      a[mt][ks] = row ? ld16(row + ks * 32 + (lane >> 4) * 8) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < 64 / RPI; ++u) {
+    const int i = w * 64 + u * RPI + rr;
+    const int c = min(ctile * kRefineTile + i, C - 1);
+    const bf16* src = k + ((j0 + cd[c]) * Hkv + g) * D + (p ^ refine_swz<D>(i)) * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(kls + (w * 64 + u * RPI) * D), 16, 0, 0);
   }
-  __syncthreads();
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void refine_stats_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                           const int32_t* __restrict__ cand,
-                                                           const int64_t* __restrict__ seq_start, int B, int Hq,
-                                                           int Hkv, int G, int C, float scale2, int ntile,
-                                                           float2* __restrict__ row_stats) {
+__device__ __forceinline__ void refine_key_frags(const bf16* kls, uint4 (&a)[4][D / 32]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int i = w * 64 + mt * 16 + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      a[mt][ks] = *reinterpret_cast<const uint4*>(kls + i * D + ((ks * 4 + (lane >> 4)) ^ refine_swz<D>(i)) * 8);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* __restrict__ q,
+                                                                   const bf16* __restrict__ k,
+                                                                   const int32_t* __restrict__ cand,
+                                                                   const int64_t* __restrict__ seq_start, int B,
+                                                                   int Hq, int Hkv, int G, int C, float scale2,
+                                                                   int ntile, float2* __restrict__ row_stats) {
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NW = kRefineTile / 64;
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G, RT = (R + 15) / 16, ldq = D + 8;
-  bf16* qs = reinterpret_cast<bf16*>(smem);
-  float2* wstat = reinterpret_cast<float2*>(smem + RT * 16 * ldq * sizeof(bf16));  // [4][RT*16]
+  const int R = B * G, RT = (R + 15) / 16;
+  bf16* qs = reinterpret_cast<bf16*>(smem);                     // [RT*16][D]
+  bf16* kls = qs + RT * 16 * D;                                 // [kRefineTile][D]
+  float2* wstat = reinterpret_cast<float2*>(kls + kRefineTile * D);  // [NW][RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cbase = tile * kRefineTile + w * 64;
   uint4 a[4][D / 32];
-  refine_prologue<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, cbase, qs, ldq, a);
+  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, kls);
+  refine_key_frags<D>(kls, a);
 
   for (int rt = 0; rt < RT; ++rt) {
     f32x4_t acc[4];
-    refine_tile_logits<D>(a, qs, ldq, rt, lane, acc);
+    refine_tile_logits<D>(a, qs, rt, lane, acc);
     float x[4][4];
     float m = -INFINITY;
 #pragma unroll
@@ -186,49 +219,62 @@ __global__ __launch_bounds__(256) void refine_stats_kernel(const bf16* __restric
     if (lane < 16) wstat[w * RT * 16 + rt * 16 + lane] = make_float2(m, l);
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += 256) {
+  for (int r = threadIdx.x; r < R; r += kRefineTile) {
     float M = -INFINITY, Z = 0.f;
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const float2 p = wstat[ww * RT * 16 + r];
       ms_merge(M, Z, p.x, p.y);
     }
-    row_stats[(((int64_t)s * Hkv + g) * ntile + tile) * R + r] = make_float2(M, Z);
+    row_stats[(((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1) + tile] = make_float2(M, Z);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void refine_scores_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                            const int32_t* __restrict__ cand,
-                                                            const int64_t* __restrict__ seq_start, int B, int Hq,
-                                                            int Hkv, int G, int C, float scale2, int ntile,
-                                                            const float2* __restrict__ row_stats,
-                                                            float* __restrict__ rscore) {
+__global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* __restrict__ q,
+                                                                    const bf16* __restrict__ k,
+                                                                    const int32_t* __restrict__ cand,
+                                                                    const int64_t* __restrict__ seq_start, int B,
+                                                                    int Hq, int Hkv, int G, int C, float scale2,
+                                                                    int ntile, const float2* __restrict__ row_stats,
+                                                                    float* __restrict__ rscore) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G, RT = (R + 15) / 16, ldq = D + 8;
-  bf16* qs = reinterpret_cast<bf16*>(smem);
-  float* rowM = reinterpret_cast<float*>(smem + RT * 16 * ldq * sizeof(bf16));  // [RT*16]
-  float* rowIZ = rowM + RT * 16;                                                // [RT*16]
+  const int R = B * G, RT = (R + 15) / 16;
+  bf16* qs = reinterpret_cast<bf16*>(smem);               // [RT*16][D]
+  bf16* kls = qs + RT * 16 * D;                           // [kRefineTile][D]
+  float* rowM = reinterpret_cast<float*>(kls + kRefineTile * D);  // [RT*16]
+  float* rowIZ = rowM + RT * 16;                                 // [RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cbase = tile * kRefineTile + w * 64;
-  // per-row normalisers over all tiles (loads issued 8 at a time, merged in tile order)
-  for (int r = threadIdx.x; r < RT * 16; r += 256) {
+  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, kls);
+  // per-row normalisers over all tiles, merged in tile order while the rows stream in
+  // (a row's tile statistics are contiguous; 32 tiles per batch of loads)
+  for (int r = threadIdx.x; r < RT * 16; r += kRefineTile) {
     float M = -INFINITY, Z = 0.f;
     if (r < R) {
-      const float2* rs = row_stats + ((int64_t)s * Hkv + g) * ntile * R + r;
-      for (int t0 = 0; t0 < ntile; t0 += 8) {
-        float2 p[8];
+      const float2* rs = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);  // 16-byte aligned rows
+      for (int t0 = 0; t0 < ntile; t0 += 32) {
+        float2 p[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) p[u] = t0 + u < ntile ? rs[(int64_t)(t0 + u) * R] : make_float2(-INFINITY, 0.f);
+        for (int u = 0; u < 32; u += 2) {
+          if (t0 + u + 1 < ntile) {
+            const float4 v = *reinterpret_cast<const float4*>(rs + t0 + u);
+            p[u] = make_float2(v.x, v.y);
+            p[u + 1] = make_float2(v.z, v.w);
+          } else {
+            p[u] = t0 + u < ntile ? rs[t0 + u] : make_float2(-INFINITY, 0.f);
+            p[u + 1] = make_float2(-INFINITY, 0.f);
+          }
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ms_merge(M, Z, p[u].x, p[u].y);
+        for (int u = 0; u < 32; ++u) ms_merge(M, Z, p[u].x, p[u].y);
       }
     }
     rowM[r] = M;
     rowIZ[r] = r < R ? 1.f / Z : 0.f;
   }
   uint4 a[4][D / 32];
-  refine_prologue<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, cbase, qs, ldq, a);
+  refine_key_frags<D>(kls, a);
 
   float rs[4][4];
 #pragma unroll
@@ -237,7 +283,7 @@ __global__ __launch_bounds__(256) void refine_scores_kernel(const bf16* __restri
     for (int i = 0; i < 4; ++i) rs[mt][i] = 0.f;
   for (int rt = 0; rt < RT; ++rt) {
     f32x4_t acc[4];
-    refine_tile_logits<D>(a, qs, ldq, rt, lane, acc);
+    refine_tile_logits<D>(a, qs, rt, lane, acc);
     const int r = rt * 16 + (lane & 15);
     const float M = rowM[r], iz = rowIZ[r];
 #pragma unroll
@@ -259,7 +305,6 @@ __global__ __launch_bounds__(256) void refine_scores_kernel(const bf16* __restri
         if (c < C) rscore[((int64_t)s * Hkv + g) * C + c] = rs[mt][i];
       }
   }
-
 }
 
 // Exact top-K of the refine scores of one (sequence, KV head), in LDS.
@@ -334,8 +379,8 @@ __global__ __launch_bounds__(256) void refine_f32_kernel(const float* __restrict
 
 static size_t refine_smem(const Shape& s, bool stats) {
   const int RT = (s.B * s.G + 15) / 16;
-  const size_t q = (size_t)RT * 16 * (s.D + 8) * sizeof(bf16);
-  return q + (stats ? (size_t)4 * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
+  const size_t rows = ((size_t)RT * 16 + kRefineTile) * s.D * sizeof(bf16);
+  return rows + (stats ? (size_t)(kRefineTile / 64) * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
 }
 
 hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
@@ -347,10 +392,10 @@ hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, con
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (s.D == 128)
-    klaunch(refine_stats_kernel<128>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
+    klaunch(refine_stats_kernel<128>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
                                                       s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
   else
-    klaunch(refine_stats_kernel<64>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
+    klaunch(refine_stats_kernel<64>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
                                                      s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
   return hipGetLastError();
 }
@@ -364,11 +409,11 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (s.D == 128)
-    klaunch(refine_scores_kernel<128>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
+    klaunch(refine_scores_kernel<128>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
                                                        s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
                                                        ws.rscore);
   else
-    klaunch(refine_scores_kernel<64>, grid, 256, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
+    klaunch(refine_scores_kernel<64>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
                                                       s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
                                                       ws.rscore);
   return hipGetLastError();
