@@ -55,7 +55,7 @@ def kernel_work(wl, lengths):
 
 # kernel name in the roofline -> the sources its code comes from (traffic figures are void once they change)
 KERNEL_SOURCES = {
-    "attn_part_kernel+attn_combine_kernel": ["attn.hip", "common.hpp"],
+    "attn_kernel": ["attn.hip", "common.hpp"],
     "scan": ["select.hip", "common.hpp"],
     "refine_stats": ["refine.hip", "common.hpp"],
     "refine_scores": ["refine.hip", "common.hpp"],
@@ -149,19 +149,19 @@ def main(argv=None):
                                               for _ in range(replicas - 1)]
     seq_dev = DevArray.from_host(hip, batch.seq_start)
     r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype,
-                    alloc=lambda shape, dt: DevArray(hip, shape, dt), seq_start_dev=seq_dev)
+                    alloc=lambda shape, dt, zero=False: DevArray(hip, shape, dt, zero), seq_start_dev=seq_dev)
     q0 = dev["q0"]
     qs, kbs, vbs = ([dev[n].offset(t) for t in range(wl.T)] for n in ("q_steps", "kb_steps", "vb_steps"))
     stream = hip.stream()
 
     call_of = {"scan": "select", "score_hist": "select", "radix": "select", "emit": "select",
                "refine_stats": "refine", "refine_scores": "refine", "refine_select": "refine",
-               "gather": "gather", "attn": "attn", "attn_combine": "attn"}
+               "gather": "gather", "attn": "attn"}
 
     def step(i, timed=None, events=None, capturing=False):
         """One block per sequence. With `timed`, `events` bracket that kernel in one launch of
         the step; with timed == "attn_op" they bracket the whole T-step attention phase
-        (T attention calls back to back: key-range kernel + merge kernel each)."""
+        (T attention calls back to back)."""
         k, v = kv[i % replicas]
 
         def run(call, fn, last=True):
@@ -189,8 +189,7 @@ def main(argv=None):
         step(i)
     hip.sync()
     launches = {"scan": 1, "score_hist": 1, "radix": 2, "emit": 1, "refine_stats": 1 if wl.dtype == "bf16" else 0,
-                "refine_scores": 1, "refine_select": 1 if wl.dtype == "bf16" else 0, "gather": 1, "attn": wl.T,
-                "attn_combine": wl.T if r.attn_splits > 1 else 0}
+                "refine_scores": 1, "refine_select": 1 if wl.dtype == "bf16" else 0, "gather": 1, "attn": wl.T}
     per_launch_us = {}
     for name, n in launches.items():
         if n == 0:
@@ -203,7 +202,6 @@ def main(argv=None):
             times.append(hip.elapsed_ms(st, sp) * 1e3)
         per_launch_us[name] = float(np.median(times))
     per_step_us = {k: per_launch_us[k] * launches[k] for k in per_launch_us}
-    per_step_us["attn"] += per_step_us.get("attn_combine", 0.0)  # one attention call = both kernels
     dominant = max((k for k in per_step_us if k in ("scan", "refine_stats", "refine_scores", "gather", "attn")),
                    key=lambda k: per_step_us[k])
     log(f"[bench] per-launch us: {json.dumps({k: round(v, 2) for k, v in per_launch_us.items()})}; "
@@ -211,10 +209,10 @@ def main(argv=None):
 
     # Timed region: K steps, each replayed from a HIP graph captured from the same calls, which
     # takes the host out of the loop (--eager launches directly). Every step carries its own
-    # event pair around the dominant operation: for attention, the whole phase of T calls
-    # (key-range kernel + merge kernel each), divided by T (an event can be recorded only
-    # once per graph); otherwise the one launch of the dominant kernel.
-    timed = "attn_op" if dominant in ("attn", "attn_combine") else dominant
+    # event pair around the dominant operation: for attention, the whole phase of T calls,
+    # divided by T (an event can be recorded only once per graph); otherwise the one launch
+    # of the dominant kernel.
+    timed = "attn_op" if dominant == "attn" else dominant
     nper = wl.T if timed == "attn_op" else 1
     evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
     graphs = []
@@ -261,7 +259,7 @@ def main(argv=None):
         achieved = work / (dom_us * 1e-6) / 1e12
         peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
         unit = "TFLOP/s"
-    rkernel = "attn_part_kernel+attn_combine_kernel" if timed == "attn_op" else dominant
+    rkernel = "attn_kernel" if timed == "attn_op" else dominant
     roofline = {"kernel": rkernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(rkernel, wl.name),
                 "avg_launch_us": round(dom_us, 3)}

@@ -9,21 +9,24 @@
 // The keys form 64-key blocks: ceil(topk/64) subset blocks (the last one masked past
 // topk) and one block of the B <= 64 in-block keys.
 //
-// bf16 path. A compute unit pulls data from L2/HBM at a few tens of GB/s (the
-// number of misses it can keep in flight bounds it), so the keys of one (sequence,
-// KV head) are spread over many workgroups: attn_part_kernel gives each workgroup a
-// contiguous range of key blocks and a set of 16-row query tiles (one per wave).
-// Per block the workgroup stages K rows (XOR-swizzled 16-byte chunks, so that the
-// 16 rows one MFMA reads fall in distinct LDS banks) and V^T (padded rows) in LDS,
-// every wave reads its fragments from there: S^T = K.Q^T on v_mfma_f32_16x16x32_bf16
-// (keys on M, the tile's query rows on N, Q fragments held in registers), an
-// online softmax in base 2 per query row, then O^T += V^T.P^T with P^T taken from
-// the S^T accumulators. The keys of a block are assigned to MFMA rows so that the
-// 32-key contraction of the second product runs over consecutive keys (one 16-byte
-// LDS read per V^T fragment). The next block is fetched into registers while the
-// current one is used. With one key range the kernel writes the output; otherwise
-// it writes partials (fp32 max and sum, the unnormalised output rounded to bf16)
-// that attn_combine_kernel merges.
+// bf16 path (attn_kernel). A workgroup of 8 waves takes up to four 16-row query tiles
+// of one (sequence, KV head) and a range of its key blocks (all of them unless the
+// subset is long). Its two groups of 4 waves take alternate blocks, each wave one
+// tile, and their partial results are merged through LDS at the end. Subset blocks
+// stream into a ring of LDS stages with coalesced direct-to-LDS loads
+// (global_load_lds_dwordx4, no registers held, up to four blocks in flight); K rows
+// and V^T rows keep their 16-byte chunks XOR-permuted so that the 16 rows one MFMA
+// fragment read touches fall in distinct banks. The in-block keys arrive key-major
+// and are transposed into a stage through registers. Per block a wave computes
+// S^T = K.Q^T on v_mfma_f32_16x16x32_bf16 (keys on M, its query rows on N, Q
+// fragments held in registers), an online base-2 softmax per query row, then
+// O^T += V^T.P^T with P^T taken from the S^T accumulators; the keys of a block are
+// assigned to MFMA rows so that the 32-key contraction of the second product runs
+// over consecutive keys. The running max is raised (and the output rescaled) only
+// when a row's max grows by more than 8 (base 2): probabilities then stay below
+// 2^8, exact in fp32 and bf16 range, and both sums use the same reference.
+// With several key ranges each workgroup writes a partial (fp32 max and sum, the
+// unnormalised output in bf16) that attn_combine_kernel merges.
 // fp32 path (attn_f32_kernel): one workgroup per query row, VALU.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -37,28 +40,68 @@ __device__ __forceinline__ int attn_key_of(int mt, int m) {
   return (mt >> 1) * 32 + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
 }
 
-// 16-byte chunk c of K row r lives at chunk c ^ swz(r): the rows one MFMA operand
-// reads (attn_key_of(mt, 0..15)) map to 16 distinct values.
+// 16-byte chunk c of K row r is stored at chunk c ^ attn_kswz(r): the rows one MFMA
+// operand reads (attn_key_of(mt, 0..15)) map to 16 distinct values.
 template <int D>
-__device__ __forceinline__ int attn_swz(int r) {
+__device__ __forceinline__ int attn_kswz(int r) {
   return ((r & 3) | ((r >> 1) & 12)) & (D / 8 - 1);
+}
+// 16-byte chunk c of V^T row e (64 keys, 128 bytes) is stored at chunk c ^ attn_vswz(e).
+__device__ __forceinline__ int attn_vswz(int e) { return (e >> 1) & 7; }
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4; lds_base must be the same in every lane of the wave).
+// Written as inline assembly so that the compiler does not wait for the transfer
+// before every later LDS read: the kernel waits on vmcnt itself (wait_vm).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt <= n (n < 64), the other counters not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// max / sum of x over lanes l, l^16, l^32, l^48 (the four lane groups of one MFMA
+// column), with the gfx950 row-swap permutes (no LDS traffic)
+__device__ __forceinline__ float xmax4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int D>
-__global__ __launch_bounds__(512) void attn_part_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kb,
-                                                        const bf16* __restrict__ vb, const bf16* __restrict__ k_sel,
-                                                        const bf16* __restrict__ v_sel, AttnGeom a, float scale2,
-                                                        bf16* __restrict__ out, bf16* __restrict__ o_part,
-                                                        float2* __restrict__ ml_part) {
+__global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kb,
+                                                   const bf16* __restrict__ vb, const bf16* __restrict__ k_sel,
+                                                   const bf16* __restrict__ v_sel, AttnGeom a, float scale2,
+                                                   bf16* __restrict__ out, bf16* __restrict__ o_part,
+                                                   float2* __restrict__ ml_part) {
+  constexpr int NW = 8;              // waves: two groups of four
   constexpr int KB = kAttnKeyBlock;  // 64
   constexpr int KS = D / 32;         // contraction steps of S^T = K.Q^T
   constexpr int DT = D / 16;         // 16-dim output tiles
   constexpr int CPR = D / 8;         // 16-byte chunks per K row
-  constexpr int LDV = KB + 8;        // V^T row stride in LDS (elements)
-  constexpr int NCH = KB * CPR;      // 16-byte chunks of K (and of V) per block
-  constexpr int PT = NCH / 256;      // chunks per thread at 256 threads
-  __shared__ __align__(16) bf16 Ks[KB * D];
-  __shared__ __align__(16) bf16 Vt[D * LDV];
+  constexpr int RPI = 64 / CPR;      // K rows per load instruction
+  constexpr int NT = NW * 64;
+  constexpr int NCH = KB * CPR;      // 16-byte chunks of K (and of V^T) per block
+  constexpr int NIK = NCH / NT;      // direct-to-LDS instructions per wave per block, K
+  constexpr int NIV = NCH / NT;      //                                                V^T
+  constexpr int NIPB = NIK + NIV;
+  constexpr int STAGE = 2 * KB * D;  // elements per stage (K then V^T)
+  constexpr float kRaise = 8.f;      // the running max moves only when exceeded by this
+  static_assert(NIK >= 1 && 3 * NIPB < 64, "vmcnt budget");
+  extern __shared__ __align__(16) bf16 stages[];
+
   // 1-D grid, XCD-aware: workgroup x runs on XCD x % 8 and each XCD takes a contiguous
   // range of items; the row splits of one key range are adjacent and share an L2.
   const int per = gridDim.x >> 3;
@@ -67,19 +110,56 @@ __global__ __launch_bounds__(512) void attn_part_kernel(const bf16* __restrict__
   const int rs = li % a.nrs, ksp = (li / a.nrs) % a.nks, unit = li / (a.nrs * a.nks);
   const int B = a.B, G = a.G, topk = a.topk;
   const int s = unit / a.Hkv, g = unit % a.Hkv;
-  const int nthr = blockDim.x, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, qd = lane >> 4, lr = lane & 15;
-  const int R = B * G, nA = (topk + KB - 1) / KB, nblk = nA + 1;
-  const int b0 = ksp * a.bps, b1 = min(nblk, b0 + a.bps);
-  const int tile = rs * a.tpw + w;
-  const bool has_tile = w < a.tpw && tile * 16 < R;
+  const int tid = threadIdx.x, lane = tid & 63, qd = lane >> 4, lr = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2, wl = w & 3;
+  const int R = B * G, nA = (topk + KB - 1) / KB;
+  const int b0 = ksp * a.bps, b1 = min(nA + 1, b0 + a.bps);
+  const int has_ib = b1 == nA + 1 ? 1 : 0;  // the in-block keys belong to the last range
+  const int nb = b1 - b0;                    // blocks of this workgroup: list index 0 is the
+  const int nst = a.nst;                     // in-block block when it has one, then subset
+  const int tile = rs * a.tpw + wl;
+  const bool has_tile = wl < a.tpw && tile * 16 < R;
 
   const bf16* ksrc = k_sel + (int64_t)unit * topk * D;
   const bf16* vsrc = v_sel + (int64_t)unit * D * a.ldv;
   const bf16* kbb = kb + ((int64_t)s * B * a.Hkv + g) * D;  // in-block key b at kbb + b * Hkv * D
   const bf16* vbb = vb + ((int64_t)s * B * a.Hkv + g) * D;
   const int64_t bstride = (int64_t)a.Hkv * D;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)stages;
 
+  // ---- per-lane parts of the direct-to-LDS addresses (the block only adds a base)
+  int koff[NIK], voff[NIV], krow[NIK];
+#pragma unroll
+  for (int u = 0; u < NIK; ++u) {
+    const int r = (u * NW + w) * RPI + lane / CPR;
+    krow[u] = r;
+    koff[u] = (lane % CPR ^ attn_kswz<D>(r)) * 8;
+  }
+#pragma unroll
+  for (int u = 0; u < NIV; ++u) {
+    const int e = (u * NW + w) * 8 + lane / 8;
+    voff[u] = e * (int)a.ldv + ((lane % 8) ^ attn_vswz(e)) * 8;
+  }
+  // list index i >= has_ib is subset block b0 + i - has_ib, in stage i % nst
+  auto issue = [&](int i) {
+    const int blk = b0 + i - has_ib;
+    const uint32_t sk = lds0 + (uint32_t)((i % nst) * STAGE) * 2u;
+    const uint32_t sv = sk + KB * D * 2;
+    const bool full = blk * KB + KB <= topk;
+#pragma unroll
+    for (int u = 0; u < NIK; ++u) {
+      const int key = full ? blk * KB + krow[u] : min(blk * KB + krow[u], topk - 1);
+      lds_dma16(ksrc + (int64_t)key * D + koff[u], sk + (uint32_t)((u * NW + w) * RPI * D) * 2u);
+    }
+#pragma unroll
+    for (int u = 0; u < NIV; ++u)
+      lds_dma16(vsrc + (int64_t)blk * KB + voff[u], sv + (uint32_t)((u * NW + w) * 8 * KB) * 2u);
+  };
+  int next = has_ib;  // next list index to fetch
+  for (; next < min(nb, nst); ++next) issue(next);
+
+  // ---- query fragments of this wave's tile
   uint4 qf[KS];
   {
     const int r = tile * 16 + lr;
@@ -88,112 +168,117 @@ __global__ __launch_bounds__(512) void attn_part_kernel(const bf16* __restrict__
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = qr ? ld16(qr + ks * 32) : make_uint4(0, 0, 0, 0);
   }
-
-  // ---- staging: chunk c of K is row c / CPR, chunk c % CPR; chunk c of V^T is, for the
-  //      subset (d-major in memory), dim c / 8, keys 8*(c % 8) ..; for the in-block keys
-  //      (key-major in memory), key c % 64, dims 8*(c / 64) .. (transposed into LDS).
-  uint4 kreg[PT], vreg[PT];
-  auto fetch = [&](int blk) {
-    const bool sub = blk < nA;
+  // ---- in-block keys (list index 0, stage 0): K rows and V^T (transposed) via registers
+  if (has_ib) {
+    constexpr int PT = NCH / NT;
+    uint4 kst[PT], vst[PT];
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int c = tid + i * nthr;
-      kreg[i] = vreg[i] = make_uint4(0, 0, 0, 0);
-      if (c < NCH) {
-        const int r = c / CPR, ch = c % CPR;
-        if (sub) {
-          kreg[i] = ld16(ksrc + (int64_t)min(blk * KB + r, topk - 1) * D + ch * 8);
-          vreg[i] = ld16(vsrc + (int64_t)(c >> 3) * a.ldv + blk * KB + (c & 7) * 8);
-        } else {
-          if (r < B) kreg[i] = ld16(kbb + r * bstride + ch * 8);
-          if ((c & 63) < B) vreg[i] = ld16(vbb + (c & 63) * bstride + (c >> 6) * 8);
-        }
+      const int c = tid + i * NT;
+      const int r = c / CPR, ch = c % CPR;
+      kst[i] = vst[i] = make_uint4(0, 0, 0, 0);
+      if (r < B) {
+        kst[i] = ld16(kbb + r * bstride + ch * 8);
+        vst[i] = ld16(vbb + r * bstride + ch * 8);
       }
     }
-  };
-  auto stash = [&](int blk) {
-    const bool sub = blk < nA;
+    bf16* sk = stages;
+    bf16* sv = stages + KB * D;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int c = tid + i * nthr;
-      if (c < NCH) {
-        const int r = c / CPR, ch = c % CPR;
-        *reinterpret_cast<uint4*>(&Ks[r * D + ((ch ^ attn_swz<D>(r)) * 8)]) = kreg[i];
-        if (sub) {
-          *reinterpret_cast<uint4*>(&Vt[(c >> 3) * LDV + (c & 7) * 8]) = vreg[i];
-        } else {
-          const int key = c & 63, e8 = (c >> 6) * 8;
-          const uint32_t xs[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-          uint16_t* vt = reinterpret_cast<uint16_t*>(Vt);
+      const int c = tid + i * NT;
+      const int r = c / CPR, ch = c % CPR;
+      *reinterpret_cast<uint4*>(sk + r * D + ((ch ^ attn_kswz<D>(r)) * 8)) = kst[i];
+      const uint32_t xs[4] = {vst[i].x, vst[i].y, vst[i].z, vst[i].w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vt[(e8 + 2 * j) * LDV + key] = (uint16_t)(xs[j] & 0xffffu);
-            vt[(e8 + 2 * j + 1) * LDV + key] = (uint16_t)(xs[j] >> 16);
-          }
-        }
+      for (int t = 0; t < 4; ++t) {
+        const int e0 = ch * 8 + 2 * t;
+        sv[e0 * KB + (((r >> 3) ^ attn_vswz(e0)) * 8) + (r & 7)] = (bf16)(xs[t] & 0xffffu);
+        sv[(e0 + 1) * KB + (((r >> 3) ^ attn_vswz(e0 + 1)) * 8) + (r & 7)] = (bf16)(xs[t] >> 16);
       }
     }
-  };
+  }
 
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  fetch(b0);
-  for (int blk = b0; blk < b1; ++blk) {
-    if (blk > b0) __syncthreads();  // every wave is done with the previous block
-    stash(blk);
-    __syncthreads();
-    if (blk + 1 < b1) fetch(blk + 1);
-    if (!has_tile) continue;
+  for (int j = 0; j < nb; j += 2) {
+    // wait for this wave's loads of the subset blocks among j, j + 1
+    const int need = min(j + 1, nb - 1);
+    if (need >= has_ib) {
+      const int later = next - 1 - need;  // subset blocks fetched after it
+      if (later <= 0) wait_vm<0>();
+      else if (later == 1) wait_vm<NIPB>();
+      else if (later == 2) wait_vm<2 * NIPB>();
+      else wait_vm<3 * NIPB>();
+    }
+    __syncthreads();  // blocks j, j + 1 are in LDS; every wave is done with j - 2, j - 1
+    for (; next < nb && next < j + nst; ++next) issue(next);
 
-    // ---- S^T = K Q^T: lane holds keys attn_key_of(mt, 4*qd + i) of query row lr
+    const int i = j + grp;  // this group's block
+    if (i >= nb || !has_tile) continue;
+    const bf16* sk = stages + (i % nst) * STAGE;
+    const bf16* sv = sk + KB * D;
+    const int valid = (i < has_ib) ? B : min(KB, topk - (b0 + i - has_ib) * KB);
+
+    // ---- S^T = K Q^T: lane holds keys attn_key_of(mt, 4*qd + i) of query row lr. All
+    //      fragment reads of a product are issued before its first MFMA; the V^T
+    //      fragments are read while the softmax runs.
+    uint4 kf[4][KS];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int r = attn_key_of(mt, lr);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[mt][ks] = *reinterpret_cast<const uint4*>(sk + r * D + (((ks * 4 + qd) ^ attn_kswz<D>(r)) * 8));
+    }
     f32x4_t sacc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int r = attn_key_of(mt, lr);
-        const uint4 kf = *reinterpret_cast<const uint4*>(&Ks[r * D + (((ks * 4 + qd) ^ attn_swz<D>(r)) * 8)]);
-        sacc[mt] = mfma16x16x32(kf, qf[ks], sacc[mt]);
+      for (int mt = 0; mt < 4; ++mt) sacc[mt] = mfma16x16x32(kf[mt][ks], qf[ks], sacc[mt]);
+    uint4 vf[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int e = dt * 16 + lr;
+        vf[dt][h2] = *reinterpret_cast<const uint4*>(sv + e * KB + (((h2 * 4 + qd) ^ attn_vswz(e)) * 8));
       }
 
-    // ---- online softmax (base 2); the scale is folded into one FMA; the output is
-    //      rescaled only when some row's running max grows (otherwise every factor is 1)
-    const int valid = blk < nA ? topk - blk * KB : B;
+    // ---- online softmax (base 2) with the scale folded into one FMA
     if (valid < KB) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (attn_key_of(mt, 4 * qd + i) >= valid) sacc[mt][i] = -INFINITY;
+        for (int t = 0; t < 4; ++t)
+          if (attn_key_of(mt, 4 * qd + t) >= valid) sacc[mt][t] = -INFINITY;
     }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sacc[mt][i]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm * scale2);
-    if (__ballot(mn > m)) {
+    float bm = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
+                         fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
+    bm = xmax4(bm) * scale2;
+    if (__ballot(bm > m + kRaise)) {
+      const float mn = fmaxf(m, bm);
       const float alpha = fast_exp2(m - mn);
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m = mn;
     }
-    m = mn;
     float p[4][4];
     float ps = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[mt][i] = fast_exp2(fmaf(sacc[mt][i], scale2, -mn));
-        ps += p[mt][i];
+      for (int t = 0; t < 4; ++t) {
+        p[mt][t] = fast_exp2(fmaf(sacc[mt][t], scale2, -m));
+        ps += p[mt][t];
       }
     l += ps;
     uint4 bp[2];
@@ -207,15 +292,40 @@ __global__ __launch_bounds__(512) void attn_part_kernel(const bf16* __restrict__
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(&Vt[(dt * 16 + lr) * LDV + h2 * 32 + qd * 8]);
-        o[dt] = mfma16x16x32(vf, bp[h2], o[dt]);
-      }
+      for (int h2 = 0; h2 < 2; ++h2) o[dt] = mfma16x16x32(vf[dt][h2], bp[h2], o[dt]);
   }
-  if (!has_tile) return;
+  l = xsum4(l);
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  // ---- merge the two groups through LDS (the stages are free once all waves are here)
+  constexpr int LDO = D + 4;
+  float* xo = reinterpret_cast<float*>(stages);  // [4 tiles][16 rows][LDO]
+  float2* xml = reinterpret_cast<float2*>(xo + 4 * 16 * LDO);
+  __syncthreads();
+  if (grp == 1 && has_tile) {
+    float* orow = xo + (wl * 16 + lr) * LDO + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(orow + dt * 16) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (qd == 0) xml[wl * 16 + lr] = make_float2(m, l);
+  }
+  __syncthreads();
+  if (grp == 1 || !has_tile) return;
+  {
+    const float2 mb = xml[wl * 16 + lr];
+    const float M = fmaxf(m, mb.x);
+    const float fa = fast_exp2(m - M), fb = mb.x == -INFINITY ? 0.f : fast_exp2(mb.x - M);
+    l = l * fa + mb.y * fb;
+    m = M;
+    const float* orow = xo + (wl * 16 + lr) * LDO + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float4 ob = *reinterpret_cast<const float4*>(orow + dt * 16);
+      o[dt][0] = o[dt][0] * fa + ob.x * fb;
+      o[dt][1] = o[dt][1] * fa + ob.y * fb;
+      o[dt][2] = o[dt][2] * fa + ob.z * fb;
+      o[dt][3] = o[dt][3] * fa + ob.w * fb;
+    }
+  }
   const int r = tile * 16 + lr;
   if (a.nks == 1) {
     if (r >= R) return;
@@ -240,8 +350,8 @@ __global__ __launch_bounds__(512) void attn_part_kernel(const bf16* __restrict__
 // the ranges taken 8 at a time (loads first) with a running (max, sum).
 template <int D>
 __global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict__ o_part,
-                                                           const float2* __restrict__ ml_part, AttnGeom a,
-                                                           bf16* __restrict__ out) {
+                                                          const float2* __restrict__ ml_part, AttnGeom a,
+                                                          bf16* __restrict__ out) {
   constexpr int CH = 8;
   const int idx = blockIdx.x * 64 + threadIdx.x;
   const int R = a.B * a.G;
@@ -350,8 +460,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------ host side
 
-// Work split: up to 8 query tiles (waves) per workgroup, then enough key ranges to
-// give about kAttnTargetWorkgroups workgroups, at most kAttnMaxSplits ranges.
+// Work split: up to four 16-row query tiles per workgroup, and key ranges of at most
+// kAttnBlocksPerRange blocks.
 AttnGeom attn_geom(const Shape& s) {
   AttnGeom a{};
   a.B = s.B;
@@ -362,16 +472,24 @@ AttnGeom attn_geom(const Shape& s) {
   a.ldv = vsel_ld(s.topk);
   a.nunits = s.nseq * s.Hkv;
   const int ntiles = (s.B * s.G + 15) / 16;
-  a.tpw = ntiles <= 8 ? ntiles : (ntiles + 1) / 2;
+  const int nblk = (s.topk + kAttnKeyBlock - 1) / kAttnKeyBlock + 1;
+  a.tpw = std::min(ntiles, 4);
   a.nrs = (ntiles + a.tpw - 1) / a.tpw;
   a.rpad = ntiles * 16;
-  const int nblk = (s.topk + kAttnKeyBlock - 1) / kAttnKeyBlock + 1;
-  const int64_t groups = (int64_t)a.nunits * a.nrs;
-  int nks = (int)std::min<int64_t>(std::max<int64_t>(1, (kAttnTargetWorkgroups + groups - 1) / groups),
-                                   std::min(nblk, kAttnMaxSplits));
+  // A workgroup keeps at most kAttnMaxStages blocks in flight, so one pulling a long
+  // range is bound by memory latency: with few (sequence, KV head) pairs the keys are
+  // split into ranges of about kAttnMaxStages blocks, to spread them over enough
+  // workgroups (the ranges are then merged by attn_combine_kernel).
+  const int groups = a.nunits * a.nrs;
+  const int spread = std::min((kAttnTargetWorkgroups + groups - 1) / groups,
+                              (nblk + kAttnMaxStages - 1) / kAttnMaxStages);
+  const int nks = std::max((nblk + kAttnBlocksPerRange - 1) / kAttnBlocksPerRange, spread);
   a.bps = (nblk + nks - 1) / nks;
   a.nks = (nblk + a.bps - 1) / a.bps;
-  a.nitems = (int)(groups * a.nks);
+  // a range of at most kAttnMaxStages blocks is fetched at once; longer ranges cycle
+  // through kAttnMaxStages stages (two blocks in use, the next two in flight)
+  a.nst = std::min(a.bps, kAttnMaxStages);
+  a.nitems = a.nunits * a.nrs * a.nks;
   return a;
 }
 
@@ -383,6 +501,47 @@ size_t attn_ws_bytes(const Shape& s) {
   if (a.nks == 1) return 0;
   const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
   return align256(rows * s.D * sizeof(bf16)) + align256(rows * sizeof(float2));
+}
+
+template <int D>
+static size_t attn_smem(const AttnGeom& a) {
+  const size_t stages = (size_t)a.nst * 2 * kAttnKeyBlock * D * sizeof(bf16);
+  const size_t merge = (size_t)4 * 16 * (D + 4) * sizeof(float) + 4 * 16 * sizeof(float2);
+  return std::max(stages, merge);
+}
+
+template <int D>
+static hipError_t launch_attn_bf16(const AttnGeom& a, const void* q, const void* kb, const void* vb,
+                                   const void* k_sel, const void* v_sel, void* out, void* ws, float scale2,
+                                   hipStream_t st) {
+  bf16* o_part = nullptr;
+  float2* ml_part = nullptr;
+  if (a.nks > 1) {
+    const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
+    o_part = static_cast<bf16*>(ws);
+    ml_part = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(rows * D * sizeof(bf16)));
+  }
+  const size_t smem = attn_smem<D>(a);
+  hipError_t e = allow_smem((const void*)attn_kernel<D>, smem);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((a.nitems + 7) / 8 * 8));
+  klaunch(attn_kernel<D>, grid, 512, smem, st, (const bf16*)q, (const bf16*)kb, (const bf16*)vb, (const bf16*)k_sel,
+          (const bf16*)v_sel, a, scale2, (bf16*)out, o_part, ml_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t st) {
+  const AttnGeom a = attn_geom(s);
+  const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
+  const bf16* o_part = static_cast<const bf16*>(ws);
+  const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(bf16)));
+  const int64_t n = (int64_t)a.nunits * a.B * a.G * (s.D / 4);
+  const dim3 grid((unsigned)((n + 63) / 64));
+  if (s.D == 128)
+    klaunch(attn_combine_kernel<128>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
+  else
+    klaunch(attn_combine_kernel<64>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void* vb, const void* k_sel,
@@ -402,36 +561,8 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
     return hipGetLastError();
   }
   const AttnGeom a = attn_geom(s);
-  bf16* o_part = nullptr;
-  float2* ml_part = nullptr;
-  if (a.nks > 1) {
-    const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
-    o_part = static_cast<bf16*>(ws);
-    ml_part = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(bf16)));
-  }
-  const dim3 grid((unsigned)((a.nitems + 7) / 8 * 8));
-  const int threads = 64 * std::max(4, a.tpw);
-  if (s.D == 128)
-    klaunch(attn_part_kernel<128>, grid, threads, 0, st, (const bf16*)q, (const bf16*)kb, (const bf16*)vb,
-            (const bf16*)k_sel, (const bf16*)v_sel, a, scale2, (bf16*)out, o_part, ml_part);
-  else
-    klaunch(attn_part_kernel<64>, grid, threads, 0, st, (const bf16*)q, (const bf16*)kb, (const bf16*)vb,
-            (const bf16*)k_sel, (const bf16*)v_sel, a, scale2, (bf16*)out, o_part, ml_part);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t st) {
-  const AttnGeom a = attn_geom(s);
-  const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
-  const bf16* o_part = static_cast<const bf16*>(ws);
-  const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(bf16)));
-  const int64_t n = (int64_t)a.nunits * s.B * s.G * (s.D / 4);
-  const dim3 grid((unsigned)((n + 63) / 64));
-  if (s.D == 128)
-    klaunch(attn_combine_kernel<128>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
-  else
-    klaunch(attn_combine_kernel<64>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
-  return hipGetLastError();
+  if (s.D == 128) return launch_attn_bf16<128>(a, q, kb, vb, k_sel, v_sel, out, ws, scale2, st);
+  return launch_attn_bf16<64>(a, q, kb, vb, k_sel, v_sel, out, ws, scale2, st);
 }
 
 }  // namespace herald

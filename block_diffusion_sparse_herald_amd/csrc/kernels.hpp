@@ -62,10 +62,12 @@ struct AttnGeom {
   int rpad;    // rows rounded up to whole tiles
   int nks;     // key ranges per unit
   int bps;     // 64-key blocks per key range
+  int nst;     // LDS stages (blocks in flight) per workgroup
   int nitems;  // workgroups
 };
-constexpr int kAttnTargetWorkgroups = 512;
-constexpr int kAttnMaxSplits = 32;
+constexpr int kAttnBlocksPerRange = 32;
+constexpr int kAttnTargetWorkgroups = 96;
+constexpr int kAttnMaxStages = 4;
 
 // select
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);

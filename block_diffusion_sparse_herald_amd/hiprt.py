@@ -28,6 +28,7 @@ class Hip:
             "hipMalloc": [ctypes.POINTER(_vp), ctypes.c_size_t],
             "hipFree": [_vp],
             "hipMemcpy": [_vp, _vp, ctypes.c_size_t, ctypes.c_int],
+            "hipMemset": [_vp, ctypes.c_int, ctypes.c_size_t],
             "hipMemcpyAsync": [_vp, _vp, ctypes.c_size_t, ctypes.c_int, _vp],
             "hipDeviceSynchronize": [],
             "hipStreamCreate": [ctypes.POINTER(_vp)],
@@ -65,6 +66,9 @@ class Hip:
         p = _vp()
         self.check(self.lib.hipMalloc(ctypes.byref(p), max(int(nbytes), 256)), "hipMalloc")
         return p.value
+
+    def memset(self, ptr: int, value: int, nbytes: int) -> None:
+        self.check(self.lib.hipMemset(ptr, value, nbytes), "hipMemset")
 
     def free(self, ptr: int) -> None:
         self.check(self.lib.hipFree(ptr), "hipFree")
@@ -136,12 +140,14 @@ class Hip:
 class DevArray:
     """A device allocation with a shape and a host dtype (for copies back)."""
 
-    def __init__(self, hip: Hip, shape, dtype):
+    def __init__(self, hip: Hip, shape, dtype, zero: bool = False):
         self.hip = hip
         self.shape = tuple(int(x) for x in shape)
         self.dtype = np.dtype(dtype)
         self.nbytes = int(np.prod(self.shape, dtype=np.int64)) * self.dtype.itemsize
         self.ptr = hip.malloc(self.nbytes)
+        if zero:
+            hip.memset(self.ptr, 0, self.nbytes)
 
     @classmethod
     def from_host(cls, hip: Hip, a: np.ndarray) -> "DevArray":

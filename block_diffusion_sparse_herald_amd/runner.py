@@ -33,10 +33,10 @@ def batch_to_device(batch, device="cuda") -> dict:
 def torch_alloc(device="cuda") -> Callable:
     import torch
 
-    def alloc(shape, dtype):
+    def alloc(shape, dtype, zero=False):
         dt = {np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32,
               np.dtype(np.uint16): torch.bfloat16, np.dtype(np.uint8): torch.uint8}[np.dtype(dtype)]
-        return torch.empty(tuple(shape), dtype=dt, device=device)
+        return (torch.zeros if zero else torch.empty)(tuple(shape), dtype=dt, device=device)
 
     return alloc
 
@@ -44,9 +44,10 @@ def torch_alloc(device="cuda") -> Callable:
 class BlockRunner:
     """Outputs and workspaces for one (workload shape, sequence offsets).
 
-    `alloc(shape, numpy_dtype)` returns device memory exposing data_ptr() and nbytes
-    (uint16 stands for bf16); `seq_start_dev` is the device copy of the offsets
-    (made with the allocator's framework when omitted).
+    `alloc(shape, numpy_dtype, zero=False)` returns device memory exposing data_ptr() and
+    nbytes (uint16 stands for bf16), zero-filled when asked (the attention workspace);
+    `seq_start_dev` is the device copy of the offsets (made with the allocator's
+    framework when omitted).
     """
 
     def __init__(self, seq_start, B, Hq, Hkv, d, C, topk, dtype: str, softmax_scale: float = 0.0, device="cuda",
@@ -69,7 +70,7 @@ class BlockRunner:
         self.ws = {}
         for name, op in [("select", H.HERALD_OP_SELECT), ("refine", H.HERALD_OP_REFINE), ("attn", H.HERALD_OP_ATTN)]:
             n = H.herald_workspace_size(self.problem, op)
-            self.ws[name] = alloc((max(n, 256),), np.uint8)
+            self.ws[name] = alloc((max(n, 256),), np.uint8, zero=name == "attn")
         self.attn_splits = H.herald_attn_splits(self.problem)
 
     def select(self, q_merge, k_cache, stream=None):

@@ -164,8 +164,9 @@ herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const
  *   v_blk  [nseq][B][Hkv][d]  device, read
  *   k_sel, v_sel              device, read, as written by herald_gather_kv
  *   out    [nseq][B][Hq][d]   device, written (fp32 accumulation, rounded to the dtype)
- *   ws     workspace of herald_workspace_size(HERALD_OP_ATTN) bytes, device (fp32
- *          partial results of the key ranges; NULL allowed when that size is 0)
+ *   ws     workspace of herald_workspace_size(HERALD_OP_ATTN) bytes, device: partial
+ *          results when the subset is long enough to be split into key ranges;
+ *          NULL allowed when that size is 0
  */
 herald_status herald_block_attn(const herald_problem* p, const void* q, const void* k_blk, const void* v_blk,
                                 const void* k_sel, const void* v_sel, void* out, void* ws, size_t ws_bytes,
@@ -178,8 +179,8 @@ const char* herald_last_error(void);
 /*
  * Instrumentation. Kernel ids: 0 merged-query scan, 1 selection scores + first
  * radix digit, 2 second and third radix digits, 3 candidate emission, 4 refine
- * statistics, 5 refine scores, 6 final top-K, 7 gather, 8 block attention
- * (per key range), 9 merge of the key ranges. While set (non-NULL), every launch of that kernel on a
+ * statistics, 5 refine scores, 6 final top-K, 7 gather, 8 block attention,
+ * 9 merge of the attention key ranges (long subsets only). While set (non-NULL), every launch of that kernel on a
  * call's stream is bracketed by records of start and stop on the same stream
  * (external event nodes when the stream is being captured into a graph); the last
  * launch wins. Pass NULL events to clear. Thread-local setting.
