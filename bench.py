@@ -48,39 +48,25 @@ def kernel_work(wl, lengths):
         "refine_scores": ("mfma", 2.0 * wl.nseq * wl.Hq * wl.B * wl.C * wl.d),
         # gather reads and writes topk rows of K and V
         "gather": ("hbm", 2 * 2 * wl.nseq * wl.Hkv * wl.topk * wl.d * esz),
-        # attention: QK^T and PV over topk + B keys for every query row
-        "attn": ("mfma", 4.0 * wl.nseq * wl.Hq * wl.B * nk * wl.d),
+        # attention (one call): 4*Hq*B*(topk+B)*d flop over the subset K/V, the step's
+        # queries, in-block keys/values and outputs, i.e. ~114 flop/byte at G=4, below
+        # MI355X's ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/byte): bound by memory
+        "attn": ("hbm", esz * wl.nseq * (2 * wl.Hkv * wl.topk * wl.d + 2 * wl.B * wl.Hq * wl.d
+                                         + 2 * wl.B * wl.Hkv * wl.d)),
     }
-
-
-# kernel name in the roofline -> the sources its code comes from (traffic figures are void once they change)
-KERNEL_SOURCES = {
-    "attn_kernel": ["attn.hip", "common.hpp"],
-    "scan": ["select.hip", "common.hpp"],
-    "refine_stats": ["refine.hip", "common.hpp"],
-    "refine_scores": ["refine.hip", "common.hpp"],
-    "gather": ["gather.hip", "common.hpp"],
-}
-
-
-def sources_digest(files) -> str:
-    import hashlib
-
-    h = hashlib.sha256()
-    for f in files:
-        h.update(open(os.path.join(ROOT, "block_diffusion_sparse_herald_amd", "csrc", f), "rb").read())
-    return h.hexdigest()
 
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter runs, if the kernel is unchanged since."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+    from block_diffusion_sparse_herald_amd.profiling import KERNELS, sources_digest
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path) or kernel not in KERNELS:
         return None
+    digest = sources_digest(KERNELS[kernel][1])
     for e in json.load(open(path)).get("entries", []):
-        if e["kernel"] == kernel and e["workload"] == workload:
-            if e["sources_sha256"] == sources_digest(KERNEL_SOURCES[kernel]):
-                return e["bytes_per_launch"]
+        if e["kernel"] == kernel and e["sources_sha256"] == digest:
+            return e["bytes_per_launch"]
     return None
 
 
@@ -156,7 +142,7 @@ def main(argv=None):
 
     call_of = {"scan": "select", "score_hist": "select", "radix": "select", "emit": "select",
                "refine_stats": "refine", "refine_scores": "refine", "refine_select": "refine",
-               "gather": "gather", "attn": "attn"}
+               "gather": "gather", "attn": "attn", "attn_combine": "attn"}
 
     def step(i, timed=None, events=None, capturing=False):
         """One block per sequence. With `timed`, `events` bracket that kernel in one launch of
@@ -189,7 +175,8 @@ def main(argv=None):
         step(i)
     hip.sync()
     launches = {"scan": 1, "score_hist": 1, "radix": 2, "emit": 1, "refine_stats": 1 if wl.dtype == "bf16" else 0,
-                "refine_scores": 1, "refine_select": 1 if wl.dtype == "bf16" else 0, "gather": 1, "attn": wl.T}
+                "refine_scores": 1, "refine_select": 1 if wl.dtype == "bf16" else 0, "gather": 1, "attn": wl.T,
+                "attn_combine": wl.T if r.attn_splits > 1 else 0}
     per_launch_us = {}
     for name, n in launches.items():
         if n == 0:
@@ -202,6 +189,7 @@ def main(argv=None):
             times.append(hip.elapsed_ms(st, sp) * 1e3)
         per_launch_us[name] = float(np.median(times))
     per_step_us = {k: per_launch_us[k] * launches[k] for k in per_launch_us}
+    per_step_us["attn"] += per_step_us.get("attn_combine", 0.0)  # one attention call: both kernels
     dominant = max((k for k in per_step_us if k in ("scan", "refine_stats", "refine_scores", "gather", "attn")),
                    key=lambda k: per_step_us[k])
     log(f"[bench] per-launch us: {json.dumps({k: round(v, 2) for k, v in per_launch_us.items()})}; "
@@ -209,9 +197,9 @@ def main(argv=None):
 
     # Timed region: K steps, each replayed from a HIP graph captured from the same calls, which
     # takes the host out of the loop (--eager launches directly). Every step carries its own
-    # event pair around the dominant operation: for attention, the whole phase of T calls,
-    # divided by T (an event can be recorded only once per graph); otherwise the one launch
-    # of the dominant kernel.
+    # event pair around the dominant operation: for attention, the whole phase of T calls
+    # (attention kernel and, for split key ranges, their merge), divided by T (an event can
+    # be recorded only once per graph); otherwise the one launch of the dominant kernel.
     timed = "attn_op" if dominant == "attn" else dominant
     nper = wl.T if timed == "attn_op" else 1
     evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
@@ -259,7 +247,8 @@ def main(argv=None):
         achieved = work / (dom_us * 1e-6) / 1e12
         peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
         unit = "TFLOP/s"
-    rkernel = "attn_kernel" if timed == "attn_op" else dominant
+    rkernel = ("attn_kernel+attn_combine_kernel" if r.attn_splits > 1 else "attn_kernel") if timed == "attn_op" \
+        else dominant
     roofline = {"kernel": rkernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(rkernel, wl.name),
                 "avg_launch_us": round(dom_us, 3)}

@@ -1,0 +1,147 @@
+"""Summaries of rocprofv3 output for the benchmark's profiles (no GPU needed).
+
+    python -m block_diffusion_sparse_herald_amd.profiling --workload W \
+        --stats DIR --fetch DIR --write DIR --copy-bytes N --out-dir profiles
+
+reads the CSV output of three rocprofv3 runs of bench.py (kernel trace + stats; one
+FETCH_SIZE pass; one WRITE_SIZE pass), and writes
+  profiles/kernel_stats_<W>.md   per-kernel average duration (kernel trace),
+  profiles/hbm_traffic_<W>.json  HBM bytes per launch of the profiled kernels.
+The counters read in KiB per dispatch; each is scaled by what it reads for a copy of
+known size (the benchmark's K/V replica copies, `--copy-bytes` each), so the figures
+are bytes as the copy defines them. The JSON records a digest of the kernel sources;
+bench.py reports the traffic only while the sources are unchanged.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "block_diffusion_sparse_herald_amd", "csrc")
+
+# profiled kernel (as the benchmark names it) -> (kernel name prefixes, source files)
+KERNELS = {
+    "attn_kernel+attn_combine_kernel": (["herald::attn_kernel", "herald::attn_combine_kernel"], ["attn.hip", "common.hpp"]),
+    "attn_kernel": (["herald::attn_kernel"], ["attn.hip", "common.hpp"]),
+    "scan": (["herald::scan_mfma_kernel"], ["select.hip", "common.hpp"]),
+    "refine_stats": (["herald::refine_stats_kernel"], ["refine.hip", "common.hpp"]),
+    "refine_scores": (["herald::refine_scores_kernel"], ["refine.hip", "common.hpp"]),
+    "gather": (["herald::gather_kernel"], ["gather.hip", "common.hpp"]),
+}
+
+
+def sources_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short(name: str) -> str:
+    n = name.split("(")[0]
+    return n[5:] if n.startswith("void ") else n
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def kernel_stats(stats_dir: str):
+    rows = []
+    with open(_one(os.path.join(stats_dir, "**", "*kernel_stats.csv"))) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return rows
+
+
+def counter_means(pmc_dir: str, counter: str):
+    """kernel short name -> list of per-dispatch values (KiB), and the copy kernels' values."""
+    per = defaultdict(list)
+    with open(_one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            per[(short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return per
+
+
+def copy_factor(per, copy_bytes: int) -> tuple[float, float]:
+    """KiB the counter should read per replica copy / KiB it reads (largest copy dispatches)."""
+    copies = [(g, v) for (k, g), v in per.items() if "copyBuffer" in k]
+    if not copies:
+        raise RuntimeError("no copy kernel in the counter run")
+    g, vals = max(copies, key=lambda x: x[0])
+    measured = sum(vals) / len(vals)
+    return (copy_bytes / 1024.0) / measured, measured
+
+
+def per_launch_kib(per, prefixes) -> float:
+    total = 0.0
+    for pre in prefixes:
+        vals = [v for (k, _), vs in per.items() if k.startswith(pre) for v in vs]
+        if not vals:
+            raise RuntimeError(f"no dispatch of {pre} in the counter run")
+        total += sum(vals) / len(vals)
+    return total
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--copy-bytes", type=int, required=True)
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--stats-cmd", default="")
+    ap.add_argument("--pmc-cmd", default="")
+    args = ap.parse_args(argv)
+    os.makedirs(args.out_dir, exist_ok=True)
+
+    stats = kernel_stats(args.stats)
+    md = [f"# Kernel durations, workload {args.workload}", "",
+          "rocprofv3 kernel trace of the benchmark (HIP graph replays, one block per sequence per step).", "",
+          "Command:", "", "```", args.stats_cmd, "```", "",
+          "| kernel | calls | average us | min us | max us | % of kernel time |", "|---|---|---|---|---|---|"]
+    for n, c, avg, mn, mx, pct in sorted(stats, key=lambda x: -x[5]):
+        md.append(f"| `{n}` | {c} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
+    with open(os.path.join(args.out_dir, f"kernel_stats_{args.workload}.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+
+    fetch = counter_means(args.fetch, "FETCH_SIZE")
+    write = counter_means(args.write, "WRITE_SIZE")
+    ff, fcopy = copy_factor(fetch, args.copy_bytes)
+    fw, wcopy = copy_factor(write, args.copy_bytes)
+    entries = []
+    for kname, (prefixes, files) in KERNELS.items():
+        try:
+            fk, wk = per_launch_kib(fetch, prefixes), per_launch_kib(write, prefixes)
+        except RuntimeError:
+            continue
+        entries.append({"kernel": kname, "workload": args.workload, "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                        "bytes_per_launch": round((fk * ff + wk * fw) * 1024.0),
+                        "sources_sha256": sources_digest(files)})
+    doc = {"calibration": {"copy_bytes": args.copy_bytes, "fetch_kib_per_copy": round(fcopy, 1),
+                           "write_kib_per_copy": round(wcopy, 1), "fetch_factor": round(ff, 4),
+                           "write_factor": round(fw, 4)},
+           "command": args.pmc_cmd, "entries": entries}
+    with open(os.path.join(args.out_dir, f"hbm_traffic_{args.workload}.json"), "w") as fh:
+        json.dump(doc, fh, indent=1)
+    print(json.dumps(doc["calibration"]), len(entries), "kernels")
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
