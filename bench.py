@@ -116,7 +116,7 @@ def main(argv=None):
     import numpy as np
 
     from block_diffusion_sparse_herald_amd import herald as H
-    from block_diffusion_sparse_herald_amd.hiprt import DevArray, Hip
+    from block_diffusion_sparse_herald_amd.hiprt import DevArray, Hip, HipError
     from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, make_batch
     from block_diffusion_sparse_herald_amd.runner import BlockRunner
 
@@ -186,8 +186,12 @@ def main(argv=None):
             st, sp = hip.event(), hip.event()
             step(rep, name, (st, sp))
             hip.sync()
-            times.append(hip.elapsed_ms(st, sp) * 1e3)
-        per_launch_us[name] = float(np.median(times))
+            try:
+                times.append(hip.elapsed_ms(st, sp) * 1e3)
+            except HipError:  # this kernel is not launched for this shape
+                break
+        if times:
+            per_launch_us[name] = float(np.median(times))
     per_step_us = {k: per_launch_us[k] * launches[k] for k in per_launch_us}
     per_step_us["attn"] += per_step_us.get("attn_combine", 0.0)  # one attention call: both kernels
     dominant = max((k for k in per_step_us if k in ("scan", "refine_stats", "refine_scores", "gather", "attn")),

@@ -56,6 +56,7 @@ herald_status ok() {
 // the kernel on every replay.
 #define HERALD_LAUNCH(id, stream, call)                                                     \
   do {                                                                                      \
+    (void)hipGetLastError(); /* the launcher reports hipGetLastError(): start clean */      \
     if (g_events[id].start) HERALD_HIP(record_event(g_events[id].start, stream));           \
     HERALD_HIP(call);                                                                       \
     if (g_events[id].stop) HERALD_HIP(record_event(g_events[id].stop, stream));             \
@@ -231,9 +232,13 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
   HERALD_HIP(launch_merge(s, q_merge, w, stream));
   HERALD_LAUNCH(0, stream, launch_scan(s, k_cache, w, stream));
   HERALD_LAUNCH(1, stream, launch_score_hist(s, w, stream));
-  HERALD_LAUNCH(2, stream, launch_radix_pass(s, w, 2, stream));
-  HERALD_LAUNCH(2, stream, launch_radix_pass(s, w, 3, stream));
-  HERALD_LAUNCH(3, stream, launch_emit_candidates(s, w, cand_idx, cand_score, stream));
+  if (topc_in_lds(s)) {
+    HERALD_LAUNCH(3, stream, launch_topc_lds(s, w, cand_idx, cand_score, stream));
+  } else {
+    HERALD_LAUNCH(2, stream, launch_radix_pass(s, w, 2, stream));
+    HERALD_LAUNCH(2, stream, launch_radix_pass(s, w, 3, stream));
+    HERALD_LAUNCH(3, stream, launch_emit_candidates(s, w, cand_idx, cand_score, stream));
+  }
   return ok();
 }
 

@@ -103,18 +103,27 @@ __device__ __forceinline__ void ms_wave_merge(float& m, float& s) {
 
 // ---------------------------------------------------------------- block-wide scans
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (no LDS traffic): row
+// shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes shifted in from outside
+// the row read 0), then the last lane of row 0 (and of row 2) is broadcast into the
+// next row, and the last lane of row 1 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // Exclusive prefix sum of `v` over the NT threads of the block (NT multiple of 64).
 // `lds` holds NT/64 + 1 ints. Every thread receives the block total in *total.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == kWave - 1) lds[wid] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -189,12 +198,7 @@ __device__ __forceinline__ void wave_find_digit_t(const uint32_t* hist, uint32_t
   uint32_t sum = 0;
 #pragma unroll
   for (int b = 0; b < PER; ++b) sum += v[b];
-  uint32_t incl = sum;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(sum);
   const uint32_t before = incl - sum;
   const bool mine = before < k && incl >= k;
   int d = 0;
@@ -214,8 +218,8 @@ __device__ __forceinline__ void wave_find_digit_t(const uint32_t* hist, uint32_t
   }
   const uint64_t who = __ballot(mine);
   const int src = who ? __builtin_ctzll(who) : 0;
-  *digit = __shfl(d, src);
-  *above = __shfl(ab, src);
+  *digit = __builtin_amdgcn_readlane(d, src);
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
 }
 
 __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, int nbins, uint32_t k, int* digit,
@@ -237,6 +241,120 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* hist, uint32_t k,
   wave_find_digit(hist + 4096, 1024, k2, &d3, &a3);
   *thr = ((uint32_t)d1 << 21) | ((uint32_t)d2 << 10) | (uint32_t)d3;
   *ties = k2 - a3;
+}
+
+// ---------------------------------------------------------------- radix threshold in LDS
+
+// The k-th largest of the n keys u[0..n) in LDS (fp32 bit patterns of non-negative
+// scores, so unsigned order is value order), digit by digit (11, 11, 10 bits) with
+// histograms h[0..kRadixBins) in LDS. With have_first, h already holds the histogram
+// of the first digit. Returns the key's bit pattern and, in *ties, how many keys
+// equal to it belong to the top k. Every thread of the NT-thread workgroup calls it.
+template <int NT>
+__device__ __forceinline__ uint32_t lds_radix_threshold(const uint32_t* u, int n, uint32_t k, uint32_t* h,
+                                                        uint32_t* dig, bool have_first, uint32_t* ties) {
+  constexpr int kBins = 2048;
+  const int tid = threadIdx.x;
+  uint32_t want = k, prefix = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    if (pass > 0 || !have_first) {
+      const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+      const uint32_t mask = pass == 2 ? 1023u : 2047u;
+      for (int i = tid; i < kBins; i += NT) h[i] = 0u;
+      __syncthreads();
+#pragma unroll 8
+      for (int i = tid; i < n; i += NT) {
+        const uint32_t v = u[i];
+        if (pass == 0 || (v >> (shift + (pass == 2 ? 10 : 11))) == prefix) atomicAdd(&h[(v >> shift) & mask], 1u);
+      }
+      __syncthreads();
+    }
+    if (tid < 64) {
+      int d;
+      uint32_t above;
+      wave_find_digit(h, pass == 2 ? 1024 : kBins, want, &d, &above);
+      if (tid == 0) {
+        dig[0] = (uint32_t)d;
+        dig[1] = above;
+      }
+    }
+    __syncthreads();
+    want -= dig[1];
+    prefix = (prefix << (pass == 2 ? 10 : 11)) | dig[0];
+    __syncthreads();
+  }
+  *ties = want;
+  return prefix;
+}
+
+// ---------------------------------------------------------------- selection emission
+
+// Writes, in ascending position order, every position i < n whose key u[i] (LDS) is
+// above thr, plus the first ties_wanted positions whose key equals thr: out[p] gets
+// the position (or idx[position] when idx is not NULL), outs[p] (if not NULL) the
+// key as a float. Wave w of NW scans positions [w*span, (w+1)*span) with ballots,
+// 64 positions per ballot and eight ballots per batch of LDS reads; one exchange of
+// the per-wave counts (wcnt, NW pairs in LDS) fixes tie ranks and output offsets.
+template <int NW>
+__device__ __forceinline__ void lds_emit(const uint32_t* u, int n, uint32_t thr, uint32_t ties_wanted,
+                                         const int32_t* __restrict__ idx, int32_t* __restrict__ out,
+                                         float* __restrict__ outs, uint32_t (*wcnt)[2]) {
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int span = ((n + NW - 1) / NW + 64 * U - 1) / (64 * U) * (64 * U);
+  const int e0 = w * span;
+  uint32_t ngt = 0, neq = 0;
+  for (int it = 0; it < span; it += 64 * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int e = e0 + it + k * 64 + lane;
+      v[k] = e < n ? u[e] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int e = e0 + it + k * 64 + lane;
+      ngt += (uint32_t)__builtin_popcountll(__ballot(e < n && v[k] > thr));
+      neq += (uint32_t)__builtin_popcountll(__ballot(e < n && v[k] == thr));
+    }
+  }
+  if (lane == 0) {
+    wcnt[w][0] = ngt;
+    wcnt[w][1] = neq;
+  }
+  __syncthreads();
+  uint32_t tie = 0, pos = 0;
+  for (int x = 0; x < w; ++x) {
+    const uint32_t take = min(wcnt[x][1], ties_wanted - min(ties_wanted, tie));
+    pos += wcnt[x][0] + take;
+    tie += wcnt[x][1];
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int it = 0; it < span; it += 64 * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int e = e0 + it + k * 64 + lane;
+      v[k] = e < n ? u[e] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int e = e0 + it + k * 64 + lane;
+      const bool gt = e < n && v[k] > thr, eq = e < n && v[k] == thr;
+      const uint64_t beq = __ballot(eq);
+      const uint32_t my_tie = tie + (uint32_t)__builtin_popcountll(beq & below);
+      const bool take = gt || (eq && my_tie < ties_wanted);
+      const uint64_t btake = __ballot(take);
+      if (take) {
+        const uint32_t p = pos + (uint32_t)__builtin_popcountll(btake & below);
+        out[p] = idx ? idx[e] : e;
+        if (outs) outs[p] = __uint_as_float(v[k]);
+      }
+      pos += (uint32_t)__builtin_popcountll(btake);
+      tie += (uint32_t)__builtin_popcountll(beq);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- MFMA

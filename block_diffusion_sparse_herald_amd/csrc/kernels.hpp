@@ -18,6 +18,8 @@ inline void klaunch(F kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st
 constexpr int kScanTok = 256;
 constexpr int kScoreTok = 1024;
 constexpr int kRadixBins = 2048;
+// Longest sequence whose selection scores one workgroup keeps in LDS (144 KiB).
+constexpr int kTopcLdsMaxLen = 36864;
 // Candidates one refine workgroup covers (bf16 MFMA path).
 constexpr int kRefineTile = 128;
 // Keys per attention block and the largest supported candidate count.
@@ -76,6 +78,8 @@ hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st)
 hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipStream_t st);
 hipError_t launch_emit_candidates(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score,
                                   hipStream_t st);
+bool topc_in_lds(const Shape& s);
+hipError_t launch_topc_lds(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score, hipStream_t st);
 // refine
 hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, const int32_t* cand,
                                const RefineWs& ws, hipStream_t st);

@@ -21,6 +21,8 @@
 //   emit_kernel       one workgroup per (sequence, KV head): exact threshold from
 //                     the three histograms, ties to the lowest indices, ascending
 //                     indices from the bitmaps (block-wide prefix counts).
+//   topc_lds_kernel   instead of the last three when every sequence's scores fit
+//                     in LDS: digits two and three and the emission on an LDS copy.
 // S >= 0, so its IEEE bit pattern orders like its value and radix select is exact.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -525,6 +527,60 @@ __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ sc
   }
 }
 
+// ------------------------------------------------------------------ top-C in LDS
+
+// One workgroup per (sequence, KV head) whose scores all fit in LDS (the sequences
+// of up to kTopcLdsMaxLen tokens): the first digit comes from the histogram that
+// score_hist_kernel built, digits two and three from histograms of the LDS copy,
+// then the candidates are emitted in ascending order with wave ballots (a wave takes
+// a contiguous range of tokens; one exchange of per-wave counts fixes the tie ranks
+// and output positions). Replaces radix_kernel<2>, radix_kernel<3> and emit_kernel.
+__global__ __launch_bounds__(1024) void topc_lds_kernel(const float* __restrict__ scores,
+                                                       const int64_t* __restrict__ seq_start, int Hkv,
+                                                       int64_t total, int C, const uint32_t* __restrict__ hist,
+                                                       int32_t* __restrict__ cand, float* __restrict__ cand_score) {
+  constexpr int NT = 1024, NW = NT / 64;
+  extern __shared__ uint32_t u[];  // [L] score bit patterns
+  __shared__ uint32_t h[kRadixBins];
+  __shared__ uint32_t wcnt[NW][2];
+  __shared__ uint32_t dig[4];
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int64_t j0 = seq_start[s];
+  const int L = (int)(seq_start[s + 1] - j0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* sc = scores + (int64_t)g * total + j0;
+  const uint32_t* gh = hist + (int64_t)(s * Hkv + g) * 3 * kRadixBins;
+
+  for (int i = tid; i < kRadixBins / 4; i += NT) reinterpret_cast<uint4*>(h)[i] = reinterpret_cast<const uint4*>(gh)[i];
+  // scores -> LDS, 16 bytes per load, eight loads in flight per thread
+  {
+    const bool al = ((uintptr_t)sc & 15) == 0;
+    const int n4 = al ? L / 4 : 0;
+    constexpr int U = 8;
+    for (int i0 = 0; i0 < n4; i0 += NT * U) {
+      uint4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int i = i0 + k * NT + tid;
+        v[k] = i < n4 ? *reinterpret_cast<const uint4*>(sc + 4 * i) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int i = i0 + k * NT + tid;
+        if (i < n4) reinterpret_cast<uint4*>(u)[i] = v[k];
+      }
+    }
+    for (int i = 4 * n4 + tid; i < L; i += NT) u[i] = __float_as_uint(sc[i]);
+  }
+  __syncthreads();
+
+  // digit 1 (bits 31..21) from the global histogram, digits 2 (20..10) and 3 (9..0) here
+  uint32_t ties_wanted;
+  const uint32_t thr = lds_radix_threshold<NT>(u, L, (uint32_t)C, h, dig, true, &ties_wanted);
+  lds_emit<NW>(u, L, thr, ties_wanted, nullptr, cand + (int64_t)(s * Hkv + g) * C,
+               cand_score ? cand_score + (int64_t)(s * Hkv + g) * C : nullptr, wcnt);
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st) {
@@ -592,6 +648,17 @@ hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipSt
     klaunch(radix_kernel<2>, grid, 256, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
   else
     klaunch(radix_kernel<3>, grid, 256, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
+  return hipGetLastError();
+}
+
+bool topc_in_lds(const Shape& s) { return s.max_len <= kTopcLdsMaxLen; }
+
+hipError_t launch_topc_lds(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score, hipStream_t st) {
+  const size_t smem = (size_t)s.max_len * sizeof(uint32_t);
+  hipError_t e = allow_smem((const void*)topc_lds_kernel, smem);
+  if (e != hipSuccess) return e;
+  klaunch(topc_lds_kernel, dim3(s.Hkv, s.nseq), 1024, smem, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.hist,
+          cand, cand_score);
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ class Hip:
             "hipGraphInstantiate": [ctypes.POINTER(_vp), _vp, _vp, _vp, ctypes.c_size_t],
             "hipGraphLaunch": [_vp, _vp],
             "hipGetErrorString": [ctypes.c_int],
+            "hipGetLastError": [],
             "hipGetDeviceCount": [ctypes.POINTER(ctypes.c_int)],
         }
         for name, args in sig.items():
@@ -54,6 +55,7 @@ class Hip:
 
     def check(self, rc: int, what: str) -> None:
         if rc != 0:
+            self.lib.hipGetLastError()  # the failure is reported here; do not leave it for the next caller
             raise HipError(f"{what}: {self.lib.hipGetErrorString(rc).decode()}")
 
     def device_count(self) -> int:

@@ -178,12 +178,14 @@ const char* herald_last_error(void);
 
 /*
  * Instrumentation. Kernel ids: 0 merged-query scan, 1 selection scores + first
- * radix digit, 2 second and third radix digits, 3 candidate emission, 4 refine
- * statistics, 5 refine scores, 6 final top-K, 7 gather, 8 block attention,
- * 9 merge of the attention key ranges (long subsets only). While set (non-NULL), every launch of that kernel on a
- * call's stream is bracketed by records of start and stop on the same stream
- * (external event nodes when the stream is being captured into a graph); the last
- * launch wins. Pass NULL events to clear. Thread-local setting.
+ * radix digit, 2 second and third radix digits (sequences longer than 36864 tokens
+ * only), 3 candidate emission (with the second and third digits for sequences up to
+ * 36864 tokens), 4 refine statistics, 5 refine scores, 6 final top-K, 7 gather,
+ * 8 block attention, 9 merge of the attention key ranges (split subsets only).
+ * While set (non-NULL), every launch of that kernel on a call's stream is bracketed
+ * by records of start and stop on the same stream (external event nodes when the
+ * stream is being captured into a graph); the last launch wins; a kernel a call does
+ * not launch records nothing. Pass NULL events to clear. Thread-local setting.
  */
 herald_status herald_set_kernel_events(int32_t kernel_id, hipEvent_t start, hipEvent_t stop);
 
