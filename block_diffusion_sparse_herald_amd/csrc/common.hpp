@@ -101,6 +101,31 @@ __device__ __forceinline__ void ms_wave_merge(float& m, float& s) {
   }
 }
 
+// max / sum of x over lanes l, l^16, l^32, l^48 (the four lane groups of one MFMA
+// column), with the gfx950 row-swap permutes (no LDS traffic)
+__device__ __forceinline__ float xmax4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// sum of x over the 16 lanes of each row (lanes 16r .. 16r+15), complete in the last
+// lane of the row (DPP row shifts, no LDS traffic)
+__device__ __forceinline__ float row_sum16_last(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));  // row_shr:1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));  // row_shr:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));  // row_shr:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));  // row_shr:8
+  return x;
+}
+
 // ---------------------------------------------------------------- block-wide scans
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP (no LDS traffic): row

@@ -11,7 +11,8 @@
 //   refine_stats_kernel   per row (b,h): (max, sum 2^(x-max)) over the tile
 //                         (stored row-major: a row's tiles are contiguous).
 //   refine_scores_kernel  per row: normalisers from all tiles; per candidate: the
-//                         sum over rows, in a fixed order.
+//                         sum over rows, in a fixed order (each lane over its row's
+//                         tiles, then over the 16 lanes of a row with DPP shifts).
 // Each wave owns 64 candidates (four 16-candidate MFMA tiles). The candidate key
 // rows (gathered from the cache by index) and the group's B*G query rows are
 // streamed into LDS with coalesced direct-to-LDS loads; the key rows are the A
@@ -205,8 +206,7 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
         x[mt][i] = c < C ? acc[mt][i] * scale2 : -INFINITY;
         m = fmaxf(m, x[mt][i]);
       }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = xmax4(m);
     float l = 0.f;
     if (m != -INFINITY) {
 #pragma unroll
@@ -214,8 +214,7 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
 #pragma unroll
         for (int i = 0; i < 4; ++i) l += fast_exp2(x[mt][i] - m);
     }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = xsum4(l);
     if (lane < 16) wstat[w * RT * 16 + rt * 16 + lane] = make_float2(m, l);
   }
   __syncthreads();
@@ -289,14 +288,14 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = r < R ? fast_exp2(acc[mt][i] * scale2 - M) * iz : 0.f;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o);
-        rs[mt][i] += p;
-      }
+      for (int i = 0; i < 4; ++i) rs[mt][i] += r < R ? fast_exp2(acc[mt][i] * scale2 - M) * iz : 0.f;
   }
-  if ((lane & 15) == 0) {
+  // each lane summed its query row over the row tiles; now sum the 16 rows of a lane row
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[mt][i] = row_sum16_last(rs[mt][i]);
+  if ((lane & 15) == 15) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
