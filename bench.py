@@ -174,8 +174,8 @@ def main(argv=None):
     for i in range(args.warmup):
         step(i)
     hip.sync()
-    launches = {"scan": 1, "score_hist": 1, "radix": 2, "emit": 1, "refine_stats": 1 if wl.dtype == "bf16" else 0,
-                "refine_scores": 1, "refine_select": 1 if wl.dtype == "bf16" else 0, "gather": 1, "attn": wl.T,
+    launches = {"scan": 1, "score_hist": 1, "radix": 2, "emit": 1, "refine_stats": 1,
+                "refine_scores": 1, "refine_select": 1, "gather": 1, "attn": wl.T,
                 "attn_combine": wl.T if r.attn_splits > 1 else 0}
     per_launch_us = {}
     for name, n in launches.items():

@@ -260,10 +260,11 @@ herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, 
   if (s.bf16) {
     HERALD_LAUNCH(4, stream, launch_refine_stats(s, q_refine, k_cache, cand_idx, w, stream));
     HERALD_LAUNCH(5, stream, launch_refine_scores(s, q_refine, k_cache, cand_idx, w, stream));
-    HERALD_LAUNCH(6, stream, launch_refine_select(s, cand_idx, w, topk_idx, topk_score, stream));
   } else {
-    HERALD_LAUNCH(5, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, topk_idx, topk_score, stream));
+    HERALD_LAUNCH(4, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, true, stream));
+    HERALD_LAUNCH(5, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, false, stream));
   }
+  HERALD_LAUNCH(6, stream, launch_refine_select(s, cand_idx, w, topk_idx, topk_score, stream));
   return ok();
 }
 

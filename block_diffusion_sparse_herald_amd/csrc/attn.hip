@@ -27,7 +27,7 @@
 // 2^8, exact in fp32 and bf16 range, and both sums use the same reference.
 // With several key ranges each workgroup writes a partial (fp32 max and sum, the
 // unnormalised output in bf16) that attn_combine_kernel merges.
-// fp32 path (attn_f32_kernel): one workgroup per query row, VALU.
+// fp32 path (attn_f32_kernel): four query rows per workgroup, VALU, keys in chunks of 128.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -387,60 +387,94 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict
       make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
-// fp32 path: one workgroup per query row; keys in chunks of 1024 with an online softmax.
+// fp32 path: a workgroup takes four query rows of one (sequence, KV head) and walks
+// the keys in chunks of 128. Logits: one key per thread (its row read straight from
+// memory), two of the four query rows per thread from LDS (broadcast reads). Online
+// base-2 softmax: one wave per query row. Output: the chunk's values staged d-major in
+// LDS (rows padded by one word, so the 64 lanes of a read hit 64 banks), each thread
+// accumulating D/64 output elements of its wave's row.
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kb,
                                                        const float* __restrict__ vb, const float* __restrict__ k_sel,
                                                        const float* __restrict__ v_sel, int B, int Hq, int Hkv,
                                                        int G, int topk, int64_t ldv, float scale2,
                                                        float* __restrict__ out) {
-  constexpr int KC = 1024;
-  __shared__ float qs[D];
-  __shared__ float xs[KC];
-  __shared__ float red[4];
-  const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, s = blockIdx.y;
-  const int g = h / G;
+  constexpr int KC = 128, RB = 4, EP = D / 64;
+  __shared__ __align__(16) float qs[RB][D];
+  __shared__ float xs[RB][KC];
+  extern __shared__ float vs[];  // [D][KC + 1]
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G, r0 = blockIdx.x * RB;
   const int64_t unit = (int64_t)s * Hkv + g;
-  const float* qrow = q + (((int64_t)s * B + b) * Hq + h) * D;
-  for (int e = threadIdx.x; e < D; e += 256) qs[e] = qrow[e];
-  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  auto qrow = [&](int r) { return q + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D; };
+  for (int i = threadIdx.x; i < RB * D; i += 256) qs[i / D][i % D] = qrow(min(r0 + i / D, R - 1))[i % D];
   const int NK = topk + B;
-  auto key = [&](int kk) -> const float* {
-    return kk < topk ? k_sel + (unit * topk + kk) * D : kb + (((int64_t)s * B + (kk - topk)) * Hkv + g) * D;
-  };
-  auto val = [&](int kk, int e) -> float {
-    return kk < topk ? v_sel[(unit * D + e) * ldv + kk] : vb[(((int64_t)s * B + (kk - topk)) * Hkv + g) * D + e];
-  };
-  float m = -INFINITY, l = 0.f, acc = 0.f;
+  float m = -INFINITY, l = 0.f, acc[EP];
+#pragma unroll
+  for (int j = 0; j < EP; ++j) acc[j] = 0.f;
   for (int k0 = 0; k0 < NK; k0 += KC) {
     const int n = min(KC, NK - k0);
-    float lm = -INFINITY;
-    for (int t = threadIdx.x; t < n; t += 256) {
-      const float* kr = key(k0 + t);
-      float d = 0.f;
-      for (int e = 0; e < D; ++e) d = fmaf(qs[e], kr[e], d);
-      xs[t] = d * scale2;
-      lm = fmaxf(lm, xs[t]);
-    }
-    for (int o = 32; o > 0; o >>= 1) lm = fmaxf(lm, __shfl_xor(lm, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = lm;
-    __syncthreads();
-    const float mn = fmaxf(m, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-    const float alpha = fast_exp2(m - mn);
-    if (threadIdx.x < D) {
-      float a = 0.f, ls = 0.f;
-      for (int t = 0; t < n; ++t) {
-        const float p = fast_exp2(xs[t] - mn);
-        ls += p;
-        a = fmaf(p, val(k0 + t, threadIdx.x), a);
+    __syncthreads();  // qs ready; the previous chunk's xs and vs consumed
+    {
+      const int kk = threadIdx.x % KC, rp = (threadIdx.x / KC) * 2;
+      float x0 = -INFINITY, x1 = -INFINITY;
+      if (kk < n) {
+        const int key = k0 + kk;
+        const float* kr = key < topk ? k_sel + (unit * topk + key) * D
+                                     : kb + (((int64_t)s * B + (key - topk)) * Hkv + g) * D;
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll 8
+        for (int e = 0; e < D; e += 4) {
+          const float4 kv = *reinterpret_cast<const float4*>(kr + e);
+          const float4 qa = *reinterpret_cast<const float4*>(&qs[rp][e]);
+          const float4 qb = *reinterpret_cast<const float4*>(&qs[rp + 1][e]);
+          d0 = fmaf(qa.w, kv.w, fmaf(qa.z, kv.z, fmaf(qa.y, kv.y, fmaf(qa.x, kv.x, d0))));
+          d1 = fmaf(qb.w, kv.w, fmaf(qb.z, kv.z, fmaf(qb.y, kv.y, fmaf(qb.x, kv.x, d1))));
+        }
+        x0 = d0 * scale2;
+        x1 = d1 * scale2;
       }
-      acc = acc * alpha + a;
-      l = l * alpha + ls;
+      xs[rp][kk] = x0;
+      xs[rp + 1][kk] = x1;
     }
-    m = mn;
+    for (int i = threadIdx.x; i < D * KC; i += 256) {
+      const int e = i / KC, kk = i % KC, key = k0 + kk;
+      float v = 0.f;
+      if (kk < n)
+        v = key < topk ? v_sel[(unit * D + e) * ldv + key] : vb[(((int64_t)s * B + (key - topk)) * Hkv + g) * D + e];
+      vs[e * (KC + 1) + kk] = v;
+    }
     __syncthreads();
+    const float x0 = xs[w][lane], x1 = xs[w][lane + 64];
+    float cm = fmaxf(x0, x1);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+    const float mn = fmaxf(m, cm);  // finite: every chunk holds at least one key
+    const float al = fast_exp2(m - mn);
+    const float p0 = fast_exp2(x0 - mn), p1 = fast_exp2(x1 - mn);
+    float ps = p0 + p1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) ps += __shfl_xor(ps, o);
+    l = l * al + ps;
+    m = mn;
+    __syncthreads();  // every wave has read its logits before they become weights
+    xs[w][lane] = p0;
+    xs[w][lane + 64] = p1;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+      const float* vr = vs + (lane + 64 * j) * (KC + 1);
+      float a = acc[j] * al;
+      for (int kk = 0; kk < n; ++kk) a = fmaf(xs[w][kk], vr[kk], a);
+      acc[j] = a;
+    }
   }
-  if (threadIdx.x < D) out[(((int64_t)s * B + b) * Hq + h) * D + threadIdx.x] = acc / l;
+  if (r0 + w < R) {
+    float* o = out + (((int64_t)s * B + (r0 + w) / G) * Hq + g * G + (r0 + w) % G) * D;
+#pragma unroll
+    for (int j = 0; j < EP; ++j) o[lane + 64 * j] = acc[j] / l;
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -534,13 +568,17 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
   const float scale2 = s.scale * kLog2e;
   if (!s.bf16) {
     const int64_t ldv = vsel_ld(s.topk);
-    dim3 grid(s.B * s.Hq, s.nseq);
+    const dim3 grid((s.B * s.G + 3) / 4, s.Hkv, s.nseq);
+    const size_t smem = (size_t)s.D * 129 * sizeof(float);
+    const void* kern = s.D == 128 ? (const void*)attn_f32_kernel<128> : (const void*)attn_f32_kernel<64>;
+    hipError_t e = allow_smem(kern, smem);
+    if (e != hipSuccess) return e;
     if (s.D == 128)
-      klaunch(attn_f32_kernel<128>, grid, 256, 0, st, (const float*)q, (const float*)kb, (const float*)vb,
+      klaunch(attn_f32_kernel<128>, grid, 256, smem, st, (const float*)q, (const float*)kb, (const float*)vb,
                                                  (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G,
                                                  s.topk, ldv, scale2, (float*)out);
     else
-      klaunch(attn_f32_kernel<64>, grid, 256, 0, st, (const float*)q, (const float*)kb, (const float*)vb,
+      klaunch(attn_f32_kernel<64>, grid, 256, smem, st, (const float*)q, (const float*)kb, (const float*)vb,
                                                 (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G,
                                                 s.topk, ldv, scale2, (float*)out);
     return hipGetLastError();

@@ -88,7 +88,7 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
 hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
                                 float* topk_score, hipStream_t st);
 hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
-                             int32_t* topk_idx, float* topk_score, hipStream_t st);
+                             bool stats, hipStream_t st);
 // gather
 hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
                          hipStream_t st);

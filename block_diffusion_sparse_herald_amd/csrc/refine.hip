@@ -21,84 +21,11 @@
 // refine_select_kernel then takes, per (sequence, KV head), the exact top-K of R
 // in LDS (three radix digits on the fp32 bit pattern, R >= 0), ties to the lower
 // cache index, ascending output.
-// fp32 path: refine_f32_kernel, one workgroup per (sequence, KV head), same top-K.
+// fp32 path: the same stats / scores / select steps, with the logits on VALU.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace herald {
-
-// Exact top-k of u[0..n) (fp32 bit patterns of non-negative scores, in LDS), ties
-// to the lower position; writes cand[pos] (or pos when cand is NULL) and the score
-// of each pick in ascending position order. h: kRadixBins LDS words; lds: NT/64+3.
-template <int NT>
-__device__ void lds_topk(const uint32_t* u, int n, int k, uint32_t* h, uint32_t* lds, const int32_t* cand,
-                         int32_t* out, float* outs) {
-  uint32_t want = (uint32_t)k;
-  uint32_t prefix = 0;  // digits found so far
-  const int shift[3] = {21, 10, 0};
-  const int width[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    for (int i = threadIdx.x; i < kRadixBins; i += NT) h[i] = 0u;
-    __syncthreads();
-    const int hi_shift = shift[pass] + width[pass];
-    const uint32_t mask = (1u << width[pass]) - 1u;
-    for (int c = threadIdx.x; c < n; c += NT) {
-      const uint32_t v = u[c];
-      if (pass == 0 || (v >> hi_shift) == prefix) atomicAdd(&h[(v >> shift[pass]) & mask], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      int d;
-      uint32_t above;
-      wave_find_digit(h, width[pass] == 11 ? kRadixBins : 1024, want, &d, &above);
-      if (threadIdx.x == 0) {
-        lds[NT / 64 + 1] = (uint32_t)d;
-        lds[NT / 64 + 2] = above;
-      }
-    }
-    __syncthreads();
-    want -= lds[NT / 64 + 2];
-    prefix = (prefix << width[pass]) | lds[NT / 64 + 1];
-    __syncthreads();
-  }
-  const uint32_t thr = prefix;  // bit pattern of the k-th largest score
-  const uint32_t ties_wanted = want;
-
-  const int cpt = (n + NT - 1) / NT;
-  const int c0 = threadIdx.x * cpt, c1 = min(n, c0 + cpt);
-  uint32_t my_ties = 0;
-  for (int c = c0; c < c1; ++c) my_ties += u[c] == thr;
-  uint32_t tot;
-  const uint32_t tie_rank = block_exclusive_scan<NT>(my_ties, lds, &tot);
-  uint32_t my_sel = 0;
-  {
-    uint32_t tr = tie_rank;
-    for (int c = c0; c < c1; ++c) {
-      if (u[c] > thr) ++my_sel;
-      else if (u[c] == thr) {
-        if (tr < ties_wanted) ++my_sel;
-        ++tr;
-      }
-    }
-  }
-  uint32_t pos = block_exclusive_scan<NT>(my_sel, lds, &tot);
-  uint32_t tr = tie_rank;
-  for (int c = c0; c < c1; ++c) {
-    bool take = false;
-    if (u[c] > thr) take = true;
-    else if (u[c] == thr) {
-      take = tr < ties_wanted;
-      ++tr;
-    }
-    if (take) {
-      if (pos < (uint32_t)k) {
-        out[pos] = cand ? cand[c] : c;
-        if (outs) outs[pos] = __uint_as_float(u[c]);
-      }
-      ++pos;
-    }
-  }
-}
 
 // 16-byte chunk c of an LDS row r (query row or candidate key row) is stored at chunk
 // c ^ refine_swz(r): the 16 rows one MFMA fragment read touches hit distinct banks.
@@ -353,56 +280,188 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
                     topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr, wcnt);
 }
 
-// fp32 path: one workgroup per (sequence, KV head); rows first, then candidates.
+// fp32 path: the same three steps on VALU (stats and scores over kRefineTile-candidate
+// tiles, then refine_select_kernel). A logit is one fma chain over the head dimension
+// in index order; fma is symmetric in its two factors, so the two kernels, which read
+// the operands from different places, compute the same bits.
 template <int D>
-__device__ __forceinline__ float dot_rows_f32(const float* __restrict__ a, const float* __restrict__ b) {
-  float acc = 0.f;
-#pragma unroll 8
-  for (int e = 0; e < D; ++e) acc = fmaf(a[e], b[e], acc);
-  return acc;
+__device__ __forceinline__ void dot4_f32(const float (&reg)[D], const float* o0, const float* o1, const float* o2,
+                                         const float* o3, float (&d)[4]) {
+  d[0] = d[1] = d[2] = d[3] = 0.f;
+#pragma unroll
+  for (int e = 0; e < D; e += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(o0 + e);
+    const float4 b = *reinterpret_cast<const float4*>(o1 + e);
+    const float4 c = *reinterpret_cast<const float4*>(o2 + e);
+    const float4 f = *reinterpret_cast<const float4*>(o3 + e);
+    d[0] = fmaf(reg[e + 3], a.w, fmaf(reg[e + 2], a.z, fmaf(reg[e + 1], a.y, fmaf(reg[e], a.x, d[0]))));
+    d[1] = fmaf(reg[e + 3], b.w, fmaf(reg[e + 2], b.z, fmaf(reg[e + 1], b.y, fmaf(reg[e], b.x, d[1]))));
+    d[2] = fmaf(reg[e + 3], c.w, fmaf(reg[e + 2], c.z, fmaf(reg[e + 1], c.y, fmaf(reg[e], c.x, d[2]))));
+    d[3] = fmaf(reg[e + 3], f.w, fmaf(reg[e + 2], f.z, fmaf(reg[e + 1], f.y, fmaf(reg[e], f.x, d[3]))));
+  }
+}
+
+// The same chains with both operands in LDS: one row p (per lane) against four rows
+// o0..o3 (broadcast).
+template <int D>
+__device__ __forceinline__ void dot4_lds_f32(const float* p, const float* o0, const float* o1, const float* o2,
+                                             const float* o3, float (&d)[4]) {
+  d[0] = d[1] = d[2] = d[3] = 0.f;
+#pragma unroll 4
+  for (int e = 0; e < D; e += 4) {
+    const float4 r = *reinterpret_cast<const float4*>(p + e);
+    const float4 a = *reinterpret_cast<const float4*>(o0 + e);
+    const float4 b = *reinterpret_cast<const float4*>(o1 + e);
+    const float4 c = *reinterpret_cast<const float4*>(o2 + e);
+    const float4 f = *reinterpret_cast<const float4*>(o3 + e);
+    d[0] = fmaf(r.w, a.w, fmaf(r.z, a.z, fmaf(r.y, a.y, fmaf(r.x, a.x, d[0]))));
+    d[1] = fmaf(r.w, b.w, fmaf(r.z, b.z, fmaf(r.y, b.y, fmaf(r.x, b.x, d[1]))));
+    d[2] = fmaf(r.w, c.w, fmaf(r.z, c.z, fmaf(r.y, c.y, fmaf(r.x, c.x, d[2]))));
+    d[3] = fmaf(r.w, f.w, fmaf(r.z, f.z, fmaf(r.y, f.y, fmaf(r.x, f.x, d[3]))));
+  }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void refine_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                         const int32_t* __restrict__ cand,
-                                                         const int64_t* __restrict__ seq_start, int B, int Hq,
-                                                         int Hkv, int G, int C, float scale2, int topk,
-                                                         float* __restrict__ rscore, int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_score) {
-  const int g = blockIdx.x, s = blockIdx.y;
+__device__ __forceinline__ void load_row_f32(const float* __restrict__ src, float (&reg)[D]) {
+#pragma unroll
+  for (int e = 0; e < D; e += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(src + e);
+    reg[e] = v.x;
+    reg[e + 1] = v.y;
+    reg[e + 2] = v.z;
+    reg[e + 3] = v.w;
+  }
+}
+
+// Per (query row, tile): (max, sum 2^(x-max)) over the tile's candidates. Lanes are
+// query rows (64 per pass, the row in registers); wave w takes candidates
+// 32w .. 32w+31 of the tile from LDS (broadcast reads); the four waves' pairs are
+// merged in wave order.
+template <int D>
+__global__ __launch_bounds__(256) void refine_stats_f32_kernel(const float* __restrict__ q,
+                                                               const float* __restrict__ k,
+                                                               const int32_t* __restrict__ cand,
+                                                               const int64_t* __restrict__ seq_start, int B, int Hq,
+                                                               int Hkv, int G, int C, float scale2, int ntile,
+                                                               float2* __restrict__ row_stats) {
+  static_assert(kRefineTile == 128, "four waves of 32 candidates");
+  extern __shared__ __align__(16) float ks[];  // [kRefineTile][D]
+  __shared__ float2 wstat[4][64];
+  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t j0 = seq_start[s];
-  __shared__ float rowM[256], rowIZ[256];
-  __shared__ uint32_t h[kRadixBins];
-  __shared__ uint32_t lds[256 / 64 + 4];
-  extern __shared__ uint32_t u[];  // [C]
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  auto qrow = [&](int r) { return q + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D; };
-  auto krow = [&](int c) { return k + ((j0 + cd[c]) * Hkv + g) * D; };
+  for (int i = threadIdx.x; i < kRefineTile * D / 4; i += 256) {
+    const int row = i / (D / 4), ch = i % (D / 4);
+    const int c = min(tile * kRefineTile + row, C - 1);
+    *reinterpret_cast<float4*>(ks + row * D + 4 * ch) =
+        *reinterpret_cast<const float4*>(k + ((j0 + cd[c]) * Hkv + g) * D + 4 * ch);
+  }
+  __syncthreads();
+  const int nvalid = min(kRefineTile, C - tile * kRefineTile);
+  for (int r0 = 0; r0 < R; r0 += 64) {
+    const int r = r0 + lane, rq = min(r, R - 1);
+    float qr[D];
+    load_row_f32<D>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D, qr);
+    float m = -INFINITY, l = 0.f;
+#pragma unroll 1
+    for (int c0 = w * 32; c0 < w * 32 + 32; c0 += 4) {
+      float d[4];
+      dot4_f32<D>(qr, ks + c0 * D, ks + (c0 + 1) * D, ks + (c0 + 2) * D, ks + (c0 + 3) * D, d);
+      float x[4], mg = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = c0 + u < nvalid ? d[u] * scale2 : -INFINITY;
+        mg = fmaxf(mg, x[u]);
+      }
+      if (mg == -INFINITY) continue;
+      float lg = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lg += fast_exp2(x[u] - mg);
+      ms_merge(m, l, mg, lg);
+    }
+    wstat[w][lane] = make_float2(m, l);
+    __syncthreads();
+    if (threadIdx.x < 64 && r < R) {
+      float M = -INFINITY, Z = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) ms_merge(M, Z, wstat[ww][lane].x, wstat[ww][lane].y);
+      row_stats[(((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1) + tile] = make_float2(M, Z);
+    }
+    __syncthreads();
+  }
+}
+
+// Per candidate: sum over query rows of 2^(x - M_row) / Z_row. Lanes are candidates
+// (key rows in LDS, padded by four words so that 16 lanes' 16-byte reads cover all
+// banks): waves 0/1 take candidates 0..63 / 64..127 of the tile over the first half
+// of every 64-row pass, waves 2/3 over the second half; the halves are added at the
+// end.
+template <int D>
+__global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __restrict__ q,
+                                                                const float* __restrict__ k,
+                                                                const int32_t* __restrict__ cand,
+                                                                const int64_t* __restrict__ seq_start, int B,
+                                                                int Hq, int Hkv, int G, int C, float scale2, int ntile,
+                                                                const float2* __restrict__ row_stats,
+                                                                float* __restrict__ rscore) {
+  constexpr int KP = D + 4;
+  extern __shared__ __align__(16) float qs[];  // [64][D], [kRefineTile][KP], rowM[R], rowIZ[R]
+  __shared__ float part[2][kRefineTile];
+  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G;
+  float* kt = qs + 64 * D;
+  float* rowM = kt + kRefineTile * KP;
+  float* rowIZ = rowM + R;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ci = (w & 1) * 64 + lane, half = w >> 1;
+  const int64_t j0 = seq_start[s];
+  const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
+  for (int i = threadIdx.x; i < kRefineTile * D / 4; i += 256) {
+    const int row = i / (D / 4), ch = i % (D / 4);
+    const int c = min(tile * kRefineTile + row, C - 1);
+    *reinterpret_cast<float4*>(kt + row * KP + 4 * ch) =
+        *reinterpret_cast<const float4*>(k + ((j0 + cd[c]) * Hkv + g) * D + 4 * ch);
+  }
   for (int r = threadIdx.x; r < R; r += 256) {
-    float m = -INFINITY, z = 0.f;
-    for (int c = 0; c < C; ++c) {
-      const float x = dot_rows_f32<D>(qrow(r), krow(c)) * scale2;
-      if (x > m) {
-        z = z * fast_exp2(m - x) + 1.f;
-        m = x;
-      } else {
-        z += fast_exp2(x - m);
+    const float2* st = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);
+    float M = -INFINITY, Z = 0.f;
+    for (int t = 0; t < ntile; ++t) {
+      const float2 p = st[t];
+      ms_merge(M, Z, p.x, p.y);
+    }
+    rowM[r] = M;
+    rowIZ[r] = 1.f / Z;
+  }
+  float acc = 0.f;
+  for (int r0 = 0; r0 < R; r0 += 64) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * D / 4; i += 256) {
+      const int rr = i / (D / 4), ch = i % (D / 4);
+      const int rq = min(r0 + rr, R - 1);
+      *reinterpret_cast<float4*>(qs + rr * D + 4 * ch) =
+          *reinterpret_cast<const float4*>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + 4 * ch);
+    }
+    __syncthreads();
+    const int rb = half * 32;
+#pragma unroll 1
+    for (int j = rb; j < rb + 32; j += 4) {
+      float d[4];
+      dot4_lds_f32<D>(kt + ci * KP, qs + j * D, qs + (j + 1) * D, qs + (j + 2) * D, qs + (j + 3) * D, d);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + j + u;
+        if (r < R) acc += fast_exp2(d[u] * scale2 - rowM[r]) * rowIZ[r];
       }
     }
-    rowM[r] = m;
-    rowIZ[r] = 1.f / z;
   }
+  part[half][ci] = acc;
   __syncthreads();
-  for (int c = threadIdx.x; c < C; c += 256) {
-    float acc = 0.f;
-    for (int r = 0; r < R; ++r) acc += fast_exp2(dot_rows_f32<D>(qrow(r), krow(c)) * scale2 - rowM[r]) * rowIZ[r];
-    rscore[((int64_t)s * Hkv + g) * C + c] = acc;
-    u[c] = __float_as_uint(acc);
+  if (threadIdx.x < kRefineTile) {
+    const int cc = tile * kRefineTile + threadIdx.x;
+    if (cc < C) rscore[((int64_t)s * Hkv + g) * C + cc] = part[0][threadIdx.x] + part[1][threadIdx.x];
   }
-  __syncthreads();
-  lds_topk<256>(u, C, topk, h, lds, cd, topk_idx + ((int64_t)s * Hkv + g) * topk,
-                topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -460,19 +519,35 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
 }
 
 hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
-                             int32_t* topk_idx, float* topk_score, hipStream_t st) {
-  dim3 grid(s.Hkv, s.nseq);
+                             bool stats, hipStream_t st) {
+  dim3 grid(ws.ntile, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
-  const size_t smem = (size_t)s.C * sizeof(uint32_t);
-  const void* kern = s.D == 128 ? (const void*)refine_f32_kernel<128> : (const void*)refine_f32_kernel<64>;
+  const size_t smem = stats ? (size_t)kRefineTile * s.D * sizeof(float)
+                            : ((size_t)64 * s.D + (size_t)kRefineTile * (s.D + 4) + 2 * (size_t)s.B * s.G) *
+                                  sizeof(float);
+  const void* kern = stats ? (s.D == 128 ? (const void*)refine_stats_f32_kernel<128>
+                                         : (const void*)refine_stats_f32_kernel<64>)
+                           : (s.D == 128 ? (const void*)refine_scores_f32_kernel<128>
+                                         : (const void*)refine_scores_f32_kernel<64>);
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
-  if (s.D == 128)
-    klaunch(refine_f32_kernel<128>, grid, 256, smem, st, (const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
-                                                    s.Hkv, s.G, s.C, scale2, s.topk, ws.rscore, topk_idx, topk_score);
-  else
-    klaunch(refine_f32_kernel<64>, grid, 256, smem, st, (const float*)q, (const float*)k, cand, s.seq_start, s.B, s.Hq,
-                                                   s.Hkv, s.G, s.C, scale2, s.topk, ws.rscore, topk_idx, topk_score);
+  const float* qf = (const float*)q;
+  const float* kf = (const float*)k;
+  if (stats) {
+    if (s.D == 128)
+      klaunch(refine_stats_f32_kernel<128>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
+                                                             s.C, scale2, ws.ntile, ws.row_stats);
+    else
+      klaunch(refine_stats_f32_kernel<64>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
+                                                            s.C, scale2, ws.ntile, ws.row_stats);
+  } else {
+    if (s.D == 128)
+      klaunch(refine_scores_f32_kernel<128>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
+                                                              s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
+    else
+      klaunch(refine_scores_f32_kernel<64>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
+                                                             s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
+  }
   return hipGetLastError();
 }
 
