@@ -29,8 +29,13 @@ __device__ __forceinline__ bf16 f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16, h);
 }
 
+// Two floats to a packed bf16 pair (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 h = __builtin_convertvector((f2){lo, hi}, b2);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 template <typename T>
@@ -77,9 +82,32 @@ struct Vec16<bf16> {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+// 16-byte store marked non-temporal (global_store_dwordx4 ... nt).
+__device__ __forceinline__ void st16_stream(void* p, const float4& v) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store((v4f){v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
+}
 
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- direct-to-LDS loads
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4; lds_base must be the same in every lane of the wave).
+// Written as inline assembly so that the compiler does not wait for the transfer
+// before every later LDS read: the kernel waits on vmcnt itself (wait_vm).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt <= n (n < 64), the other counters not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // ---------------------------------------------------------------- (max, sum) pairs
 

@@ -10,6 +10,7 @@
 //   merge_kernel      qbar = mean_b q * scale * log2(e) (fp32); also zeroes the
 //                     radix histograms.
 //   scan_*_kernel     one pass over K: base-2 logits of every (query head, token),
+//                     (scan_lds_kernel for large batches, else scan_mfma_kernel)
 //                     stored token-major with the group's heads padded to 4 or 8,
 //                     and per-chunk (max, sum 2^(x-max)) pairs. HBM-bound: on
 //                     MFMA for bf16 caches, on the VALU for fp32 caches.
@@ -143,8 +144,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
     const int64_t j = wtok0 + b * 16 + n;
     if (j < L) {
       if (4 * kq < GP)
-        *reinterpret_cast<float4*>(logits + ((int64_t)g * total + j0 + j) * GP + 4 * kq) =
-            make_float4(acc[0], acc[1], acc[2], acc[3]);
+        st16_stream(logits + ((int64_t)g * total + j0 + j) * GP + 4 * kq, make_float4(acc[0], acc[1], acc[2], acc[3]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = kq * 4 + i;
@@ -175,6 +175,171 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
     float M = -INFINITY, Z = 0.f;
     for (int ww = 0; ww < 4; ++ww) ms_merge(M, Z, red[ww][threadIdx.x].x, red[ww][threadIdx.x].y);
     partials[((int64_t)s * Hq + g * G + threadIdx.x) * nchunk + chunk] = make_float2(M, Z);
+  }
+}
+
+// Chunk c of a row r of a scan stage is stored at chunk c ^ scan_swz(r): the 16 rows
+// one MFMA operand read touches (16 consecutive tokens of one KV head) then fall in
+// distinct banks. hshift = log2(Hkv); r >> hshift is the token within the stage.
+template <int D>
+__device__ __forceinline__ int scan_swz(int r, int hshift) {
+  return (r >> hshift) & (D / 8 - 1);
+}
+
+// bf16 caches with Hkv in {1, 2, 4, 8}: the same logits (same MFMA sequence per key
+// as scan_mfma_kernel), with the cache moved through LDS so that every load
+// instruction reads 1 KiB of contiguous cache. A workgroup covers tpc tokens of one
+// sequence, all KV heads, in steps of SR cache rows (SR / Hkv tokens x Hkv heads,
+// contiguous in the token-major cache): direct-to-LDS loads of the step, one wait,
+// then the products. Several workgroups share a compute unit, so one's loads overlap
+// another's products. Wave w takes the step's 16-row blocks p = w, w + 4, ...; block p
+// is 16 tokens (16 (p / Hkv) ..) of KV head p % Hkv. The logits of the tpc tokens
+// collect in LDS and leave at the end as one contiguous run per KV head (small
+// scattered stores between the loads cost several times their bytes).
+template <int D, int SR>
+__global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ k, const float* __restrict__ qbar,
+                                                       const int64_t* __restrict__ seq_start, int Hq, int Hkv, int G,
+                                                       int64_t total, int tpc, int nchunk, float* __restrict__ logits,
+                                                       float2* __restrict__ partials) {
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;      // rows per load instruction
+  constexpr int NIS = SR / RPI / 4;  // load instructions per wave per step
+  constexpr int NBW = SR / 64;       // 16-row blocks per wave per step
+  constexpr int KS = D / 32;
+  static_assert(NIS < 64 && NBW % 2 == 0, "step shape");
+  __shared__ __align__(16) bf16 rows[SR * D];
+  __shared__ float2 red[SR / 16][8];  // (max, sum) per block, per query head of the group
+  extern __shared__ __align__(16) float lg[];  // [Hkv][tpc][GP] logits of this workgroup
+
+  const int chunk = blockIdx.x, s = blockIdx.y;
+  const int64_t j0 = seq_start[s];
+  const int64_t L = seq_start[s + 1] - j0;
+  const int64_t tok0 = (int64_t)chunk * tpc;
+  if (tok0 >= L) return;
+  const int hshift = 31 - __builtin_clz(Hkv);
+  const int TS = SR >> hshift;  // tokens per step
+  const int nstep = (int)((min((int64_t)tpc, L - tok0) + TS - 1) / TS);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, kq = lane >> 4;
+  const int GP = G <= 4 ? 4 : 8;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)rows;
+
+  // A operands: blocks w + 4q use KV head (w + 4q) % Hkv, which alternates between
+  // two heads (q even / odd)
+  uint4 ahi[2][KS], alo[2][KS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int gg = (w + 4 * qb) & (Hkv - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float x[8];
+      if (n < G) {
+        const float* qp = qbar + ((int64_t)s * Hq + gg * G + n) * D + ks * 32 + kq * 8;
+        const float4 x0 = *reinterpret_cast<const float4*>(qp);
+        const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
+        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      uint32_t h[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a0 = x[2 * e], a1 = x[2 * e + 1];
+        h[e] = pack_bf16x2(a0, a1);
+        const float r0 = a0 - __uint_as_float(h[e] << 16), r1 = a1 - __uint_as_float(h[e] & 0xffff0000u);
+        lo[e] = pack_bf16x2(r0, r1);
+      }
+      ahi[qb][ks] = make_uint4(h[0], h[1], h[2], h[3]);
+      alo[qb][ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+  }
+  float m[NBW][4], z[NBW][4];
+#pragma unroll
+  for (int q = 0; q < NBW; ++q)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      m[q][t] = -INFINITY;
+      z[q][t] = 0.f;
+    }
+
+  const int rr = lane / CPR, pc = lane % CPR;
+  for (int i = 0; i < nstep; ++i) {
+    // ---- the step's rows into LDS: instruction u of wave w fills rows (4u + w) * RPI ..
+    const int64_t t0 = tok0 + (int64_t)i * TS;
+#pragma unroll
+    for (int u = 0; u < NIS; ++u) {
+      const int r = (4 * u + w) * RPI + rr;
+      const int64_t tok = min(t0 + (r >> hshift), L - 1);
+      const bf16* src = k + ((j0 + tok) * Hkv + (r & (Hkv - 1))) * D + ((pc ^ scan_swz<D>(r, hshift)) * 8);
+      lds_dma16(src, lds0 + (uint32_t)((4 * u + w) * RPI * D) * 2u);
+    }
+    wait_vm<0>();
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const int p = w + 4 * q;
+      const int gg = p & (Hkv - 1);
+      const int tl = (p >> hshift) * 16 + n;  // token within the step
+      const int r = (tl << hshift) + gg;
+      uint4 kb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[ks] = *reinterpret_cast<const uint4*>(rows + r * D + (((ks * 4 + kq) ^ scan_swz<D>(r, hshift)) * 8));
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = mfma16x16x32(ahi[q & 1][ks], kb[ks], acc);
+        acc = mfma16x16x32(alo[q & 1][ks], kb[ks], acc);
+      }
+      const int64_t j = t0 + tl;
+      if (j < L) {
+        if (4 * kq < GP)
+          *reinterpret_cast<float4*>(lg + ((int64_t)gg * tpc + (j - tok0)) * GP + 4 * kq) =
+              make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (kq * 4 + t < G) {
+            const float x = acc[t];
+            if (x > m[q][t]) {
+              z[q][t] = z[q][t] * fast_exp2(m[q][t] - x) + 1.f;
+              m[q][t] = x;
+            } else {
+              z[q][t] += fast_exp2(x - m[q][t]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with the rows before the next step's loads
+  }
+  // (max, sum) per block and head: over the 16 tokens of the lane group
+#pragma unroll
+  for (int q = 0; q < NBW; ++q)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float m2 = __shfl_xor(m[q][t], o), z2 = __shfl_xor(z[q][t], o);
+        ms_merge(m[q][t], z[q][t], m2, z2);
+      }
+      if (n == 0 && kq * 4 + t < 8) red[w + 4 * q][kq * 4 + t] = make_float2(m[q][t], z[q][t]);
+    }
+  __syncthreads();
+  // per query head: the blocks of its KV head (p = g, g + Hkv, ...) in order
+  if (threadIdx.x < Hkv * G) {
+    const int gg = threadIdx.x / G, hh = threadIdx.x % G;
+    float M = -INFINITY, Z = 0.f;
+    for (int p = gg; p < SR / 16; p += Hkv) ms_merge(M, Z, red[p][hh].x, red[p][hh].y);
+    partials[((int64_t)s * Hq + gg * G + hh) * nchunk + chunk] = make_float2(M, Z);
+  }
+  // the logits, one contiguous run of ntok * GP floats per KV head
+  const int n4 = (int)min((int64_t)tpc, L - tok0) * GP / 4;
+  for (int gg = 0; gg < Hkv; ++gg) {
+    float4* dst = reinterpret_cast<float4*>(logits + ((int64_t)gg * total + j0 + tok0) * GP);
+    const float4* src = reinterpret_cast<const float4*>(lg + (int64_t)gg * tpc * GP);
+    for (int i = threadIdx.x; i < n4; i += 256) st16_stream(dst + i, src[i]);
   }
 }
 
@@ -599,8 +764,30 @@ hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipSt
 
 static int maxg_of(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
+// The LDS-staged scan streams faster once there are enough workgroups to keep
+// several on every compute unit; below that the register-load scan, with its 8x more
+// workgroups (one KV head each), finishes sooner. Measured ahead with 8 KV heads
+// (1 KiB of contiguous cache per 16-row block pair); with 4 KV heads the register
+// scan was ahead, so the LDS scan is used for 8 only (the kernel takes 1, 2, 4, 8).
+static bool scan_in_lds(const Shape& s) {
+  return s.bf16 && s.Hkv == 8 && s.G <= 8 && s.total >= (int64_t)4 * 256 * kScanTok;
+}
+
 hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st) {
   dim3 grid(ws.nchunk, s.Hkv, s.nseq);
+  if (scan_in_lds(s)) {
+    const size_t smem = (size_t)s.Hkv * ws.tpc * (s.G <= 4 ? 4 : 8) * sizeof(float);
+    const void* kern = s.D == 128 ? (const void*)scan_lds_kernel<128, 128> : (const void*)scan_lds_kernel<64, 128>;
+    hipError_t e = allow_smem(kern, smem);
+    if (e != hipSuccess) return e;
+    if (s.D == 128)
+      klaunch(scan_lds_kernel<128, 128>, dim3(ws.nchunk, s.nseq), 256, smem, st, (const bf16*)k, ws.qbar, s.seq_start,
+              s.Hq, s.Hkv, s.G, s.total, ws.tpc, ws.nchunk, ws.logits, ws.partials);
+    else
+      klaunch(scan_lds_kernel<64, 128>, dim3(ws.nchunk, s.nseq), 256, smem, st, (const bf16*)k, ws.qbar, s.seq_start,
+              s.Hq, s.Hkv, s.G, s.total, ws.tpc, ws.nchunk, ws.logits, ws.partials);
+    return hipGetLastError();
+  }
   if (s.bf16) {
     if (s.D == 128)
       klaunch(scan_mfma_kernel<128>, grid, 256, 0, st, (const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,

@@ -55,6 +55,12 @@ SMALL = {
     # the largest candidate set (C = 16384: LDS beyond 64 KiB in the emit and top-K kernels)
     "c16384": Workload("c16384", nseq=1, L=40000, Hq=8, Hkv=2, d=128, dtype="bf16", B=8, C=16384, topk=3000, T=1,
                        seed_base=7900),
+    # batches long enough for the LDS-staged scan (8 KV heads, >= 262144 tokens in all):
+    # head dim 64 with a partial last step; 8 query heads per KV head
+    "lds_scan_d64": Workload("lds_scan_d64", nseq=3, L=90000, Hq=16, Hkv=8, d=64, dtype="bf16", B=4,
+                             C=700, topk=100, T=1, planted=8, seed_base=8100),
+    "lds_scan_g8": Workload("lds_scan_g8", nseq=2, L=131100, Hq=64, Hkv=8, d=128, dtype="bf16", B=2, C=600,
+                            topk=64, T=1, planted=8, seed_base=8200),
     # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
     "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
                            T=2, seed_base=7800),
