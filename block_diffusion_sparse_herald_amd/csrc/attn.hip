@@ -49,7 +49,7 @@ __device__ __forceinline__ int attn_kswz(int r) {
 // 16-byte chunk c of V^T row e (64 keys, 128 bytes) is stored at chunk c ^ attn_vswz(e).
 __device__ __forceinline__ int attn_vswz(int e) { return (e >> 1) & 7; }
 
-template <int D, int TW>
+template <int D>
 __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kb,
                                                    const bf16* __restrict__ vb, const bf16* __restrict__ k_sel,
                                                    const bf16* __restrict__ v_sel, AttnGeom a, float scale2,
@@ -87,12 +87,8 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   const int has_ib = b1 == nA + 1 ? 1 : 0;  // the in-block keys belong to the last range
   const int nb = b1 - b0;                    // blocks of this workgroup: list index 0 is the
   const int nst = a.nst;                     // in-block block when it has one, then subset
-  // wave wl of each group holds query tiles tile0 .. tile0 + TW - 1
-  const int tile0 = rs * a.tpw + wl * TW;
-  bool has_t[TW];
-#pragma unroll
-  for (int t = 0; t < TW; ++t) has_t[t] = wl * TW + t < a.tpw && (tile0 + t) * 16 < R;
-  const bool has_tile = has_t[0];
+  const int tile = rs * a.tpw + wl;
+  const bool has_tile = wl < a.tpw && tile * 16 < R;
 
   const bf16* ksrc = k_sel + (int64_t)unit * topk * D;
   const bf16* vsrc = v_sel + (int64_t)unit * D * a.ldv;
@@ -132,15 +128,14 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   int next = has_ib;  // next list index to fetch
   for (; next < min(nb, nst); ++next) issue(next);
 
-  // ---- query fragments of this wave's tiles
-  uint4 qf[TW][KS];
-#pragma unroll
-  for (int t = 0; t < TW; ++t) {
-    const int r = (tile0 + t) * 16 + lr;
+  // ---- query fragments of this wave's tile
+  uint4 qf[KS];
+  {
+    const int r = tile * 16 + lr;
     const bf16* qr =
-        has_t[t] && r < R ? q + (((int64_t)s * B + r / G) * a.Hq + g * G + r % G) * D + qd * 8 : nullptr;
+        has_tile && r < R ? q + (((int64_t)s * B + r / G) * a.Hq + g * G + r % G) * D + qd * 8 : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[t][ks] = qr ? ld16(qr + ks * 32) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qr ? ld16(qr + ks * 32) : make_uint4(0, 0, 0, 0);
   }
   // ---- in-block keys (list index 0, stage 0): K rows and V^T (transposed) via registers
   if (has_ib) {
@@ -173,15 +168,10 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
     }
   }
 
-  f32x4_t o[TW][DT];
-  float m[TW], l[TW];
+  f32x4_t o[DT];
 #pragma unroll
-  for (int t = 0; t < TW; ++t) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m[t] = -INFINITY;
-    l[t] = 0.f;
-  }
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
   // The query fragments (and in-block rows) are the only loads the compiler tracks.
   // Waiting for them here, once, keeps it from placing that wait inside the loop,
   // where (the direct-to-LDS transfers being invisible to it) it would be a full
@@ -207,29 +197,24 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
     const bf16* sv = sk + KB * D;
     const int valid = (i < has_ib) ? B : min(KB, topk - (b0 + i - has_ib) * KB);
 
-    // ---- S^T = K Q^T per tile: lane holds keys attn_key_of(mt, 4*qd + i) of query row
-    //      lr. The K fragments are read once for the TW tiles; the V^T fragments are
-    //      read while the softmax runs.
-    f32x4_t sacc[TW][4];
-    {
-      uint4 kf[4][KS];
+    // ---- S^T = K Q^T: lane holds keys attn_key_of(mt, 4*qd + i) of query row lr. All
+    //      fragment reads of a product are issued before its first MFMA; the V^T
+    //      fragments are read while the softmax runs.
+    uint4 kf[4][KS];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int r = attn_key_of(mt, lr);
+    for (int mt = 0; mt < 4; ++mt) {
+      const int r = attn_key_of(mt, lr);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kf[mt][ks] = *reinterpret_cast<const uint4*>(sk + r * D + (((ks * 4 + qd) ^ attn_kswz<D>(r)) * 8));
-      }
-#pragma unroll
-      for (int t = 0; t < TW; ++t) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) sacc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) sacc[t][mt] = mfma16x16x32(kf[mt][ks], qf[t][ks], sacc[t][mt]);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        kf[mt][ks] = *reinterpret_cast<const uint4*>(sk + r * D + (((ks * 4 + qd) ^ attn_kswz<D>(r)) * 8));
     }
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) sacc[mt] = mfma16x16x32(kf[mt][ks], qf[ks], sacc[mt]);
     uint4 vf[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -240,109 +225,98 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
       }
 
     // ---- online softmax (base 2) with the scale folded into one FMA
-    uint4 bp[TW][2];
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (valid < KB) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (attn_key_of(mt, 4 * qd + u) >= valid) sacc[t][mt][u] = -INFINITY;
-      }
-      float bm = fmaxf(fmaxf(fmaxf(sacc[t][0][0], sacc[t][0][1]), fmaxf(sacc[t][0][2], sacc[t][0][3])),
-                       fmaxf(fmaxf(sacc[t][1][0], sacc[t][1][1]), fmaxf(sacc[t][1][2], sacc[t][1][3])));
-      bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(sacc[t][2][0], sacc[t][2][1]), fmaxf(sacc[t][2][2], sacc[t][2][3])),
-                           fmaxf(fmaxf(sacc[t][3][0], sacc[t][3][1]), fmaxf(sacc[t][3][2], sacc[t][3][3]))));
-      bm = xmax4(bm) * scale2;
-      if (__ballot(bm > m[t] + kRaise)) {
-        const float mn = fmaxf(m[t], bm);
-        const float alpha = fast_exp2(m[t] - mn);
-        l[t] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
-        m[t] = mn;
-      }
-      float pp[4][4];
-      float ps = 0.f;
+    if (valid < KB) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pp[mt][u] = fast_exp2(fmaf(sacc[t][mt][u], scale2, -m[t]));
-          ps += pp[mt][u];
-        }
-      l[t] += ps;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        bp[t][h2] = make_uint4(pack_bf16x2(pp[2 * h2][0], pp[2 * h2][1]), pack_bf16x2(pp[2 * h2][2], pp[2 * h2][3]),
-                               pack_bf16x2(pp[2 * h2 + 1][0], pp[2 * h2 + 1][1]),
-                               pack_bf16x2(pp[2 * h2 + 1][2], pp[2 * h2 + 1][3]));
+        for (int t = 0; t < 4; ++t)
+          if (attn_key_of(mt, 4 * qd + t) >= valid) sacc[mt][t] = -INFINITY;
     }
+    float bm = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
+                         fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
+    bm = xmax4(bm) * scale2;
+    if (__ballot(bm > m + kRaise)) {
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m = mn;
+    }
+    float p[4][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        p[mt][t] = fast_exp2(fmaf(sacc[mt][t], scale2, -m));
+        ps += p[mt][t];
+      }
+    l += ps;
+    uint4 bp[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      bp[h2] = make_uint4(pack_bf16x2(p[2 * h2][0], p[2 * h2][1]), pack_bf16x2(p[2 * h2][2], p[2 * h2][3]),
+                          pack_bf16x2(p[2 * h2 + 1][0], p[2 * h2 + 1][1]),
+                          pack_bf16x2(p[2 * h2 + 1][2], p[2 * h2 + 1][3]));
 
     // ---- O^T += V^T P^T over the two 32-key halves of the block
 #pragma unroll
-    for (int t = 0; t < TW; ++t)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) o[t][dt] = mfma16x16x32(vf[dt][h2], bp[t][h2], o[t][dt]);
+      for (int h2 = 0; h2 < 2; ++h2) o[dt] = mfma16x16x32(vf[dt][h2], bp[h2], o[dt]);
   }
-#pragma unroll
-  for (int t = 0; t < TW; ++t) l[t] = xsum4(l[t]);
+  l = xsum4(l);
 
   // ---- merge the two groups through LDS (the stages are free once all waves are here)
   constexpr int LDO = D + 4;
-  float* xo = reinterpret_cast<float*>(stages);  // [4 waves][TW tiles][16 rows][LDO]
-  float2* xml = reinterpret_cast<float2*>(xo + 4 * TW * 16 * LDO);
+  float* xo = reinterpret_cast<float*>(stages);  // [4 tiles][16 rows][LDO]
+  float2* xml = reinterpret_cast<float2*>(xo + 4 * 16 * LDO);
   __syncthreads();
   if (grp == 1 && has_tile) {
+    float* orow = xo + (wl * 16 + lr) * LDO + qd * 4;
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      float* orow = xo + ((wl * TW + t) * 16 + lr) * LDO + qd * 4;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(orow + dt * 16) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
-      if (qd == 0) xml[(wl * TW + t) * 16 + lr] = make_float2(m[t], l[t]);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(orow + dt * 16) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (qd == 0) xml[wl * 16 + lr] = make_float2(m, l);
   }
   __syncthreads();
   if (grp == 1 || !has_tile) return;
-#pragma unroll
-  for (int t = 0; t < TW; ++t) {
-    if (!has_t[t]) break;
-    const float2 mb = xml[(wl * TW + t) * 16 + lr];
-    const float M = fmaxf(m[t], mb.x);
-    const float fa = fast_exp2(m[t] - M), fb = mb.x == -INFINITY ? 0.f : fast_exp2(mb.x - M);
-    const float L = l[t] * fa + mb.y * fb;
-    const float* xrow = xo + ((wl * TW + t) * 16 + lr) * LDO + qd * 4;
+  {
+    const float2 mb = xml[wl * 16 + lr];
+    const float M = fmaxf(m, mb.x);
+    const float fa = fast_exp2(m - M), fb = mb.x == -INFINITY ? 0.f : fast_exp2(mb.x - M);
+    l = l * fa + mb.y * fb;
+    m = M;
+    const float* orow = xo + (wl * 16 + lr) * LDO + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const float4 ob = *reinterpret_cast<const float4*>(xrow + dt * 16);
-      o[t][dt][0] = o[t][dt][0] * fa + ob.x * fb;
-      o[t][dt][1] = o[t][dt][1] * fa + ob.y * fb;
-      o[t][dt][2] = o[t][dt][2] * fa + ob.z * fb;
-      o[t][dt][3] = o[t][dt][3] * fa + ob.w * fb;
+      const float4 ob = *reinterpret_cast<const float4*>(orow + dt * 16);
+      o[dt][0] = o[dt][0] * fa + ob.x * fb;
+      o[dt][1] = o[dt][1] * fa + ob.y * fb;
+      o[dt][2] = o[dt][2] * fa + ob.z * fb;
+      o[dt][3] = o[dt][3] * fa + ob.w * fb;
     }
-    const int r = (tile0 + t) * 16 + lr;
-    if (a.nks == 1) {
-      if (r < R) {
-        bf16* orow = out + (((int64_t)s * B + r / G) * a.Hq + g * G + r % G) * D + qd * 4;
-        const float inv = 1.f / L;
+  }
+  const int r = tile * 16 + lr;
+  if (a.nks == 1) {
+    if (r >= R) return;
+    bf16* orow = out + (((int64_t)s * B + r / G) * a.Hq + g * G + r % G) * D + qd * 4;
+    const float inv = 1.f / l;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<uint2*>(orow + dt * 16) = make_uint2(pack_bf16x2(o[t][dt][0] * inv, o[t][dt][1] * inv),
-                                                                 pack_bf16x2(o[t][dt][2] * inv, o[t][dt][3] * inv));
-      }
-    } else {
-      const int64_t prow = ((int64_t)unit * a.nks + ksp) * a.rpad + r;
-      bf16* orow = o_part + prow * D + qd * 4;
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<uint2*>(orow + dt * 16) =
+          make_uint2(pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv));
+  } else {
+    const int64_t prow = ((int64_t)unit * a.nks + ksp) * a.rpad + r;
+    bf16* orow = o_part + prow * D + qd * 4;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<uint2*>(orow + dt * 16) =
-            make_uint2(pack_bf16x2(o[t][dt][0], o[t][dt][1]), pack_bf16x2(o[t][dt][2], o[t][dt][3]));
-      if (qd == 0) ml_part[prow] = make_float2(M, L);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<uint2*>(orow + dt * 16) =
+          make_uint2(pack_bf16x2(o[dt][0], o[dt][1]), pack_bf16x2(o[dt][2], o[dt][3]));
+    if (qd == 0) ml_part[prow] = make_float2(m, l);
   }
 }
 
@@ -507,8 +481,7 @@ AttnGeom attn_geom(const Shape& s) {
   a.nunits = s.nseq * s.Hkv;
   const int ntiles = (s.B * s.G + 15) / 16;
   const int nblk = (s.topk + kAttnKeyBlock - 1) / kAttnKeyBlock + 1;
-  a.tw = 1;
-  a.tpw = std::min(ntiles, 4 * a.tw);
+  a.tpw = std::min(ntiles, 4);
   a.nrs = (ntiles + a.tpw - 1) / a.tpw;
   a.rpad = ntiles * 16;
   // A workgroup keeps at most kAttnMaxStages blocks in flight, so one pulling a long
@@ -541,7 +514,7 @@ size_t attn_ws_bytes(const Shape& s) {
 template <int D>
 static size_t attn_smem(const AttnGeom& a) {
   const size_t stages = (size_t)a.nst * 2 * kAttnKeyBlock * D * sizeof(bf16);
-  const size_t merge = (size_t)4 * a.tw * 16 * ((D + 4) * sizeof(float) + sizeof(float2));
+  const size_t merge = (size_t)4 * 16 * (D + 4) * sizeof(float) + 4 * 16 * sizeof(float2);
   return std::max(stages, merge);
 }
 
@@ -557,16 +530,11 @@ static hipError_t launch_attn_bf16(const AttnGeom& a, const void* q, const void*
     ml_part = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(rows * D * sizeof(bf16)));
   }
   const size_t smem = attn_smem<D>(a);
-  const void* kern = a.tw == 2 ? (const void*)attn_kernel<D, 2> : (const void*)attn_kernel<D, 1>;
-  hipError_t e = allow_smem(kern, smem);
+  hipError_t e = allow_smem((const void*)attn_kernel<D>, smem);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.nitems + 7) / 8 * 8));
-  if (a.tw == 2)
-    klaunch(attn_kernel<D, 2>, grid, 512, smem, st, (const bf16*)q, (const bf16*)kb, (const bf16*)vb,
-            (const bf16*)k_sel, (const bf16*)v_sel, a, scale2, (bf16*)out, o_part, ml_part);
-  else
-    klaunch(attn_kernel<D, 1>, grid, 512, smem, st, (const bf16*)q, (const bf16*)kb, (const bf16*)vb,
-            (const bf16*)k_sel, (const bf16*)v_sel, a, scale2, (bf16*)out, o_part, ml_part);
+  klaunch(attn_kernel<D>, grid, 512, smem, st, (const bf16*)q, (const bf16*)kb, (const bf16*)vb, (const bf16*)k_sel,
+          (const bf16*)v_sel, a, scale2, (bf16*)out, o_part, ml_part);
   return hipGetLastError();
 }
 

@@ -59,8 +59,7 @@ struct AttnGeom {
   int B, G, Hq, Hkv, topk;
   int64_t ldv;
   int nunits;  // nseq * Hkv
-  int tw;      // 16-row query tiles per wave (1 or 2)
-  int tpw;     // 16-row query tiles per workgroup (up to 4 * tw)
+  int tpw;     // 16-row query tiles per workgroup (one per wave)
   int nrs;     // row splits: workgroups per key range
   int rpad;    // rows rounded up to whole tiles
   int nks;     // key ranges per unit

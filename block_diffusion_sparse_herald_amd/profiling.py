@@ -30,7 +30,7 @@ CSRC = os.path.join(ROOT, "block_diffusion_sparse_herald_amd", "csrc")
 KERNELS = {
     "attn_kernel+attn_combine_kernel": (["herald::attn_kernel", "herald::attn_combine_kernel"], ["attn.hip", "common.hpp"]),
     "attn_kernel": (["herald::attn_kernel"], ["attn.hip", "common.hpp"]),
-    "scan": (["herald::scan_mfma_kernel"], ["select.hip", "common.hpp"]),
+    "scan": (["herald::scan_mfma_kernel", "herald::scan_lds_kernel"], ["select.hip", "common.hpp"]),
     "refine_stats": (["herald::refine_stats_kernel"], ["refine.hip", "common.hpp"]),
     "refine_scores": (["herald::refine_scores_kernel"], ["refine.hip", "common.hpp"]),
     "gather": (["herald::gather_kernel"], ["gather.hip", "common.hpp"]),
