@@ -30,7 +30,7 @@ CSRC = os.path.join(ROOT, "block_diffusion_sparse_herald_amd", "csrc")
 KERNELS = {
     "attn_kernel+attn_combine_kernel": (["herald::attn_kernel", "herald::attn_combine_kernel"], ["attn.hip", "common.hpp"]),
     "attn_kernel": (["herald::attn_kernel"], ["attn.hip", "common.hpp"]),
-    "scan": (["herald::scan_mfma_kernel", "herald::scan_lds_kernel"], ["select.hip", "common.hpp"]),
+    "scan": (["herald::scan_"], ["select.hip", "common.hpp"]),  # whichever scan kernel the workload uses
     "refine_stats": (["herald::refine_stats_kernel"], ["refine.hip", "common.hpp"]),
     "refine_scores": (["herald::refine_scores_kernel"], ["refine.hip", "common.hpp"]),
     "gather": (["herald::gather_kernel"], ["gather.hip", "common.hpp"]),
@@ -104,6 +104,8 @@ def main(argv=None) -> int:
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-bytes", type=int, required=True)
+    ap.add_argument("--calibration-from", default="",
+                    help="take the copy factors from another workload's JSON (for runs without replica copies)")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--stats-cmd", default="")
     ap.add_argument("--pmc-cmd", default="")
@@ -122,8 +124,13 @@ def main(argv=None) -> int:
 
     fetch = counter_means(args.fetch, "FETCH_SIZE")
     write = counter_means(args.write, "WRITE_SIZE")
-    ff, fcopy = copy_factor(fetch, args.copy_bytes)
-    fw, wcopy = copy_factor(write, args.copy_bytes)
+    if args.calibration_from:
+        with open(args.calibration_from) as fh:
+            cal = json.load(fh)["calibration"]
+        ff, fcopy, fw, wcopy = cal["fetch_factor"], cal["fetch_kib_per_copy"], cal["write_factor"], cal["write_kib_per_copy"]
+    else:
+        ff, fcopy = copy_factor(fetch, args.copy_bytes)
+        fw, wcopy = copy_factor(write, args.copy_bytes)
     entries = []
     for kname, (prefixes, files) in KERNELS.items():
         try:
@@ -135,7 +142,8 @@ def main(argv=None) -> int:
                         "sources_sha256": sources_digest(files)})
     doc = {"calibration": {"copy_bytes": args.copy_bytes, "fetch_kib_per_copy": round(fcopy, 1),
                            "write_kib_per_copy": round(wcopy, 1), "fetch_factor": round(ff, 4),
-                           "write_factor": round(fw, 4)},
+                           "write_factor": round(fw, 4),
+                           "from": os.path.basename(args.calibration_from) if args.calibration_from else "this run"},
            "command": args.pmc_cmd, "entries": entries}
     with open(os.path.join(args.out_dir, f"hbm_traffic_{args.workload}.json"), "w") as fh:
         json.dump(doc, fh, indent=1)
