@@ -10,6 +10,14 @@ least 512 MiB and consecutive steps rotate through them.
 Prints one JSON line. `roofline` is for the kernel that takes the most time per
 step, timed with HIP events recorded by the library around that kernel on the
 stream it runs on. `cpu_baseline` times the CPU oracle on a bounded sample.
+
+`--method dense` and `--method mage` time the two exact layer baselines instead,
+through the same calls: dense attention over the whole cache for the T steps
+(herald_block_attn with topk = L, the cache gathered once into the subset layout
+before timing), and MAGE-exact selection (herald_refine_topk with every key a
+candidate, then gather and the T steps over the top-K). Both need sequences of one
+length. They print the same record with "method" set and `vs_herald` = their
+blocks/s over the HERALD path's, measured in the same process.
 """
 
 from __future__ import annotations
@@ -107,6 +115,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step directly instead of replaying graphs")
+    ap.add_argument("--method", choices=["herald", "dense", "mage"], default="herald",
+                    help="the HERALD path (default) or one of the exact layer baselines")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the per-block path needs no "
@@ -139,6 +149,8 @@ def main(argv=None):
     q0 = dev["q0"]
     qs, kbs, vbs = ([dev[n].offset(t) for t in range(wl.T)] for n in ("q_steps", "kb_steps", "vb_steps"))
     stream = hip.stream()
+    if args.method != "herald":
+        return exact_baseline(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, stream)
 
     call_of = {"scan": "select", "score_hist": "select", "radix": "select", "emit": "select",
                "refine_stats": "refine", "refine_scores": "refine", "refine_select": "refine",
@@ -281,6 +293,99 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(wl, batch, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def time_steps(hip, stream, step, steps: int, warmup: int, eager: bool) -> float:
+    """Milliseconds for `steps` steps (graph replays unless eager), after `warmup` eager steps."""
+    for i in range(warmup):
+        step(i)
+    hip.sync()
+    graphs = [] if eager else [hip.capture(stream, lambda: step(i)) for i in range(steps)]
+    a, b = hip.event(), hip.event()
+    hip.sync()
+    hip.record(a, stream)
+    for i in range(steps):
+        if graphs:
+            hip.launch(graphs[i], stream)
+        else:
+            step(i)
+    hip.record(b, stream)
+    hip.sync()
+    return hip.elapsed_ms(a, b)
+
+
+def exact_baseline(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, stream):
+    """Dense attention or MAGE-exact selection, timed like the HERALD path, with the
+    HERALD path timed alongside in the same process for the ratio."""
+    import numpy as np
+
+    from block_diffusion_sparse_herald_amd import herald as H
+    from block_diffusion_sparse_herald_amd.hiprt import DevArray
+    from block_diffusion_sparse_herald_amd.runner import BlockRunner
+
+    lengths = np.asarray(batch.lengths)
+    if (lengths != lengths[0]).any():
+        print(f"--method {args.method} needs sequences of one length (the subset size is one number per call); "
+              f"workload {wl.name} is ragged", file=sys.stderr)
+        return 2
+    L = int(lengths[0])
+    alloc = lambda shape, dt, zero=False: DevArray(hip, shape, dt, zero)  # noqa: E731
+    iota = DevArray.from_host(hip, np.ascontiguousarray(
+        np.broadcast_to(np.arange(L, dtype=np.int32), (wl.nseq, wl.Hkv, L))))
+    if args.method == "dense":
+        b = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, L, L, wl.dtype, alloc=alloc,
+                        seq_start_dev=seq_dev)
+        # the whole cache in the subset layout, once; copies rotate like the cache replicas
+        pool_bytes = b.k_sel.nbytes + b.v_sel.nbytes
+        pools = []
+        for _ in range(max(1, math.ceil(512 * 2**20 / pool_bytes))):
+            b.gather(kv[0][0], kv[0][1], sel=iota, stream=stream)
+            hip.sync()
+            pools.append((b.k_sel.clone(), b.v_sel.clone()))
+        hip.sync()
+
+        def step(i):
+            ks, vs = pools[i % len(pools)]
+            for t in range(wl.T):
+                H.herald_block_attn(b.problem, qs[t], kbs[t], vbs[t], ks, vs, b.out, b.ws["attn"], stream=stream)
+        what = f"dense attention over all {L} keys + {wl.B} in-block keys, {wl.T} steps; {len(pools)} pool copies"
+    else:
+        b = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, L, wl.topk, wl.dtype, alloc=alloc,
+                        seq_start_dev=seq_dev)
+
+        def step(i):
+            k, v = kv[i % len(kv)]
+            b.refine(q0, k, cand=iota, stream=stream)
+            b.gather(k, v, stream=stream)
+            for t in range(wl.T):
+                b.attn(qs[t], kbs[t], vbs[t], stream=stream)
+        what = f"exact top-{wl.topk} of the real queries over all {L} keys (refine with C = L), gather, {wl.T} steps"
+
+    def herald_step(i):
+        k, v = kv[i % len(kv)]
+        r.select(q0, k, stream=stream)
+        r.refine(q0, k, stream=stream)
+        r.gather(k, v, stream=stream)
+        for t in range(wl.T):
+            r.attn(qs[t], kbs[t], vbs[t], stream=stream)
+
+    log(f"[bench] {args.method}: {what}")
+    ms = time_steps(hip, stream, step, args.steps, args.warmup, args.eager)
+    ms_h = time_steps(hip, stream, herald_step, args.steps, args.warmup, args.eager)
+    value = wl.nseq * args.steps / (ms / 1e3)
+    herald_value = wl.nseq * args.steps / (ms_h / 1e3)
+    log(f"[bench] {args.method}: {ms / args.steps * 1e3:.1f} us/step; HERALD path {ms_h / args.steps * 1e3:.1f} us/step")
+    result = {
+        "metric": METRIC, "method": args.method, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "nseq": wl.nseq, "L": L, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.d,
+                   "B": wl.B, "topk": L if args.method == "dense" else wl.topk, "C": L, "T": wl.T},
+        "tokens_per_s": round(value * wl.B, 1), "launch": "eager" if args.eager else "hip_graph_per_step",
+        "what": what, "herald_value": round(herald_value, 2), "vs_herald": round(value / herald_value, 4),
+    }
     print(json.dumps(result), flush=True)
     return 0
 

@@ -108,8 +108,6 @@ herald_status make_shape(const herald_problem* p, Shape* s) {
     return fail(HERALD_ERR_UNSUPPORTED, "head_dim = %d is not 64 or 128", p->head_dim);
   if (p->dtype != HERALD_F32 && p->dtype != HERALD_BF16) return fail(HERALD_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
   if (p->num_candidates < 1) return fail(HERALD_ERR_INVALID_ARG, "num_candidates = %d < 1", p->num_candidates);
-  if (p->num_candidates > kMaxCandidates)
-    return fail(HERALD_ERR_UNSUPPORTED, "num_candidates = %d exceeds %d", p->num_candidates, kMaxCandidates);
   if (p->topk < 1 || p->topk > p->num_candidates)
     return fail(HERALD_ERR_INVALID_ARG, "topk = %d outside [1, num_candidates = %d]", p->topk, p->num_candidates);
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
@@ -184,6 +182,13 @@ RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
 
 size_t gather_host_bytes(const Shape& s) { return align256(2 * (size_t)s.nseq * s.Hkv * s.topk * s.D * elem_bytes(s)); }
 
+// The merged-query selection keeps its candidate set in LDS during emission.
+herald_status check_select_shape(const Shape& s) {
+  if (s.C > kMaxCandidates)
+    return fail(HERALD_ERR_UNSUPPORTED, "num_candidates = %d exceeds %d for herald_select_merged", s.C, kMaxCandidates);
+  return HERALD_OK;
+}
+
 herald_status check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return HERALD_OK;
   if (!ws) return fail(HERALD_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -202,7 +207,10 @@ herald_status herald_workspace_size(const herald_problem* p, int op, size_t* byt
   HERALD_TRY(make_shape(p, &s));
   size_t n = 0;
   switch (op) {
-    case HERALD_OP_SELECT: carve_select(s, nullptr, &n); break;
+    case HERALD_OP_SELECT:
+      HERALD_TRY(check_select_shape(s));
+      carve_select(s, nullptr, &n);
+      break;
     case HERALD_OP_REFINE: carve_refine(s, nullptr, &n); break;
     case HERALD_OP_ATTN: n = attn_ws_bytes(s); break;
     case HERALD_OP_GATHER_HOST: n = gather_host_bytes(s); break;
@@ -220,6 +228,7 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
                                    hipStream_t stream) {
   Shape s;
   HERALD_TRY(make_shape(p, &s));
+  HERALD_TRY(check_select_shape(s));
   if (s.nseq == 0) return ok();
   HERALD_TRY(check_ptr(q_merge, "q_merge"));
   HERALD_TRY(check_ptr(k_cache, "k_cache"));

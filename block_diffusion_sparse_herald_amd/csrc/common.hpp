@@ -298,7 +298,8 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* hist, uint32_t k,
 
 // ---------------------------------------------------------------- radix threshold in LDS
 
-// The k-th largest of the n keys u[0..n) in LDS (fp32 bit patterns of non-negative
+// The k-th largest of the n keys u[0..n) (in LDS, or in global memory for sets too
+// large for it; fp32 bit patterns of non-negative
 // scores, so unsigned order is value order), digit by digit (11, 11, 10 bits) with
 // histograms h[0..kRadixBins) in LDS. With have_first, h already holds the histogram
 // of the first digit. Returns the key's bit pattern and, in *ties, how many keys
@@ -343,7 +344,8 @@ __device__ __forceinline__ uint32_t lds_radix_threshold(const uint32_t* u, int n
 
 // ---------------------------------------------------------------- selection emission
 
-// Writes, in ascending position order, every position i < n whose key u[i] (LDS) is
+// Writes, in ascending position order, every position i < n whose key u[i] (LDS or
+// global memory) is
 // above thr, plus the first ties_wanted positions whose key equals thr: out[p] gets
 // the position (or idx[position] when idx is not NULL), outs[p] (if not NULL) the
 // key as a float. Wave w of NW scans positions [w*span, (w+1)*span) with ballots,

@@ -233,22 +233,27 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
   }
 }
 
-// Exact top-K of the refine scores of one (sequence, KV head), in LDS: scores and
-// candidate indices staged with 16-byte loads, three radix digits, ballot emission.
+// Exact top-K of the refine scores of one (sequence, KV head): three radix digits,
+// ballot emission. STAGED (C <= kMaxCandidates): scores and candidate indices first
+// copied to LDS with 16-byte loads; otherwise (candidate sets up to the whole sequence)
+// the same passes read them from global memory.
+template <bool STAGED>
 __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __restrict__ cand,
                                                             const float* __restrict__ rscore, int Hkv, int C,
                                                             int topk, int32_t* __restrict__ topk_idx,
                                                             float* __restrict__ topk_score) {
   constexpr int NT = 1024;
   const int g = blockIdx.x, s = blockIdx.y;
-  extern __shared__ uint32_t sm[];  // [C] scores, then [C] candidate indices
-  uint32_t* u = sm;
-  int32_t* ci = reinterpret_cast<int32_t*>(sm + C);
+  extern __shared__ uint32_t sm[];  // STAGED: [C] scores, then [C] candidate indices
   __shared__ uint32_t h[kRadixBins];
   __shared__ uint32_t wcnt[NT / 64][2];
   __shared__ uint32_t dig[2];
   const int64_t base = ((int64_t)s * Hkv + g) * C;
-  {
+  const uint32_t* u = STAGED ? sm : reinterpret_cast<const uint32_t*>(rscore + base);
+  const int32_t* ci = STAGED ? reinterpret_cast<const int32_t*>(sm + C) : cand + base;
+  if (STAGED) {
+    uint32_t* su = sm;
+    int32_t* sc = reinterpret_cast<int32_t*>(sm + C);
     constexpr int U = 4;
     const int n4 = C % 4 == 0 ? C / 4 : 0;  // 16-byte loads need 16-byte aligned rows
     for (int i0 = 0; i0 < n4; i0 += NT * U) {
@@ -263,17 +268,17 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
       for (int k = 0; k < U; ++k) {
         const int i = i0 + k * NT + threadIdx.x;
         if (i < n4) {
-          reinterpret_cast<uint4*>(u)[i] = a[k];
-          reinterpret_cast<uint4*>(ci)[i] = b[k];
+          reinterpret_cast<uint4*>(su)[i] = a[k];
+          reinterpret_cast<uint4*>(sc)[i] = b[k];
         }
       }
     }
     for (int i = 4 * n4 + threadIdx.x; i < C; i += NT) {
-      u[i] = __float_as_uint(rscore[base + i]);
-      ci[i] = cand[base + i];
+      su[i] = __float_as_uint(rscore[base + i]);
+      sc[i] = cand[base + i];
     }
+    __syncthreads();
   }
-  __syncthreads();
   uint32_t ties;
   const uint32_t thr = lds_radix_threshold<NT>(u, C, (uint32_t)topk, h, dig, false, &ties);
   lds_emit<NT / 64>(u, C, thr, ties, ci, topk_idx + ((int64_t)s * Hkv + g) * topk,
@@ -510,11 +515,16 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
 
 hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
                                 float* topk_score, hipStream_t st) {
+  if (s.C > kMaxCandidates) {
+    klaunch(refine_select_kernel<false>, dim3(s.Hkv, s.nseq), 1024, 0, st, cand, ws.rscore, s.Hkv, s.C, s.topk,
+            topk_idx, topk_score);
+    return hipGetLastError();
+  }
   const size_t smem = 2 * (size_t)s.C * sizeof(uint32_t);
-  hipError_t e = allow_smem((const void*)refine_select_kernel, smem);
+  hipError_t e = allow_smem((const void*)refine_select_kernel<true>, smem);
   if (e != hipSuccess) return e;
-  klaunch(refine_select_kernel, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, s.Hkv, s.C, s.topk, topk_idx,
-                                                                topk_score);
+  klaunch(refine_select_kernel<true>, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, s.Hkv, s.C, s.topk,
+          topk_idx, topk_score);
   return hipGetLastError();
 }
 

@@ -69,7 +69,15 @@ class BlockRunner:
         self.out = alloc((nseq, B, Hq, d), el)
         self.ws = {}
         for name, op in [("select", H.HERALD_OP_SELECT), ("refine", H.HERALD_OP_REFINE), ("attn", H.HERALD_OP_ATTN)]:
-            n = H.herald_workspace_size(self.problem, op)
+            try:
+                n = H.herald_workspace_size(self.problem, op)
+            except H.HeraldError as e:
+                # the merged-query selection takes at most 16384 candidates; larger sets (the
+                # exact baselines: every key a candidate) use the other three calls only
+                if name == "select" and e.status == H.HERALD_ERR_UNSUPPORTED:
+                    self.ws[name] = None
+                    continue
+                raise
             self.ws[name] = alloc((max(n, 256),), np.uint8, zero=name == "attn")
         self.attn_splits = H.herald_attn_splits(self.problem)
 

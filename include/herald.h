@@ -76,7 +76,12 @@ typedef enum herald_op {
  *   nseq >= 0 (0 makes every call a no-op); 1 <= block_size <= 64;
  *   num_kv_heads >= 1; num_q_heads = G * num_kv_heads with 1 <= G <= 8;
  *   block_size * G <= 256; head_dim in {64, 128};
- *   1 <= topk <= num_candidates <= 16384; num_candidates <= L_s <= 2^30 for every s;
+ *   1 <= topk <= num_candidates <= L_s <= 2^30 for every s; herald_select_merged (and
+ *   its workspace query) also needs num_candidates <= 16384 (HERALD_ERR_UNSUPPORTED
+ *   otherwise). The other calls take any candidate count and subset size up to the
+ *   shortest sequence, which expresses the exact baselines: refine over every key of
+ *   the sequence (num_candidates = L_s), or attention over the whole cache
+ *   (topk = L_s).
  *   softmax_scale finite and >= 0 (0 selects 1/sqrt(head_dim)).
  * seq_start_host and seq_start_dev hold the same nseq+1 offsets (host copy for
  * validation and launch sizing, device copy for the kernels); seq_start[0] = 0.
@@ -122,6 +127,9 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
  *   q_refine   [nseq][B][Hq][d]   device, read
  *   k_cache    [sumL][Hkv][d]     device, read
  *   cand_idx   [nseq][Hkv][C]     device, read: ascending, sequence-local, each < L_s
+ *                                 (C = L_s with cand_idx = 0..L_s-1 is the exact top-K
+ *                                 of the real queries over the whole cache; candidate
+ *                                 sets above 16384 are ranked from global memory)
  *   topk_idx   [nseq][Hkv][topk]  device, written: int32, ascending, sequence-local
  *   topk_score [nseq][Hkv][topk]  device, written (may be NULL): fp32 R_g of each pick
  *   ws         workspace of herald_workspace_size(HERALD_OP_REFINE) bytes, device

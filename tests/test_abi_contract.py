@@ -94,7 +94,6 @@ def test_vsel_ld(lib):
     (dict(topk=0), H.HERALD_ERR_INVALID_ARG),
     (dict(C=0, topk=0), H.HERALD_ERR_INVALID_ARG),
     (dict(C=5000, topk=10), H.HERALD_ERR_INVALID_ARG),        # C > L_0 = 4096
-    (dict(C=20000, topk=10, seq_start=[0, 30000]), H.HERALD_ERR_UNSUPPORTED),  # C > 16384
     (dict(dtype=7), H.HERALD_ERR_INVALID_ARG),
     (dict(seq_start=[1, 5000]), H.HERALD_ERR_INVALID_ARG),    # seq_start[0] != 0
     (dict(seq_start=[0, 5000, 4000]), H.HERALD_ERR_INVALID_ARG),  # negative length
@@ -108,6 +107,18 @@ def test_invalid_problem(lib, kw, status):
     assert status_of(H.herald_refine_topk, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_block_attn, p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, None, 0, 0, None) == status
+
+
+def test_candidate_limit_is_the_selections_only(lib):
+    """C > 16384 is refused by the merged-query selection (its emission keeps C in LDS) and
+    accepted by the other calls: refine over a whole sequence, attention over the whole cache."""
+    p = prob(C=30000, topk=30000, seq_start=[0, 30000, 61000])
+    assert status_of(H.herald_workspace_size, p, H.HERALD_OP_SELECT) == H.HERALD_ERR_UNSUPPORTED
+    assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == H.HERALD_ERR_UNSUPPORTED
+    assert H.herald_workspace_size(p, H.HERALD_OP_REFINE) > 0
+    assert H.herald_workspace_size(p, H.HERALD_OP_ATTN) > 0
+    assert H.herald_workspace_size(p, H.HERALD_OP_GATHER_HOST) > 0
+    assert H.herald_attn_splits(p) > 1
 
 
 def test_negative_nseq_and_reserved(lib):
