@@ -223,14 +223,16 @@ herald_status herald_workspace_size(const herald_problem* p, int op, size_t* byt
 
 int64_t herald_vsel_ld(int32_t topk) { return topk < 1 ? 0 : vsel_ld(topk); }
 
-herald_status herald_select_merged(const herald_problem* p, const void* q_merge, const void* k_cache,
+// Stage one with the query fed to the scan given as [nseq][nq][Hq][d]: the mean of
+// nq rows per head (the block's B queries, or one given query when nq = 1).
+static herald_status select_common(const herald_problem* p, const void* q, int nq, const void* k_cache,
                                    int32_t* cand_idx, float* cand_score, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const char* qname) {
   Shape s;
   HERALD_TRY(make_shape(p, &s));
   HERALD_TRY(check_select_shape(s));
   if (s.nseq == 0) return ok();
-  HERALD_TRY(check_ptr(q_merge, "q_merge"));
+  HERALD_TRY(check_ptr(q, qname));
   HERALD_TRY(check_ptr(k_cache, "k_cache"));
   HERALD_TRY(check_ptr(cand_idx, "cand_idx"));
   HERALD_TRY(check_ptr(cand_score, "cand_score", true));
@@ -238,7 +240,9 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
   carve_select(s, nullptr, &need);
   HERALD_TRY(check_ws(ws, ws_bytes, need));
   const SelectWs w = carve_select(s, ws, &need);
-  HERALD_HIP(launch_merge(s, q_merge, w, stream));
+  Shape sq = s;
+  sq.B = nq;
+  HERALD_HIP(launch_merge(sq, q, w, stream));
   HERALD_LAUNCH(0, stream, launch_scan(s, k_cache, w, stream));
   HERALD_LAUNCH(1, stream, launch_score_hist(s, w, stream));
   if (topc_in_lds(s)) {
@@ -249,6 +253,19 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
     HERALD_LAUNCH(3, stream, launch_emit_candidates(s, w, cand_idx, cand_score, stream));
   }
   return ok();
+}
+
+herald_status herald_select_merged(const herald_problem* p, const void* q_merge, const void* k_cache,
+                                   int32_t* cand_idx, float* cand_score, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!p) return fail(HERALD_ERR_INVALID_ARG, "problem is NULL");
+  return select_common(p, q_merge, p->block_size, k_cache, cand_idx, cand_score, ws, ws_bytes, stream, "q_merge");
+}
+
+herald_status herald_select_query(const herald_problem* p, const void* q_sel, const void* k_cache,
+                                  int32_t* cand_idx, float* cand_score, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return select_common(p, q_sel, 1, k_cache, cand_idx, cand_score, ws, ws_bytes, stream, "q_sel");
 }
 
 herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, const void* k_cache,

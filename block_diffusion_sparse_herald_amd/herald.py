@@ -37,7 +37,7 @@ KERNEL_IDS = {
 }
 
 EXPORTED = [
-    "herald_workspace_size", "herald_vsel_ld", "herald_select_merged", "herald_refine_topk",
+    "herald_workspace_size", "herald_vsel_ld", "herald_select_merged", "herald_select_query", "herald_refine_topk",
     "herald_gather_kv", "herald_block_attn", "herald_last_error", "herald_set_kernel_events",
     "herald_attn_splits",
 ]
@@ -84,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "herald_workspace_size": ([P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "herald_vsel_ld": ([ctypes.c_int32], ctypes.c_int64),
         "herald_select_merged": ([P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "herald_select_query": ([P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "herald_refine_topk": ([P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "herald_gather_kv": ([P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp],
                              ctypes.c_int),
@@ -182,6 +183,13 @@ def herald_select_merged(problem: Problem, q_merge, k_cache, cand_idx, cand_scor
     _check(load().herald_select_merged(problem.ref, _ptr(q_merge), _ptr(k_cache), _ptr(cand_idx), _ptr(cand_score),
                                        _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)),
            "herald_select_merged")
+
+
+def herald_select_query(problem: Problem, q_sel, k_cache, cand_idx, cand_score, ws, ws_bytes=None,
+                        stream=None) -> None:
+    _check(load().herald_select_query(problem.ref, _ptr(q_sel), _ptr(k_cache), _ptr(cand_idx), _ptr(cand_score),
+                                      _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)),
+           "herald_select_query")
 
 
 def herald_refine_topk(problem: Problem, q_refine, k_cache, cand_idx, topk_idx, topk_score, ws, ws_bytes=None,

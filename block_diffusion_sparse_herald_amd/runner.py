@@ -85,6 +85,11 @@ class BlockRunner:
         H.herald_select_merged(self.problem, q_merge, k_cache, self.cand, self.cand_score, self.ws["select"],
                                stream=stream)
 
+    def select_query(self, q_sel, k_cache, stream=None):
+        """Stage one from one query per head (q_sel [nseq][Hq][d]) instead of the block mean."""
+        H.herald_select_query(self.problem, q_sel, k_cache, self.cand, self.cand_score, self.ws["select"],
+                              stream=stream)
+
     def refine(self, q_refine, k_cache, cand=None, stream=None):
         H.herald_refine_topk(self.problem, q_refine, k_cache, self.cand if cand is None else cand, self.sel,
                              self.sel_score, self.ws["refine"], stream=stream)

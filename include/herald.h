@@ -121,6 +121,19 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
                                    hipStream_t stream);
 
 /*
+ * Stage one from one given query per head instead of the block mean: the same scan,
+ * scores and top-C as herald_select_merged, with q_sel taking the place of the merged
+ * query (HERALD abstract on the mlsift listing: the selection cost is cut by searching
+ * with a single [MASK] query; MAGE abstract: the All-[MASK] step's attention predicts
+ * the important entries). Every other argument, the workspace and the errors are those
+ * of herald_select_merged.
+ *   q_sel      [nseq][Hq][d]      device, read
+ */
+herald_status herald_select_query(const herald_problem* p, const void* q_sel, const void* k_cache,
+                                  int32_t* cand_idx, float* cand_score, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
  * Stage two: refine the candidates with the B real queries into the final subset
  * (HERALD v3 abstract: the GPU refines the candidates into the final top-K subset
  * with the block's real queries).

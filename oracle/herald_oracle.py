@@ -51,6 +51,7 @@ __all__ = [
     "group_scores",
     "top_k_ascending",
     "select_merged",
+    "select_query",
     "refine_scores",
     "refine_topk",
     "gather_kv",
@@ -147,6 +148,19 @@ def select_merged(q_merge: np.ndarray, k_cache: np.ndarray, C: int, scale: float
     """
     Hkv = k_cache.shape[1]
     S = group_scores(scan_logits(merge_queries(q_merge), k_cache, scale), Hkv)
+    cand = np.stack([top_k_ascending(S[g], C) for g in range(Hkv)])
+    return cand, S
+
+
+def select_query(q_sel: np.ndarray, k_cache: np.ndarray, C: int, scale: float):
+    """Stage one searched with one given query per head ([HERALD-v1]: a single [MASK]
+    query cuts the selection cost) instead of the block mean.
+
+    q_sel: [Hq][d]; k_cache: [L][Hkv][d]. The scan, scores and top-C are those of
+    select_merged with q_sel as the merged query. Returns (cand [Hkv][C], S [Hkv][L]).
+    """
+    Hkv = k_cache.shape[1]
+    S = group_scores(scan_logits(np.asarray(q_sel, dtype=np.float64), k_cache, scale), Hkv)
     cand = np.stack([top_k_ascending(S[g], C) for g in range(Hkv)])
     return cand, S
 

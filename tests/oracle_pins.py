@@ -136,6 +136,21 @@ def pin_scores_match_library_attention(orc):
     np.testing.assert_allclose(S, want, rtol=0, atol=1e-12)
 
 
+def pin_select_query_library_attention(orc):
+    """Single-query selection: scores = sum over the group of torch SDPA weights of the
+    given query itself (no merge), and the candidates are their top-C by argsort."""
+    Hq, Hkv, d, L, C = 6, 3, 16, 70, 9
+    r = _rng(21)
+    q, k = r.standard_normal((Hq, d)), r.standard_normal((L, Hkv, d))
+    G = Hq // Hkv
+    w = _sdpa_weights(q[:, None, :], np.ascontiguousarray(k.transpose(1, 0, 2)))[:, 0, :]
+    want = np.stack([w[g * G:(g + 1) * G].sum(axis=0) for g in range(Hkv)])
+    cand, S = orc.select_query(q, k, C, orc.default_scale(d))
+    np.testing.assert_allclose(S, want, rtol=0, atol=1e-12)
+    for g in range(Hkv):
+        assert cand[g].tolist() == np.sort(np.argsort(-want[g], kind="stable")[:C]).tolist()
+
+
 def pin_softmax_library(orc):
     """The oracle's softmax equals scipy's."""
     x = _rng(3).standard_normal((4, 33)) * 7

@@ -104,6 +104,7 @@ def test_invalid_problem(lib, kw, status):
     p = prob(**kw)
     assert status_of(H.herald_workspace_size, p, H.HERALD_OP_SELECT) == status
     assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
+    assert status_of(H.herald_select_query, p, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_refine_topk, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_block_attn, p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, None, 0, 0, None) == status
@@ -142,6 +143,9 @@ def test_pointer_checks(lib):
     assert status_of(H.herald_select_merged, p, None, FAKE, FAKE, None, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
     assert status_of(H.herald_select_merged, p, FAKE + 8, FAKE, FAKE, None, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
     assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, FAKE + 4, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_query, p, None, FAKE, FAKE, None, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_query, p, FAKE + 8, FAKE, FAKE, None, FAKE, ws, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_query, p, FAKE, FAKE, FAKE, None, FAKE, ws - 1, 0) == H.HERALD_ERR_WORKSPACE
     # workspace too small / missing
     assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, FAKE, ws - 1, 0) == H.HERALD_ERR_WORKSPACE
     assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, None, ws, 0) == H.HERALD_ERR_WORKSPACE

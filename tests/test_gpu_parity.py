@@ -315,3 +315,24 @@ def test_graph_replay_matches_eager():
         for a, b in zip(want, got):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("name", ["gqa32x8_L5000_b2", "ragged_g7_L1500-6000", "tiny_f32_L4096"])
+def test_select_query_parity(name):
+    """Selection from one given query per head (a [MASK]-query stand-in: the block's first query),
+    band test against the oracle's single-query selection."""
+    wl = SMALL[name]
+    batch = make_batch(wl)
+    dev = batch_to_device(batch)
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
+    q_sel = dev["q0"][:, 0].contiguous()  # [nseq][Hq][d]
+    r.select_query(q_sel, dev["k_cache"])
+    torch.cuda.synchronize()
+    cand, cand_score = to_np(r.cand).astype(np.int64), to_np(r.cand_score)
+    scale = orc.default_scale(wl.d)
+    for s in range(wl.nseq):
+        a, e = int(batch.seq_start[s]), int(batch.seq_start[s + 1])
+        _, S = orc.select_query(widen(batch.q0[s][0]), widen(batch.k_cache[a:e]), wl.C, scale)
+        for g in range(wl.Hkv):
+            band_check(cand[s, g], S[g], wl.C, what=f"{name} s{s} g{g} single-query candidates")
+            np.testing.assert_allclose(cand_score[s, g], S[g][cand[s, g]], rtol=1e-4, atol=1e-30)
