@@ -17,7 +17,8 @@ Sources (titles of the pages the method is taken from):
               Cooperative KV Cache Retrieval", abstract (catalyzex author page).
   [SparDA]    hyper.ai summary of arXiv 2606.04511 (SparDA), Method section,
               target-score equation S_tgt = sum over the G heads of a KV group of
-              softmax(Q_h K^T / tau).
+              softmax(Q_h K^T / tau); keys mean-pooled into overlapping compressed
+              representations for block-level relevance.
 
 Readings taken where the pages leave a step open (each is listed, with its
 reason, in the design notes of the repository):
@@ -29,7 +30,14 @@ reason, in the design notes of the repository):
     heads of its group, of a softmax taken over the C candidates only;
   * top-k ties go to the lower cache index; index sets are returned ascending;
   * block attention attends to the selected keys plus the B in-block keys of the
-    step, with no mask.
+    step, with no mask;
+  * compressed keys: block m of a sequence owns tokens [m*stride, (m+1)*stride)
+    (the last block may be short); its compressed key is the mean of the keys in
+    the window [m*stride, m*stride + ksize) cut at the sequence end (windows
+    overlap when ksize > stride); the block score is the group-summed softmax over
+    the blocks; the candidates are the top-C tokens of the score each token takes
+    from its block (whole blocks in score order, the boundary block from its lowest
+    token up).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
 invariants, special cases reduced to library routines, brute force on tiny
@@ -52,6 +60,8 @@ __all__ = [
     "top_k_ascending",
     "select_merged",
     "select_query",
+    "compress_keys",
+    "select_compressed",
     "refine_scores",
     "refine_topk",
     "gather_kv",
@@ -163,6 +173,39 @@ def select_query(q_sel: np.ndarray, k_cache: np.ndarray, C: int, scale: float):
     S = group_scores(scan_logits(np.asarray(q_sel, dtype=np.float64), k_cache, scale), Hkv)
     cand = np.stack([top_k_ascending(S[g], C) for g in range(Hkv)])
     return cand, S
+
+
+def compress_keys(k_cache: np.ndarray, ksize: int, stride: int) -> np.ndarray:
+    """Mean-pooled, overlapping compressed keys ([SparDA] Method: keys mean-pooled into
+    overlapping compressed representations), one per block of `stride` tokens.
+
+    k_cache: [L][Hkv][d]. Returns [ceil(L / stride)][Hkv][d]: row m is the mean of
+    k_cache[j] over j in [m*stride, min(m*stride + ksize, L)).
+    """
+    k = np.asarray(k_cache, dtype=np.float64)
+    L = k.shape[0]
+    M = -(-L // stride)
+    out = np.empty((M,) + k.shape[1:], dtype=np.float64)
+    for m in range(M):
+        a = m * stride
+        out[m] = k[a:min(a + ksize, L)].mean(axis=0)
+    return out
+
+
+def select_compressed(q_merge: np.ndarray, k_cache: np.ndarray, C: int, scale: float, ksize: int, stride: int):
+    """Block-granular stage one over compressed keys for one sequence.
+
+    q_merge: [B][Hq][d]; k_cache: [L][Hkv][d]. Block scores S_blk [Hkv][M] are the
+    group-summed softmax of the merged query over the M compressed keys; token j takes
+    the score of its block j // stride; the candidates are the top-C tokens of that
+    score, ties to the lower token. Returns (cand [Hkv][C], S_tok [Hkv][L], S_blk [Hkv][M]).
+    """
+    L, Hkv = k_cache.shape[0], k_cache.shape[1]
+    kc = compress_keys(k_cache, ksize, stride)
+    S_blk = group_scores(scan_logits(merge_queries(q_merge), kc, scale), Hkv)
+    S_tok = S_blk[:, np.arange(L) // stride]
+    cand = np.stack([top_k_ascending(S_tok[g], C) for g in range(Hkv)])
+    return cand, S_tok, S_blk
 
 
 def refine_scores(q_refine: np.ndarray, k_cache: np.ndarray, cand: np.ndarray, scale: float) -> np.ndarray:

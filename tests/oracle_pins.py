@@ -151,6 +151,51 @@ def pin_select_query_library_attention(orc):
         assert cand[g].tolist() == np.sort(np.argsort(-want[g], kind="stable")[:C]).tolist()
 
 
+def pin_compress_keys_library_pooling(orc):
+    """Compressed keys = torch avg_pool1d over the token axis (windows cut at the end:
+    ceil_mode with padding excluded from the count), for overlapping and disjoint windows."""
+    r = _rng(22)
+    for L, ksize, stride in [(50, 8, 4), (33, 5, 5), (17, 3, 2), (40, 1, 1), (9, 16, 4)]:
+        k = r.standard_normal((L, 2, 6))
+        x = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 2, 0)))  # [Hkv][d][L]
+        # pad on the right so every window that starts inside the sequence is produced,
+        # then average only over the real tokens it covers
+        M = -(-L // stride)
+        need = (M - 1) * stride + ksize
+        xp = F.pad(x, (0, max(0, need - L)))
+        ones = F.pad(torch.ones(1, 1, L, dtype=torch.float64), (0, max(0, need - L)))
+        sums = F.avg_pool1d(xp, ksize, stride) * ksize
+        cnt = F.avg_pool1d(ones, ksize, stride) * ksize
+        want = (sums / cnt)[..., :M].numpy().transpose(2, 0, 1)
+        np.testing.assert_allclose(orc.compress_keys(k, ksize, stride), want, rtol=0, atol=1e-12)
+
+
+def pin_select_compressed_reduces(orc):
+    """ksize = stride = 1 is the raw-key selection; with blocks, the candidates are whole
+    blocks taken in block-score order (SDPA weights of the merged query over the pooled
+    keys), the boundary block from its lowest tokens up."""
+    q, k, _ = _tiny(23, L=120, Hq=6, Hkv=2, d=8, B=3)
+    scale = orc.default_scale(8)
+    cand1, S1, _ = orc.select_compressed(q, k, 30, scale, 1, 1)
+    cand0, S0 = orc.select_merged(q, k, 30, scale)
+    assert cand1.tolist() == cand0.tolist()
+    np.testing.assert_allclose(S1, S0, rtol=0, atol=1e-15)
+    ksize, stride, C = 12, 8, 45
+    cand, S_tok, S_blk = orc.select_compressed(q, k, C, scale, ksize, stride)
+    kc = orc.compress_keys(k, ksize, stride)
+    G = 3
+    w = _sdpa_weights(q.mean(axis=0)[:, None, :], np.ascontiguousarray(kc.transpose(1, 0, 2)))[:, 0, :]
+    want_blk = np.stack([w[g * G:(g + 1) * G].sum(axis=0) for g in range(2)])
+    np.testing.assert_allclose(S_blk, want_blk, rtol=0, atol=1e-12)
+    L = k.shape[0]
+    for g in range(2):
+        order = np.argsort(-want_blk[g], kind="stable")
+        toks = []
+        for m in order:
+            toks += list(range(m * stride, min((m + 1) * stride, L)))
+        assert cand[g].tolist() == sorted(toks[:C]), g
+
+
 def pin_softmax_library(orc):
     """The oracle's softmax equals scipy's."""
     x = _rng(3).standard_normal((4, 33)) * 7

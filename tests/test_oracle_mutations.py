@@ -97,7 +97,31 @@ def _scan_transposed_group(q_merged, k_cache, scale):
     return np.stack([scale * (k[:, h % Hkv, :] @ q[h]) for h in range(Hq)])
 
 
-_ORIG = {n: getattr(orc, n) for n in ["refine_scores", "block_attention", "gather_kv", "scan_logits"]}
+def _compress_window_not_cut(k_cache, ksize, stride):
+    # divides by ksize even where the window runs past the end of the sequence
+    k = np.asarray(k_cache, np.float64)
+    L = k.shape[0]
+    M = -(-L // stride)
+    return np.stack([k[m * stride:min(m * stride + ksize, L)].sum(axis=0) / ksize for m in range(M)])
+
+
+def _compress_disjoint(k_cache, ksize, stride):
+    # ignores the overlap: windows of `stride` tokens
+    return _ORIG["compress_keys"](k_cache, stride, stride)
+
+
+def _select_compressed_block_index(q_merge, k_cache, C, scale, ksize, stride):
+    # maps token j to block j // ksize instead of j // stride
+    L, Hkv = k_cache.shape[0], k_cache.shape[1]
+    kc = orc.compress_keys(k_cache, ksize, stride)
+    S_blk = orc.group_scores(orc.scan_logits(orc.merge_queries(q_merge), kc, scale), Hkv)
+    S_tok = S_blk[:, np.minimum(np.arange(L) // ksize, S_blk.shape[1] - 1)]
+    cand = np.stack([orc.top_k_ascending(S_tok[g], C) for g in range(Hkv)])
+    return cand, S_tok, S_blk
+
+
+_ORIG = {n: getattr(orc, n) for n in ["refine_scores", "block_attention", "gather_kv", "scan_logits",
+                                       "compress_keys"]}
 
 MUTANTS = {
     "merge_sum_not_mean": ("merge_queries", lambda q: np.asarray(q, np.float64).sum(axis=0)),
@@ -118,6 +142,9 @@ MUTANTS = {
     "attention_drops_selected": ("block_attention", _attention_without_selected),
     "gather_wrong_head": ("gather_kv", _gather_head0),
     "gather_k_as_v": ("gather_kv", _gather_k_for_v),
+    "compress_window_not_cut": ("compress_keys", _compress_window_not_cut),
+    "compress_disjoint": ("compress_keys", _compress_disjoint),
+    "select_compressed_block_index": ("select_compressed", _select_compressed_block_index),
 }
 
 
