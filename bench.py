@@ -11,7 +11,10 @@ Prints one JSON line. `roofline` is for the kernel that takes the most time per
 step, timed with HIP events recorded by the library around that kernel on the
 stream it runs on. `cpu_baseline` times the CPU oracle on a bounded sample.
 
-`--method dense` and `--method mage` time the two exact layer baselines instead,
+`--method compressed` runs the HERALD path with the selection over compressed keys
+(herald_select_compressed; --ksize / --stride windows, the compressed cache built
+once per replica before timing, as a serving system maintains it when the cache
+grows). `--method dense` and `--method mage` time the two exact layer baselines instead,
 through the same calls: dense attention over the whole cache for the T steps
 (herald_block_attn with topk = L, the cache gathered once into the subset layout
 before timing), and MAGE-exact selection (herald_refine_topk with every key a
@@ -115,8 +118,10 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step directly instead of replaying graphs")
-    ap.add_argument("--method", choices=["herald", "dense", "mage"], default="herald",
-                    help="the HERALD path (default) or one of the exact layer baselines")
+    ap.add_argument("--method", choices=["herald", "compressed", "dense", "mage"], default="herald",
+                    help="the HERALD path (default), its compressed-key selection, or an exact layer baseline")
+    ap.add_argument("--ksize", type=int, default=32, help="compressed-key window (tokens), --method compressed")
+    ap.add_argument("--stride", type=int, default=16, help="compressed-key block (tokens), --method compressed")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the per-block path needs no "
@@ -150,7 +155,7 @@ def main(argv=None):
     qs, kbs, vbs = ([dev[n].offset(t) for t in range(wl.T)] for n in ("q_steps", "kb_steps", "vb_steps"))
     stream = hip.stream()
     if args.method != "herald":
-        return exact_baseline(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, stream)
+        return other_method(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, stream)
 
     call_of = {"scan": "select", "score_hist": "select", "radix": "select", "emit": "select",
                "refine_stats": "refine", "refine_scores": "refine", "refine_select": "refine",
@@ -316,9 +321,9 @@ def time_steps(hip, stream, step, steps: int, warmup: int, eager: bool) -> float
     return hip.elapsed_ms(a, b)
 
 
-def exact_baseline(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, stream):
-    """Dense attention or MAGE-exact selection, timed like the HERALD path, with the
-    HERALD path timed alongside in the same process for the ratio."""
+def other_method(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, stream):
+    """Compressed-key selection, dense attention or MAGE-exact selection, timed like the
+    HERALD path, with the HERALD path timed alongside in the same process for the ratio."""
     import numpy as np
 
     from block_diffusion_sparse_herald_amd import herald as H
@@ -326,15 +331,37 @@ def exact_baseline(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, strea
     from block_diffusion_sparse_herald_amd.runner import BlockRunner
 
     lengths = np.asarray(batch.lengths)
-    if (lengths != lengths[0]).any():
+    if args.method != "compressed" and (lengths != lengths[0]).any():
         print(f"--method {args.method} needs sequences of one length (the subset size is one number per call); "
               f"workload {wl.name} is ragged", file=sys.stderr)
         return 2
-    L = int(lengths[0])
+    L = int(lengths.max())
     alloc = lambda shape, dt, zero=False: DevArray(hip, shape, dt, zero)  # noqa: E731
-    iota = DevArray.from_host(hip, np.ascontiguousarray(
+    iota = None if args.method == "compressed" else DevArray.from_host(hip, np.ascontiguousarray(
         np.broadcast_to(np.arange(L, dtype=np.int32), (wl.nseq, wl.Hkv, L))))
-    if args.method == "dense":
+    if args.method == "compressed":
+        b = r
+        rows = H.herald_compressed_rows(b.problem, args.stride)
+        ws_c = DevArray(hip, (H.herald_workspace_size(b.problem, H.HERALD_OP_SELECT_COMPRESSED),), np.uint8)
+        comp_bytes = rows * wl.Hkv * wl.d * 4
+        comps = []
+        for _ in range(max(1, math.ceil(512 * 2**20 / comp_bytes))):
+            kc = DevArray(hip, (rows, wl.Hkv, wl.d), np.float32)
+            H.herald_compress_keys(b.problem, kv[len(comps) % len(kv)][0], args.ksize, args.stride, kc, stream=stream)
+            comps.append(kc)
+        hip.sync()
+
+        def step(i):
+            k, v = kv[i % len(kv)]
+            H.herald_select_compressed(b.problem, q0, comps[i % len(comps)], args.stride, b.cand, b.cand_score, ws_c,
+                                       stream=stream)
+            b.refine(q0, k, stream=stream)
+            b.gather(k, v, stream=stream)
+            for t in range(wl.T):
+                b.attn(qs[t], kbs[t], vbs[t], stream=stream)
+        what = (f"selection over compressed keys (window {args.ksize}, block {args.stride}: {rows} rows, "
+                f"{comp_bytes / 2**20:.1f} MiB fp32 per copy, {len(comps)} copies), refine, gather, {wl.T} steps")
+    elif args.method == "dense":
         b = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, L, L, wl.dtype, alloc=alloc,
                         seq_start_dev=seq_dev)
         # the whole cache in the subset layout, once; copies rotate like the cache replicas
@@ -382,7 +409,9 @@ def exact_baseline(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, strea
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "nseq": wl.nseq, "L": L, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.d,
-                   "B": wl.B, "topk": L if args.method == "dense" else wl.topk, "C": L, "T": wl.T},
+                   "B": wl.B, "topk": L if args.method == "dense" else wl.topk,
+                   "C": wl.C if args.method == "compressed" else L, "T": wl.T,
+                   **({"ksize": args.ksize, "stride": args.stride} if args.method == "compressed" else {})},
         "tokens_per_s": round(value * wl.B, 1), "launch": "eager" if args.eager else "hip_graph_per_step",
         "what": what, "herald_value": round(herald_value, 2), "vs_herald": round(value / herald_value, 4),
     }

@@ -24,7 +24,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-unused-command-line-argument",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
-SOURCES = ["select.hip", "refine.hip", "gather.hip", "attn.hip", "abi.cpp"]
+SOURCES = ["select.hip", "compress.hip", "refine.hip", "gather.hip", "attn.hip", "abi.cpp"]
 
 
 def _hipcc() -> str:

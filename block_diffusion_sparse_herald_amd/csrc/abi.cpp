@@ -170,6 +170,59 @@ SelectWs carve_select(const Shape& s, void* ws, size_t* bytes) {
   return w;
 }
 
+// Compressed selection: the token-level buffers of the top-C (merged query, scores,
+// histograms, bitmaps) and the compressed scan's own (logits, pairs, block scores,
+// a scratch histogram, row offsets), for compressed sequences of ceil(L_s / stride) rows.
+struct CompressedWs {
+  SelectWs tok;    // qbar, scores [Hkv][total], hist, bits
+  SelectWs blk;    // qbar (shared), logits, partials, scores = block scores [Hkv][ctotal], hist (scratch)
+  int64_t* coff;   // [nseq + 1] compressed row offsets
+  int64_t ctotal;  // compressed rows of the batch
+  int64_t cmax;    // compressed rows of the longest sequence
+};
+
+int64_t compressed_total(const herald_problem* p, int stride, int64_t* cmax) {
+  int64_t t = 0, mx = 0;
+  for (int i = 0; i < p->nseq; ++i) {
+    const int64_t m = (p->seq_start_host[i + 1] - p->seq_start_host[i] + stride - 1) / stride;
+    t += m;
+    mx = std::max(mx, m);
+  }
+  if (cmax) *cmax = mx;
+  return t;
+}
+
+CompressedWs carve_compressed(const herald_problem* p, const Shape& s, int stride, void* ws, size_t* bytes) {
+  Carver c{static_cast<char*>(ws)};
+  CompressedWs w;
+  w.ctotal = compressed_total(p, stride, &w.cmax);
+  const int GP = s.G <= 4 ? 4 : 8;
+  w.tok.tpc = w.blk.tpc = kScanTok;
+  w.tok.nchunk = 0;
+  w.blk.nchunk = (int)((w.cmax + kScanTok - 1) / kScanTok);
+  w.tok.nwords = w.blk.nwords = (int)((s.max_len + 63) / 64);
+  w.tok.qbar = w.blk.qbar = c.take<float>((size_t)s.nseq * s.Hq * s.D);
+  w.tok.logits = nullptr;
+  w.tok.partials = nullptr;
+  w.tok.scores = c.take<float>((size_t)s.Hkv * s.total);
+  w.tok.hist = c.take<uint32_t>((size_t)s.nseq * s.Hkv * 3 * kRadixBins);
+  w.tok.bits = c.take<uint64_t>((size_t)s.nseq * s.Hkv * 2 * w.tok.nwords);
+  w.blk.logits = c.take<float>((size_t)s.Hkv * w.ctotal * GP);
+  w.blk.partials = c.take<float2>((size_t)s.nseq * s.Hq * std::max(w.blk.nchunk, 1));
+  w.blk.scores = c.take<float>((size_t)s.Hkv * w.ctotal);
+  w.blk.hist = c.take<uint32_t>((size_t)s.nseq * s.Hkv * 3 * kRadixBins);
+  w.blk.bits = nullptr;
+  w.coff = c.take<int64_t>((size_t)s.nseq + 1);
+  *bytes = c.off;
+  return w;
+}
+
+herald_status check_compression(int ksize, int stride) {
+  if (stride < 2 || stride > 65536) return fail(HERALD_ERR_INVALID_ARG, "stride = %d outside [2, 65536]", stride);
+  if (ksize < 1 || ksize > 65536) return fail(HERALD_ERR_INVALID_ARG, "ksize = %d outside [1, 65536]", ksize);
+  return HERALD_OK;
+}
+
 RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
   Carver c{static_cast<char*>(ws)};
   RefineWs w;
@@ -213,6 +266,10 @@ herald_status herald_workspace_size(const herald_problem* p, int op, size_t* byt
       break;
     case HERALD_OP_REFINE: carve_refine(s, nullptr, &n); break;
     case HERALD_OP_ATTN: n = attn_ws_bytes(s); break;
+    case HERALD_OP_SELECT_COMPRESSED:
+      HERALD_TRY(check_select_shape(s));
+      carve_compressed(p, s, 2, nullptr, &n);  // stride 2 has the most compressed rows
+      break;
     case HERALD_OP_GATHER_HOST: n = gather_host_bytes(s); break;
     default: return fail(HERALD_ERR_INVALID_ARG, "unknown op %d", op);
   }
@@ -266,6 +323,61 @@ herald_status herald_select_query(const herald_problem* p, const void* q_sel, co
                                   int32_t* cand_idx, float* cand_score, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
   return select_common(p, q_sel, 1, k_cache, cand_idx, cand_score, ws, ws_bytes, stream, "q_sel");
+}
+
+int64_t herald_compressed_rows(const herald_problem* p, int32_t stride) {
+  Shape s;
+  if (make_shape(p, &s) != HERALD_OK || check_compression(1, stride) != HERALD_OK) return -1;
+  return compressed_total(p, stride, nullptr);
+}
+
+herald_status herald_compress_keys(const herald_problem* p, const void* k_cache, int32_t ksize, int32_t stride,
+                                   float* k_comp, hipStream_t stream) {
+  Shape s;
+  HERALD_TRY(make_shape(p, &s));
+  HERALD_TRY(check_compression(ksize, stride));
+  if (s.nseq == 0) return ok();
+  HERALD_TRY(check_ptr(k_cache, "k_cache"));
+  HERALD_TRY(check_ptr(k_comp, "k_comp"));
+  HERALD_HIP(launch_compress(s, k_cache, ksize, stride, k_comp, stream));
+  return ok();
+}
+
+herald_status herald_select_compressed(const herald_problem* p, const void* q_merge, const float* k_comp,
+                                       int32_t stride, int32_t* cand_idx, float* cand_score, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  HERALD_TRY(make_shape(p, &s));
+  HERALD_TRY(check_select_shape(s));
+  HERALD_TRY(check_compression(1, stride));
+  if (s.nseq == 0) return ok();
+  HERALD_TRY(check_ptr(q_merge, "q_merge"));
+  HERALD_TRY(check_ptr(k_comp, "k_comp"));
+  HERALD_TRY(check_ptr(cand_idx, "cand_idx"));
+  HERALD_TRY(check_ptr(cand_score, "cand_score", true));
+  size_t need;
+  carve_compressed(p, s, 2, nullptr, &need);
+  HERALD_TRY(check_ws(ws, ws_bytes, need));
+  const CompressedWs w = carve_compressed(p, s, stride, ws, &need);
+  // the compressed cache as a batch of its own: fp32 rows, offsets computed on the device
+  Shape sc = s;
+  sc.bf16 = 0;
+  sc.seq_start = w.coff;
+  sc.total = w.ctotal;
+  sc.max_len = w.cmax;
+  HERALD_HIP(launch_merge(s, q_merge, w.tok, stream));  // merged query; zeroes the token histograms
+  HERALD_HIP(launch_coffsets(s, stride, w.coff, stream));
+  HERALD_LAUNCH(0, stream, launch_scan(sc, k_comp, w.blk, stream));
+  HERALD_LAUNCH(1, stream, launch_score_hist(sc, w.blk, stream));  // block scores (its histogram is not used)
+  HERALD_LAUNCH(1, stream, launch_expand_hist(s, w.blk.scores, w.coff, w.ctotal, stride, w.tok, stream));
+  if (topc_in_lds(s)) {
+    HERALD_LAUNCH(3, stream, launch_topc_lds(s, w.tok, cand_idx, cand_score, stream));
+  } else {
+    HERALD_LAUNCH(2, stream, launch_radix_pass(s, w.tok, 2, stream));
+    HERALD_LAUNCH(2, stream, launch_radix_pass(s, w.tok, 3, stream));
+    HERALD_LAUNCH(3, stream, launch_emit_candidates(s, w.tok, cand_idx, cand_score, stream));
+  }
+  return ok();
 }
 
 herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, const void* k_cache,

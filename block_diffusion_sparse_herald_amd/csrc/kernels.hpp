@@ -78,6 +78,11 @@ hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st)
 hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipStream_t st);
 hipError_t launch_emit_candidates(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score,
                                   hipStream_t st);
+// compressed keys (compress.hip)
+hipError_t launch_compress(const Shape& s, const void* k, int ksize, int stride, float* k_comp, hipStream_t st);
+hipError_t launch_coffsets(const Shape& s, int stride, int64_t* coff, hipStream_t st);
+hipError_t launch_expand_hist(const Shape& s, const float* s_blk, const int64_t* coff, int64_t ctotal, int stride,
+                              const SelectWs& ws, hipStream_t st);
 bool topc_in_lds(const Shape& s);
 hipError_t launch_topc_lds(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score, hipStream_t st);
 // refine

@@ -30,6 +30,7 @@ HERALD_OP_SELECT = 0
 HERALD_OP_REFINE = 1
 HERALD_OP_ATTN = 2
 HERALD_OP_GATHER_HOST = 3
+HERALD_OP_SELECT_COMPRESSED = 4
 
 KERNEL_IDS = {
     "scan": 0, "score_hist": 1, "radix": 2, "emit": 3, "refine_stats": 4, "refine_scores": 5,
@@ -39,7 +40,7 @@ KERNEL_IDS = {
 EXPORTED = [
     "herald_workspace_size", "herald_vsel_ld", "herald_select_merged", "herald_select_query", "herald_refine_topk",
     "herald_gather_kv", "herald_block_attn", "herald_last_error", "herald_set_kernel_events",
-    "herald_attn_splits",
+    "herald_attn_splits", "herald_compressed_rows", "herald_compress_keys", "herald_select_compressed",
 ]
 
 
@@ -85,6 +86,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "herald_vsel_ld": ([ctypes.c_int32], ctypes.c_int64),
         "herald_select_merged": ([P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "herald_select_query": ([P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "herald_compressed_rows": ([P, ctypes.c_int32], ctypes.c_int64),
+        "herald_compress_keys": ([P, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp], ctypes.c_int),
+        "herald_select_compressed": ([P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "herald_refine_topk": ([P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "herald_gather_kv": ([P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp],
                              ctypes.c_int),
@@ -190,6 +194,23 @@ def herald_select_query(problem: Problem, q_sel, k_cache, cand_idx, cand_score, 
     _check(load().herald_select_query(problem.ref, _ptr(q_sel), _ptr(k_cache), _ptr(cand_idx), _ptr(cand_score),
                                       _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)),
            "herald_select_query")
+
+
+def herald_compressed_rows(problem: Problem, stride: int) -> int:
+    return int(load().herald_compressed_rows(problem.ref, stride))
+
+
+def herald_compress_keys(problem: Problem, k_cache, ksize: int, stride: int, k_comp, stream=None) -> None:
+    _check(load().herald_compress_keys(problem.ref, _ptr(k_cache), ksize, stride, _ptr(k_comp), _stream(stream)),
+           "herald_compress_keys")
+
+
+def herald_select_compressed(problem: Problem, q_merge, k_comp, stride: int, cand_idx, cand_score, ws,
+                             ws_bytes=None, stream=None) -> None:
+    _check(load().herald_select_compressed(problem.ref, _ptr(q_merge), _ptr(k_comp), stride, _ptr(cand_idx),
+                                           _ptr(cand_score), _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes,
+                                           _stream(stream)),
+           "herald_select_compressed")
 
 
 def herald_refine_topk(problem: Problem, q_refine, k_cache, cand_idx, topk_idx, topk_score, ws, ws_bytes=None,

@@ -68,7 +68,8 @@ typedef enum herald_op {
   HERALD_OP_SELECT = 0,      /* herald_select_merged                                  */
   HERALD_OP_REFINE = 1,      /* herald_refine_topk                                    */
   HERALD_OP_ATTN = 2,        /* herald_block_attn                                     */
-  HERALD_OP_GATHER_HOST = 3  /* herald_gather_kv with src_is_host = 1                 */
+  HERALD_OP_GATHER_HOST = 3, /* herald_gather_kv with src_is_host = 1                 */
+  HERALD_OP_SELECT_COMPRESSED = 4 /* herald_select_compressed, any stride >= 2       */
 } herald_op;
 
 /*
@@ -132,6 +133,34 @@ herald_status herald_select_merged(const herald_problem* p, const void* q_merge,
 herald_status herald_select_query(const herald_problem* p, const void* q_sel, const void* k_cache,
                                   int32_t* cand_idx, float* cand_score, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/*
+ * Compressed keys (SparDA, hyper.ai summary, Method section: block-level relevance
+ * against keys mean-pooled into overlapping compressed representations). Block m of
+ * sequence s owns tokens [m*stride, (m+1)*stride) (the last block may be short); its
+ * compressed key is the mean of the keys in [m*stride, m*stride + ksize), cut at the
+ * end of the sequence (ksize > stride overlaps the windows).
+ *   herald_compressed_rows: rows of the compressed cache, sum over s of
+ *     ceil(L_s / stride); -1 for an invalid problem or stride.
+ *   herald_compress_keys: k_comp [rows][Hkv][d] fp32, device, written (sequences
+ *     concatenated in order); k_cache as for the other calls. 2 <= stride <= 65536,
+ *     1 <= ksize <= 65536 (HERALD_ERR_INVALID_ARG otherwise). Reads each key
+ *     ceil(ksize / stride) times; meant to be run when the cache grows, not per block.
+ *   herald_select_compressed: stage one over the compressed cache: block score =
+ *     sum over the group's heads of the merged query's softmax over the blocks of the
+ *     sequence; every token takes its block's score, and the candidates are the exact
+ *     top-C tokens of that (ties to the lower index: whole blocks in score order, the
+ *     boundary block from its lowest token up). Outputs as herald_select_merged;
+ *     workspace herald_workspace_size(HERALD_OP_SELECT_COMPRESSED) (valid for every
+ *     stride >= 2). The scan reads the compressed cache instead of the token cache:
+ *     4 * d bytes per block and KV head.
+ */
+int64_t herald_compressed_rows(const herald_problem* p, int32_t stride);
+herald_status herald_compress_keys(const herald_problem* p, const void* k_cache, int32_t ksize, int32_t stride,
+                                   float* k_comp, hipStream_t stream);
+herald_status herald_select_compressed(const herald_problem* p, const void* q_merge, const float* k_comp,
+                                       int32_t stride, int32_t* cand_idx, float* cand_score, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
 
 /*
  * Stage two: refine the candidates with the B real queries into the final subset
@@ -202,7 +231,9 @@ const char* herald_last_error(void);
  * radix digit, 2 second and third radix digits (sequences longer than 36864 tokens
  * only), 3 candidate emission (with the second and third digits for sequences up to
  * 36864 tokens), 4 refine statistics, 5 refine scores, 6 final top-K, 7 gather,
- * 8 block attention, 9 merge of the attention key ranges (split subsets only).
+ * 8 block attention, 9 merge of the attention key ranges (split subsets only). The
+ * single-query and compressed selections use ids 0-3 the same way (for the compressed
+ * one, 0 is the scan of the compressed cache and 1 the last of its two score kernels).
  * While set (non-NULL), every launch of that kernel on a call's stream is bracketed
  * by records of start and stop on the same stream (external event nodes when the
  * stream is being captured into a graph); the last launch wins; a kernel a call does

@@ -105,6 +105,9 @@ def test_invalid_problem(lib, kw, status):
     assert status_of(H.herald_workspace_size, p, H.HERALD_OP_SELECT) == status
     assert status_of(H.herald_select_merged, p, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_select_query, p, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
+    assert status_of(H.herald_select_compressed, p, FAKE, FAKE, 16, FAKE, None, FAKE, 1 << 40, 0) == status
+    assert status_of(H.herald_compress_keys, p, FAKE, 32, 16, FAKE, 0) == status
+    assert H.herald_compressed_rows(p, 16) == -1
     assert status_of(H.herald_refine_topk, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_block_attn, p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == status
     assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, None, 0, 0, None) == status
@@ -120,6 +123,23 @@ def test_candidate_limit_is_the_selections_only(lib):
     assert H.herald_workspace_size(p, H.HERALD_OP_ATTN) > 0
     assert H.herald_workspace_size(p, H.HERALD_OP_GATHER_HOST) > 0
     assert H.herald_attn_splits(p) > 1
+
+
+def test_compressed_keys_contract(lib):
+    p = prob()  # lengths 4096 and 4904
+    assert H.herald_compressed_rows(p, 16) == 256 + 307
+    assert H.herald_compressed_rows(p, 4096) == 1 + 2
+    assert H.herald_compressed_rows(p, 1) == -1
+    n = H.herald_workspace_size(p, H.HERALD_OP_SELECT_COMPRESSED)
+    assert n > 0
+    for stride, ksize in [(1, 8), (0, 8), (65537, 8), (16, 0), (16, 65537)]:
+        assert status_of(H.herald_compress_keys, p, FAKE, ksize, stride, FAKE, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_compressed, p, FAKE, FAKE, 1, FAKE, None, FAKE, n, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_compressed, p, FAKE, None, 16, FAKE, None, FAKE, n, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_select_compressed, p, FAKE, FAKE, 16, FAKE, None, FAKE, n - 1, 0) == H.HERALD_ERR_WORKSPACE
+    assert status_of(H.herald_compress_keys, p, None, 32, 16, FAKE, 0) == H.HERALD_ERR_INVALID_ARG
+    big = prob(C=20000, topk=10, seq_start=[0, 30000])
+    assert status_of(H.herald_workspace_size, big, H.HERALD_OP_SELECT_COMPRESSED) == H.HERALD_ERR_UNSUPPORTED
 
 
 def test_negative_nseq_and_reserved(lib):
