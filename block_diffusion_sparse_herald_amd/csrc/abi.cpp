@@ -417,9 +417,25 @@ herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const
   HERALD_TRY(check_ptr(topk_idx, "topk_idx"));
   HERALD_TRY(check_ptr(k_sel, "k_sel"));
   HERALD_TRY(check_ptr(v_sel, "v_sel"));
-  if (src_is_host != 0 && src_is_host != 1) return fail(HERALD_ERR_INVALID_ARG, "src_is_host must be 0 or 1");
-  if (!src_is_host) {
+  if (src_is_host < 0 || src_is_host > 2) return fail(HERALD_ERR_INVALID_ARG, "src_is_host must be 0, 1 or 2");
+  if (src_is_host == 0) {
     HERALD_LAUNCH(7, stream, launch_gather(s, k_src, v_src, topk_idx, k_sel, v_sel, stream));
+    if (done) HERALD_HIP(hipEventRecord(done, stream));
+    return ok();
+  }
+  if (src_is_host == 2) {
+    // the kernel reads the pinned pool directly: device addresses of the host rows
+    const void* src[2] = {k_src, v_src};
+    const void* dev[2];
+    for (int i = 0; i < 2; ++i) {
+      hipPointerAttribute_t a{};
+      if (hipPointerGetAttributes(&a, src[i]) != hipSuccess || a.type != hipMemoryTypeHost || !a.devicePointer) {
+        (void)hipGetLastError();
+        return fail(HERALD_ERR_INVALID_ARG, "%s is not pinned host memory (hipHostMalloc)", i ? "v_src" : "k_src");
+      }
+      dev[i] = a.devicePointer;
+    }
+    HERALD_LAUNCH(7, stream, launch_gather(s, dev[0], dev[1], topk_idx, k_sel, v_sel, stream));
     if (done) HERALD_HIP(hipEventRecord(done, stream));
     return ok();
   }

@@ -46,6 +46,9 @@ class Hip:
             "hipGetErrorString": [ctypes.c_int],
             "hipGetLastError": [],
             "hipGetDeviceCount": [ctypes.POINTER(ctypes.c_int)],
+            "hipHostMalloc": [ctypes.POINTER(_vp), ctypes.c_size_t, ctypes.c_uint],
+            "hipHostFree": [_vp],
+            "hipStreamWaitEvent": [_vp, _vp, ctypes.c_uint],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -85,6 +88,16 @@ class Hip:
 
     def copy(self, dst: int, src: int, nbytes: int) -> None:
         self.check(self.lib.hipMemcpy(dst, src, nbytes, _D2D), "hipMemcpy D2D")
+
+    def host_malloc(self, nbytes: int) -> int:
+        """Pinned host memory (hipHostMalloc, default flags: mapped into the device's address space)."""
+        p = _vp()
+        self.check(self.lib.hipHostMalloc(ctypes.byref(p), max(int(nbytes), 256), 0), "hipHostMalloc")
+        return p.value
+
+    def wait(self, stream: int, event: int) -> None:
+        """`stream` waits for the work recorded in `event`."""
+        self.check(self.lib.hipStreamWaitEvent(stream, event, 0), "hipStreamWaitEvent")
 
     # streams and events
     def stream(self) -> int:
@@ -137,6 +150,24 @@ class Hip:
 
     def launch(self, graph_exec: int, stream: int) -> None:
         self.check(self.lib.hipGraphLaunch(graph_exec, stream), "hipGraphLaunch")
+
+
+class HostArray:
+    """Pinned host memory with a shape and dtype, viewable as a numpy array."""
+
+    def __init__(self, hip: Hip, shape, dtype):
+        self.hip = hip
+        self.shape = tuple(int(x) for x in shape)
+        self.dtype = np.dtype(dtype)
+        self.nbytes = int(np.prod(self.shape, dtype=np.int64)) * self.dtype.itemsize
+        self.ptr = hip.host_malloc(self.nbytes)
+
+    def data_ptr(self) -> int:
+        return self.ptr
+
+    def numpy(self) -> np.ndarray:
+        buf = (ctypes.c_char * self.nbytes).from_address(self.ptr)
+        return np.frombuffer(buf, dtype=self.dtype).reshape(self.shape)
 
 
 class DevArray:

@@ -185,7 +185,7 @@ herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, 
  * abstract on the mlsift listing: only a small critical subset is fetched, once
  * per block).
  *   k_src, v_src [sumL][Hkv][d]   the full cache: device memory (src_is_host = 0) or
- *                                 pinned host memory from hipHostMalloc (src_is_host = 1)
+ *                                 pinned host memory from hipHostMalloc (src_is_host = 1, 2)
  *   topk_idx  [nseq][Hkv][topk]   device, read
  *   k_sel     [nseq][Hkv][topk][d]               device, written
  *   v_sel     [nseq][Hkv][d][herald_vsel_ld(topk)] device, written: V stored d-major
@@ -199,6 +199,13 @@ herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, 
  * host-to-device of the packed rows into ws (herald_workspace_size(
  * HERALD_OP_GATHER_HOST) bytes), lays them out into k_sel / v_sel with a kernel and
  * records `done` (required). The main stream waits on `done` before attention.
+ * Host-pool path read by the GPU (src_is_host = 2): the gather kernel itself reads the
+ * picked rows from the pinned host pool over PCIe (each row 16-byte loads of one
+ * contiguous row), with no host work and no synchronisation, so it can run on a side
+ * stream while the other stream computes, and be captured into a graph. k_src and
+ * v_src must be pinned host memory (HERALD_ERR_INVALID_ARG otherwise, checked with
+ * hipPointerGetAttributes); host_staging, host_idx and ws may be NULL; `done`, when
+ * not NULL, is recorded after the kernel.
  */
 herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const void* v_src,
                                int32_t src_is_host, const int32_t* topk_idx, void* k_sel, void* v_sel,

@@ -248,6 +248,19 @@ def test_host_pool_gather_matches_device_gather():
     torch.cuda.synchronize()
     assert torch.equal(k_sel.view(torch.int16), r.k_sel.view(torch.int16))
     assert torch.equal(v_sel.view(torch.int16), r.v_sel.view(torch.int16))
+    # the GPU reading the pinned pool itself (no staging, no host work), on the side stream
+    k_sel.zero_()
+    v_sel.fill_(7.0)
+    side.wait_stream(torch.cuda.current_stream())
+    H.herald_gather_kv(r.problem, kh, vh, 2, r.sel, k_sel, v_sel, None, None, None, stream=side, done=done)
+    torch.cuda.current_stream().wait_event(done)
+    torch.cuda.synchronize()
+    assert torch.equal(k_sel.view(torch.int16), r.k_sel.view(torch.int16))
+    assert torch.equal(v_sel.view(torch.int16), r.v_sel.view(torch.int16))
+    # device memory is refused on that path
+    with pytest.raises(H.HeraldError):
+        H.herald_gather_kv(r.problem, run.dev["k_cache"], run.dev["v_cache"], 2, r.sel, k_sel, v_sel, None, None,
+                           None, stream=side)
 
 
 def test_kernel_events_time_the_scan():
