@@ -323,11 +323,11 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
 // Merges the key ranges of one (sequence, KV head): 4 output dimensions per thread,
 // the ranges taken 8 at a time (loads first) with a running (max, sum).
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict__ o_part,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restrict__ o_part,
                                                           const float2* __restrict__ ml_part, AttnGeom a,
                                                           bf16* __restrict__ out) {
   constexpr int CH = 8;
-  const int idx = blockIdx.x * 64 + threadIdx.x;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
   const int R = a.B * a.G;
   const int per_unit = R * (D / 4);
   const int unit = idx / per_unit;
@@ -544,11 +544,11 @@ hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t 
   const bf16* o_part = static_cast<const bf16*>(ws);
   const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(bf16)));
   const int64_t n = (int64_t)a.nunits * a.B * a.G * (s.D / 4);
-  const dim3 grid((unsigned)((n + 63) / 64));
+  const dim3 grid((unsigned)((n + 255) / 256));
   if (s.D == 128)
-    klaunch(attn_combine_kernel<128>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
+    klaunch(attn_combine_kernel<128>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
   else
-    klaunch(attn_combine_kernel<64>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
+    klaunch(attn_combine_kernel<64>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
   return hipGetLastError();
 }
 
