@@ -22,10 +22,19 @@
 
 namespace herald {
 
+// First compressed row of sequence s: sum over t < s of ceil(L_t / stride), summed by
+// the 256 threads of the workgroup (each a strided part, then through LDS).
 __device__ __forceinline__ int64_t compressed_offset(const int64_t* __restrict__ seq_start, int s, int stride) {
+  __shared__ int64_t part[256];
   int64_t off = 0;
-  for (int t = 0; t < s; ++t) off += (seq_start[t + 1] - seq_start[t] + stride - 1) / stride;
-  return off;
+  for (int t = threadIdx.x; t < s; t += 256) off += (seq_start[t + 1] - seq_start[t] + stride - 1) / stride;
+  part[threadIdx.x] = off;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  return part[0];
 }
 
 // Four blocks per workgroup of one (sequence, KV head), 64 threads per block, each
@@ -38,6 +47,8 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ k, 
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
   const int64_t M = (L + stride - 1) / stride;
+  if ((int64_t)blockIdx.x * 4 >= M) return;  // whole workgroup past this sequence's blocks
+  const int64_t cbase = compressed_offset(seq_start, s, stride);
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
   const int e0 = (threadIdx.x & 63) * EPT;
@@ -51,7 +62,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ k, 
     for (int t = 0; t < EPT; ++t) acc[t] += to_f32(row[t]);
   }
   const float n = (float)(b - a);
-  float* out = k_comp + ((compressed_offset(seq_start, s, stride) + m) * Hkv + g) * D + e0;
+  float* out = k_comp + ((cbase + m) * Hkv + g) * D + e0;
 #pragma unroll
   for (int t = 0; t < EPT; ++t) out[t] = acc[t] / n;
 }
