@@ -173,10 +173,11 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
   // The query fragments (and in-block rows) are the only loads the compiler tracks.
-  // Waiting for them here, once, keeps it from placing that wait inside the loop,
-  // where (the direct-to-LDS transfers being invisible to it) it would be a full
-  // vmcnt(0) that also drains every block prefetched since.
-  wait_vm<0>();
+  // When blocks are refilled inside the loop, waiting for them here, once, keeps the
+  // compiler from placing that wait inside the loop, where (the direct-to-LDS transfers
+  // being invisible to it) it would be a full vmcnt(0) that also drains every block
+  // prefetched since. When every block is fetched up front it costs more than it saves.
+  if (nb > nst) wait_vm<0>();
 
   for (int j = 0; j < nb; j += 2) {
     // wait for this wave's loads of the subset blocks among j, j + 1
@@ -323,11 +324,11 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
 // Merges the key ranges of one (sequence, KV head): 4 output dimensions per thread,
 // the ranges taken 8 at a time (loads first) with a running (max, sum).
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restrict__ o_part,
+__global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict__ o_part,
                                                           const float2* __restrict__ ml_part, AttnGeom a,
                                                           bf16* __restrict__ out) {
   constexpr int CH = 8;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int idx = blockIdx.x * 64 + threadIdx.x;
   const int R = a.B * a.G;
   const int per_unit = R * (D / 4);
   const int unit = idx / per_unit;
@@ -481,7 +482,16 @@ AttnGeom attn_geom(const Shape& s) {
   a.nunits = s.nseq * s.Hkv;
   const int ntiles = (s.B * s.G + 15) / 16;
   const int nblk = (s.topk + kAttnKeyBlock - 1) / kAttnKeyBlock + 1;
+  // Four query tiles per workgroup; two when few (sequence, KV head) pairs leave the
+  // chip idle even with the keys split: twice the workgroups (each pulling the same
+  // keys for fewer rows), a larger target for the key split and ranges of 3 blocks.
   a.tpw = std::min(ntiles, 4);
+  int target = kAttnTargetWorkgroups, minrange = kAttnMaxStages;
+  if (a.nunits * ((ntiles + 3) / 4) * 5 < kAttnTargetWorkgroups) {
+    a.tpw = std::min(ntiles, 2);
+    target = kAttnTargetWorkgroupsFew;
+    minrange = 3;
+  }
   a.nrs = (ntiles + a.tpw - 1) / a.tpw;
   a.rpad = ntiles * 16;
   // A workgroup keeps at most kAttnMaxStages blocks in flight, so one pulling a long
@@ -489,8 +499,7 @@ AttnGeom attn_geom(const Shape& s) {
   // split into ranges of about kAttnMaxStages blocks, to spread them over enough
   // workgroups (the ranges are then merged by attn_combine_kernel).
   const int groups = a.nunits * a.nrs;
-  const int spread = std::min((kAttnTargetWorkgroups + groups - 1) / groups,
-                              (nblk + kAttnMaxStages - 1) / kAttnMaxStages);
+  const int spread = std::min((target + groups - 1) / groups, (nblk + minrange - 1) / minrange);
   const int nks = std::max((nblk + kAttnBlocksPerRange - 1) / kAttnBlocksPerRange, spread);
   a.bps = (nblk + nks - 1) / nks;
   a.nks = (nblk + a.bps - 1) / a.bps;
@@ -544,11 +553,11 @@ hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t 
   const bf16* o_part = static_cast<const bf16*>(ws);
   const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(bf16)));
   const int64_t n = (int64_t)a.nunits * a.B * a.G * (s.D / 4);
-  const dim3 grid((unsigned)((n + 255) / 256));
+  const dim3 grid((unsigned)((n + 63) / 64));
   if (s.D == 128)
-    klaunch(attn_combine_kernel<128>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
+    klaunch(attn_combine_kernel<128>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
   else
-    klaunch(attn_combine_kernel<64>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
+    klaunch(attn_combine_kernel<64>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
   return hipGetLastError();
 }
 

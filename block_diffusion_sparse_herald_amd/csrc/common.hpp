@@ -385,25 +385,30 @@ __device__ __forceinline__ void lds_emit(const uint32_t* u, int n, uint32_t thr,
     pos += wcnt[x][0] + take;
     tie += wcnt[x][1];
   }
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // set bits of m in the lanes below this one (v_mbcnt)
+  auto below = [](uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  };
   for (int it = 0; it < span; it += 64 * U) {
     uint32_t v[U];
+    int32_t ix[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int e = e0 + it + k * 64 + lane;
       v[k] = e < n ? u[e] : 0u;
+      ix[k] = idx ? (e < n ? idx[e] : 0) : e;  // all reads of the batch issued together
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int e = e0 + it + k * 64 + lane;
       const bool gt = e < n && v[k] > thr, eq = e < n && v[k] == thr;
       const uint64_t beq = __ballot(eq);
-      const uint32_t my_tie = tie + (uint32_t)__builtin_popcountll(beq & below);
+      const uint32_t my_tie = tie + below(beq);
       const bool take = gt || (eq && my_tie < ties_wanted);
       const uint64_t btake = __ballot(take);
       if (take) {
-        const uint32_t p = pos + (uint32_t)__builtin_popcountll(btake & below);
-        out[p] = idx ? idx[e] : e;
+        const uint32_t p = pos + below(btake);
+        out[p] = ix[k];
         if (outs) outs[p] = __uint_as_float(v[k]);
       }
       pos += (uint32_t)__builtin_popcountll(btake);

@@ -69,6 +69,7 @@ struct AttnGeom {
 };
 constexpr int kAttnBlocksPerRange = 32;
 constexpr int kAttnTargetWorkgroups = 96;
+constexpr int kAttnTargetWorkgroupsFew = 192;  // with two query tiles per workgroup
 constexpr int kAttnMaxStages = 4;
 
 // select
