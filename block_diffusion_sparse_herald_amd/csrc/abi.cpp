@@ -226,7 +226,8 @@ herald_status check_compression(int ksize, int stride) {
 RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
   Carver c{static_cast<char*>(ws)};
   RefineWs w;
-  w.ntile = (s.C + kRefineTile - 1) / kRefineTile;
+  const int tile = s.bf16 ? kRefineTile : kRefineTileF32;
+  w.ntile = (s.C + tile - 1) / tile;
   w.row_stats = c.take<float2>((size_t)s.nseq * s.Hkv * ((w.ntile + 1) & ~1) * s.B * s.G);
   w.rscore = c.take<float>((size_t)s.nseq * s.Hkv * s.C);
   *bytes = c.off;

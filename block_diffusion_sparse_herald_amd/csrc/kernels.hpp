@@ -20,8 +20,9 @@ constexpr int kScoreTok = 1024;
 constexpr int kRadixBins = 2048;
 // Longest sequence whose selection scores one workgroup keeps in LDS (144 KiB).
 constexpr int kTopcLdsMaxLen = 36864;
-// Candidates one refine workgroup covers (bf16 MFMA path).
-constexpr int kRefineTile = 128;
+// Candidates one refine workgroup covers (bf16 MFMA path: 64 per wave; fp32 path).
+constexpr int kRefineTile = 256;
+constexpr int kRefineTileF32 = 128;
 // Keys per attention block and the largest supported candidate count.
 constexpr int kAttnKeyBlock = 64;
 constexpr int kMaxCandidates = 16384;

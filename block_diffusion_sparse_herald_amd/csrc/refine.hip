@@ -13,11 +13,13 @@
 //   refine_scores_kernel  per row: normalisers from all tiles; per candidate: the
 //                         sum over rows, in a fixed order (each lane over its row's
 //                         tiles, then over the 16 lanes of a row with DPP shifts).
-// Each wave owns 64 candidates (four 16-candidate MFMA tiles). The candidate key
-// rows (gathered from the cache by index) and the group's B*G query rows are
-// streamed into LDS with coalesced direct-to-LDS loads; the key rows are the A
-// operand (read once into registers), the query rows the B operand
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// A workgroup covers kRefineTile candidates, each wave 64 of them (four 16-candidate
+// MFMA tiles). The candidate key rows, gathered from the cache by index, go straight
+// into registers as the A operand; the group's B*G query rows, shared by the waves,
+// are streamed into LDS with direct-to-LDS loads and read as the B operand
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulate). Only the query rows take LDS (32 KiB
+// at B*G = 128, d = 128), so several workgroups share a compute unit and one's loads
+// overlap another's products.
 // refine_select_kernel then takes, per (sequence, KV head), the exact top-K of R
 // in LDS (three radix digits on the fp32 bit pattern, R >= 0), ties to the lower
 // cache index, ascending output.
@@ -51,16 +53,17 @@ __device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[4][D / 32], 
 }
 
 // Shared prologue of both refine kernels, in two parts. refine_issue_rows: the
-// group's query rows and this workgroup's kRefineTile candidate key rows go to LDS
-// with coalesced direct-to-LDS loads (rows past R re-read query row 0, candidates
-// past C re-read the last one; both are masked later). refine_key_frags: once the
-// loads have landed, each wave reads the key fragments of its 64 candidates into
-// registers.
+// group's query rows go to LDS with coalesced direct-to-LDS loads (rows past R re-read
+// query row 0, masked later), and each wave loads the MFMA fragments of its 64
+// candidate key rows straight into registers, gathered from the cache by index
+// (candidates past C re-read the last one, masked later); every lane reads 16 bytes of
+// a row per load, a load covers 64 contiguous bytes of 16 rows. refine_wait_rows:
+// once both have landed, the workgroup may read the query rows.
 template <int D>
 __device__ __forceinline__ void refine_issue_rows(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                   const int32_t* __restrict__ cand, int64_t j0, int s, int g, int B,
                                                   int Hq, int Hkv, int G, int C, int R, int RT, int ctile, bf16* qs,
-                                                  bf16* kls) {
+                                                  uint4 (&a)[4][D / 32]) {
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int RPI = 64 / CPR; // rows per load instruction
   constexpr int NW = kRefineTile / 64;
@@ -74,30 +77,23 @@ __device__ __forceinline__ void refine_issue_rows(const bf16* __restrict__ q, co
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)(qs + r0 * D), 16, 0, 0);
   }
-  // candidate key rows: wave w loads (and later uses) rows w*64 .. w*64+63 of the tile
+  // candidate key fragments of wave w: rows w*64 + mt*16 + (lane & 15) of the tile
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-#pragma unroll
-  for (int u = 0; u < 64 / RPI; ++u) {
-    const int i = w * 64 + u * RPI + rr;
-    const int c = min(ctile * kRefineTile + i, C - 1);
-    const bf16* src = k + ((j0 + cd[c]) * Hkv + g) * D + (p ^ refine_swz<D>(i)) * 8;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(kls + (w * 64 + u * RPI) * D), 16, 0, 0);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void refine_key_frags(const bf16* kls, uint4 (&a)[4][D / 32]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  const bf16* rows[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const int i = w * 64 + mt * 16 + (lane & 15);
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      a[mt][ks] = *reinterpret_cast<const uint4*>(kls + i * D + ((ks * 4 + (lane >> 4)) ^ refine_swz<D>(i)) * 8);
+    const int c = min(ctile * kRefineTile + w * 64 + mt * 16 + (lane & 15), C - 1);
+    rows[mt] = k + ((j0 + cd[c]) * Hkv + g) * D + (lane >> 4) * 8;
   }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) a[mt][ks] = *reinterpret_cast<const uint4*>(rows[mt] + ks * 32);
+}
+
+__device__ __forceinline__ void refine_wait_rows() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 template <int D>
@@ -112,13 +108,12 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G, RT = (R + 15) / 16;
   bf16* qs = reinterpret_cast<bf16*>(smem);                     // [RT*16][D]
-  bf16* kls = qs + RT * 16 * D;                                 // [kRefineTile][D]
-  float2* wstat = reinterpret_cast<float2*>(kls + kRefineTile * D);  // [NW][RT*16]
+  float2* wstat = reinterpret_cast<float2*>(qs + RT * 16 * D);  // [NW][RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cbase = tile * kRefineTile + w * 64;
   uint4 a[4][D / 32];
-  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, kls);
-  refine_key_frags<D>(kls, a);
+  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
+  refine_wait_rows();
 
   for (int rt = 0; rt < RT; ++rt) {
     f32x4_t acc[4];
@@ -167,22 +162,22 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G, RT = (R + 15) / 16;
   bf16* qs = reinterpret_cast<bf16*>(smem);               // [RT*16][D]
-  bf16* kls = qs + RT * 16 * D;                           // [kRefineTile][D]
-  float* rowM = reinterpret_cast<float*>(kls + kRefineTile * D);  // [RT*16]
-  float* rowIZ = rowM + RT * 16;                                 // [RT*16]
+  float* rowM = reinterpret_cast<float*>(qs + RT * 16 * D);  // [RT*16]
+  float* rowIZ = rowM + RT * 16;                            // [RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cbase = tile * kRefineTile + w * 64;
-  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, kls);
+  uint4 a[4][D / 32];
+  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
   // per-row normalisers over all tiles, merged in tile order while the rows stream in
-  // (a row's tile statistics are contiguous; 32 tiles per batch of loads)
+  // (a row's tile statistics are contiguous; 16 tiles per batch of loads)
   for (int r = threadIdx.x; r < RT * 16; r += kRefineTile) {
     float M = -INFINITY, Z = 0.f;
     if (r < R) {
       const float2* rs = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);  // 16-byte aligned rows
-      for (int t0 = 0; t0 < ntile; t0 += 32) {
-        float2 p[32];
+      for (int t0 = 0; t0 < ntile; t0 += 16) {
+        float2 p[16];
 #pragma unroll
-        for (int u = 0; u < 32; u += 2) {
+        for (int u = 0; u < 16; u += 2) {
           if (t0 + u + 1 < ntile) {
             const float4 v = *reinterpret_cast<const float4*>(rs + t0 + u);
             p[u] = make_float2(v.x, v.y);
@@ -193,14 +188,13 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
           }
         }
 #pragma unroll
-        for (int u = 0; u < 32; ++u) ms_merge(M, Z, p[u].x, p[u].y);
+        for (int u = 0; u < 16; ++u) ms_merge(M, Z, p[u].x, p[u].y);
       }
     }
     rowM[r] = M;
     rowIZ[r] = r < R ? 1.f / Z : 0.f;
   }
-  uint4 a[4][D / 32];
-  refine_key_frags<D>(kls, a);
+  refine_wait_rows();
 
   float rs[4][4];
 #pragma unroll
@@ -285,7 +279,7 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
                     topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr, wcnt);
 }
 
-// fp32 path: the same three steps on VALU (stats and scores over kRefineTile-candidate
+// fp32 path: the same three steps on VALU (stats and scores over kRefineTileF32-candidate
 // tiles, then refine_select_kernel). A logit is one fma chain over the head dimension
 // in index order; fma is symmetric in its two factors, so the two kernels, which read
 // the operands from different places, compute the same bits.
@@ -349,22 +343,22 @@ __global__ __launch_bounds__(256) void refine_stats_f32_kernel(const float* __re
                                                                const int64_t* __restrict__ seq_start, int B, int Hq,
                                                                int Hkv, int G, int C, float scale2, int ntile,
                                                                float2* __restrict__ row_stats) {
-  static_assert(kRefineTile == 128, "four waves of 32 candidates");
-  extern __shared__ __align__(16) float ks[];  // [kRefineTile][D]
+  static_assert(kRefineTileF32 == 128, "four waves of 32 candidates");
+  extern __shared__ __align__(16) float ks[];  // [kRefineTileF32][D]
   __shared__ float2 wstat[4][64];
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t j0 = seq_start[s];
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  for (int i = threadIdx.x; i < kRefineTile * D / 4; i += 256) {
+  for (int i = threadIdx.x; i < kRefineTileF32 * D / 4; i += 256) {
     const int row = i / (D / 4), ch = i % (D / 4);
-    const int c = min(tile * kRefineTile + row, C - 1);
+    const int c = min(tile * kRefineTileF32 + row, C - 1);
     *reinterpret_cast<float4*>(ks + row * D + 4 * ch) =
         *reinterpret_cast<const float4*>(k + ((j0 + cd[c]) * Hkv + g) * D + 4 * ch);
   }
   __syncthreads();
-  const int nvalid = min(kRefineTile, C - tile * kRefineTile);
+  const int nvalid = min(kRefineTileF32, C - tile * kRefineTileF32);
   for (int r0 = 0; r0 < R; r0 += 64) {
     const int r = r0 + lane, rq = min(r, R - 1);
     float qr[D];
@@ -412,20 +406,20 @@ __global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __r
                                                                 const float2* __restrict__ row_stats,
                                                                 float* __restrict__ rscore) {
   constexpr int KP = D + 4;
-  extern __shared__ __align__(16) float qs[];  // [64][D], [kRefineTile][KP], rowM[R], rowIZ[R]
-  __shared__ float part[2][kRefineTile];
+  extern __shared__ __align__(16) float qs[];  // [64][D], [kRefineTileF32][KP], rowM[R], rowIZ[R]
+  __shared__ float part[2][kRefineTileF32];
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G;
   float* kt = qs + 64 * D;
-  float* rowM = kt + kRefineTile * KP;
+  float* rowM = kt + kRefineTileF32 * KP;
   float* rowIZ = rowM + R;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ci = (w & 1) * 64 + lane, half = w >> 1;
   const int64_t j0 = seq_start[s];
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  for (int i = threadIdx.x; i < kRefineTile * D / 4; i += 256) {
+  for (int i = threadIdx.x; i < kRefineTileF32 * D / 4; i += 256) {
     const int row = i / (D / 4), ch = i % (D / 4);
-    const int c = min(tile * kRefineTile + row, C - 1);
+    const int c = min(tile * kRefineTileF32 + row, C - 1);
     *reinterpret_cast<float4*>(kt + row * KP + 4 * ch) =
         *reinterpret_cast<const float4*>(k + ((j0 + cd[c]) * Hkv + g) * D + 4 * ch);
   }
@@ -463,8 +457,8 @@ __global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __r
   }
   part[half][ci] = acc;
   __syncthreads();
-  if (threadIdx.x < kRefineTile) {
-    const int cc = tile * kRefineTile + threadIdx.x;
+  if (threadIdx.x < kRefineTileF32) {
+    const int cc = tile * kRefineTileF32 + threadIdx.x;
     if (cc < C) rscore[((int64_t)s * Hkv + g) * C + cc] = part[0][threadIdx.x] + part[1][threadIdx.x];
   }
 }
@@ -473,7 +467,7 @@ __global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __r
 
 static size_t refine_smem(const Shape& s, bool stats) {
   const int RT = (s.B * s.G + 15) / 16;
-  const size_t rows = ((size_t)RT * 16 + kRefineTile) * s.D * sizeof(bf16);
+  const size_t rows = (size_t)RT * 16 * s.D * sizeof(bf16);
   return rows + (stats ? (size_t)(kRefineTile / 64) * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
 }
 
@@ -532,8 +526,8 @@ hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const
                              bool stats, hipStream_t st) {
   dim3 grid(ws.ntile, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
-  const size_t smem = stats ? (size_t)kRefineTile * s.D * sizeof(float)
-                            : ((size_t)64 * s.D + (size_t)kRefineTile * (s.D + 4) + 2 * (size_t)s.B * s.G) *
+  const size_t smem = stats ? (size_t)kRefineTileF32 * s.D * sizeof(float)
+                            : ((size_t)64 * s.D + (size_t)kRefineTileF32 * (s.D + 4) + 2 * (size_t)s.B * s.G) *
                                   sizeof(float);
   const void* kern = stats ? (s.D == 128 ? (const void*)refine_stats_f32_kernel<128>
                                          : (const void*)refine_stats_f32_kernel<64>)
