@@ -115,26 +115,31 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
   refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
   refine_wait_rows();
 
+  const bool full = cbase + 64 <= C;  // no candidate of this wave past C
   for (int rt = 0; rt < RT; ++rt) {
     f32x4_t acc[4];
     refine_tile_logits<D>(a, qs, rt, lane, acc);
-    float x[4][4];
-    float m = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = cbase + mt * 16 + (lane >> 4) * 4 + i;
-        x[mt][i] = c < C ? acc[mt][i] * scale2 : -INFINITY;
-        m = fmaxf(m, x[mt][i]);
-      }
-    m = xmax4(m);
-    float l = 0.f;
-    if (m != -INFINITY) {
+    if (!full) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) l += fast_exp2(x[mt][i] - m);
+        for (int i = 0; i < 4; ++i)
+          if (cbase + mt * 16 + (lane >> 4) * 4 + i >= C) acc[mt][i] = -INFINITY;
+    }
+    // the row max on the raw products (scale2 > 0), the logits as one fma each
+    float mr = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mr = fmaxf(mr, acc[mt][i]);
+    mr = xmax4(mr);
+    const float m = mr * scale2;
+    float l = 0.f;
+    if (mr != -INFINITY) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l += fast_exp2(fmaf(acc[mt][i], scale2, -m));
     }
     l = xsum4(l);
     if (lane < 16) wstat[w * RT * 16 + rt * 16 + lane] = make_float2(m, l);
@@ -191,7 +196,8 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
         for (int u = 0; u < 16; ++u) ms_merge(M, Z, p[u].x, p[u].y);
       }
     }
-    rowM[r] = M;
+    // rows past R: a reference far above any logit and a zero weight, so they add 0
+    rowM[r] = r < R ? M : 3.0e38f;
     rowIZ[r] = r < R ? 1.f / Z : 0.f;
   }
   refine_wait_rows();
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rs[mt][i] += r < R ? fast_exp2(acc[mt][i] * scale2 - M) * iz : 0.f;
+      for (int i = 0; i < 4; ++i) rs[mt][i] = fmaf(fast_exp2(fmaf(acc[mt][i], scale2, -M)), iz, rs[mt][i]);
   }
   // each lane summed its query row over the row tiles; now sum the 16 rows of a lane row
 #pragma unroll
