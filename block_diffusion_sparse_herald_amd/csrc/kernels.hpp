@@ -17,6 +17,10 @@ inline void klaunch(F kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st
 // workgroup covers.
 constexpr int kScanTok = 256;
 constexpr int kScoreTok = 1024;
+// Score / radix workgroups of 2048 tokens once the cache holds this many tokens: fewer
+// workgroups amortise the per-workgroup normaliser merge and histogram flush.
+constexpr int kScoreTokLarge = 2048;
+constexpr int64_t kScoreTokLargeFrom = 262144;
 constexpr int kRadixBins = 2048;
 // Longest sequence whose selection scores one workgroup keeps in LDS (144 KiB).
 constexpr int kTopcLdsMaxLen = 36864;

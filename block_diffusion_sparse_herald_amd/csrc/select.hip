@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ score + first radix digit
 
-template <int GP>
+template <int GP, int TOK>
 __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict__ logits,
                                                          const float2* __restrict__ partials,
                                                          const int64_t* __restrict__ seq_start, int Hq, int Hkv,
@@ -437,14 +437,23 @@ __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict
   const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
-  const int64_t tok0 = (int64_t)chunk * kScoreTok;
+  const int64_t tok0 = (int64_t)chunk * TOK;
   if (tok0 >= L) return;
-  constexpr int IT = kScoreTok / 256;
+  constexpr int IT = TOK / 256;
   __shared__ uint32_t h[kRadixBins];
   __shared__ float2 red[4][GP];
   __shared__ float Msh[GP], invZ[GP];
 
-  // this workgroup's logits: token-major, GP heads per token; loads first
+  // Loads first: this thread's first chunk statistics per head, then the workgroup's
+  // logits (token-major, GP heads per token). The memory counter is in order, so with
+  // the statistics issued first the normaliser merge below starts while the logits
+  // are still in flight.
+  const int nc = (int)((L + tpc - 1) / tpc);
+  float2 p0[GP];
+#pragma unroll
+  for (int hh = 0; hh < GP; ++hh)
+    p0[hh] = hh < G && (int)threadIdx.x < nc ? partials[((int64_t)s * Hq + g * G + hh) * nchunk + threadIdx.x]
+                                              : make_float2(-INFINITY, 0.f);
   float4 lv[IT][GP / 4];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -456,14 +465,14 @@ __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict
   for (int i = threadIdx.x; i < kRadixBins; i += 256) h[i] = 0u;
 
   // per-head normalisers over the whole sequence, same order in every workgroup
-  const int nc = (int)((L + tpc - 1) / tpc);
   float m[GP], z[GP];
 #pragma unroll
   for (int hh = 0; hh < GP; ++hh) {
     m[hh] = -INFINITY;
     z[hh] = 0.f;
+    ms_merge(m[hh], z[hh], p0[hh].x, p0[hh].y);
   }
-  for (int c = threadIdx.x; c < nc; c += 256) {
+  for (int c = threadIdx.x + 256; c < nc; c += 256) {
     float2 p[GP];
 #pragma unroll
     for (int hh = 0; hh < GP; ++hh)
@@ -506,7 +515,7 @@ __global__ __launch_bounds__(256) void score_hist_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ radix passes 2 and 3
 
-template <int PASS>
+template <int PASS, int TOK>
 __global__ __launch_bounds__(256) void radix_kernel(const float* __restrict__ scores,
                                                     const int64_t* __restrict__ seq_start, int Hkv, int64_t total,
                                                     int C, int nwords, uint32_t* __restrict__ hist,
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(256) void radix_kernel(const float* __restrict__ sc
   const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
-  const int64_t tok0 = (int64_t)chunk * kScoreTok;
+  const int64_t tok0 = (int64_t)chunk * TOK;
   if (tok0 >= L) return;
   __shared__ uint32_t h[kRadixBins];                // this pass
   __shared__ uint32_t prev[(PASS - 1) * kRadixBins];  // the finished histograms of the earlier passes
@@ -523,7 +532,7 @@ __global__ __launch_bounds__(256) void radix_kernel(const float* __restrict__ sc
   const float* sc = scores + (int64_t)g * total + j0;
 
   // issue the score loads first; they do not depend on the digits
-  constexpr int IT = kScoreTok / 256;
+  constexpr int IT = TOK / 256;
   uint32_t u[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -816,25 +825,25 @@ hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStr
   return hipGetLastError();
 }
 
-static int score_chunks(const Shape& s) { return (int)((s.max_len + kScoreTok - 1) / kScoreTok); }
+static int score_tok(const Shape& s) { return s.total >= kScoreTokLargeFrom ? kScoreTokLarge : kScoreTok; }
+static int score_chunks(const Shape& s) { return (int)((s.max_len + score_tok(s) - 1) / score_tok(s)); }
 
 hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st) {
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
-  if (s.G <= 4)
-    klaunch(score_hist_kernel<4>, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
-            ws.nchunk, ws.tpc, ws.scores, ws.hist);
-  else
-    klaunch(score_hist_kernel<8>, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
-            ws.nchunk, ws.tpc, ws.scores, ws.hist);
+  const bool large = score_tok(s) == kScoreTokLarge;
+  auto kern = s.G <= 4 ? (large ? score_hist_kernel<4, kScoreTokLarge> : score_hist_kernel<4, kScoreTok>)
+                       : (large ? score_hist_kernel<8, kScoreTokLarge> : score_hist_kernel<8, kScoreTok>);
+  klaunch(kern, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total, ws.nchunk, ws.tpc,
+          ws.scores, ws.hist);
   return hipGetLastError();
 }
 
 hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipStream_t st) {
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
-  if (pass == 2)
-    klaunch(radix_kernel<2>, grid, 256, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
-  else
-    klaunch(radix_kernel<3>, grid, 256, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
+  const bool large = score_tok(s) == kScoreTokLarge;
+  auto kern = pass == 2 ? (large ? radix_kernel<2, kScoreTokLarge> : radix_kernel<2, kScoreTok>)
+                        : (large ? radix_kernel<3, kScoreTokLarge> : radix_kernel<3, kScoreTok>);
+  klaunch(kern, grid, 256, 0, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords, ws.hist, ws.bits);
   return hipGetLastError();
 }
 
