@@ -231,48 +231,36 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
   __syncthreads();
 }
 
-// Radix-select step run by wave 0 alone on a histogram in LDS: finds the largest
-// digit b whose suffix count reaches k and the count strictly above it. Each lane
-// holds PER = nbins/64 consecutive bins in registers (16-byte LDS reads), lane 0
-// the top ones. Only wave 0 may call it; the result is returned in every lane.
+// Radix-select step run by one wave on a histogram (LDS or global memory): finds the
+// largest digit b whose suffix count reaches k and the count strictly above it, with
+// no branches. Lane l owns the PER = nbins/64 consecutive bins starting at
+// (63 - l) * PER (lane 0 the top ones) and sums them (16-byte reads, rotated by lane so
+// that the lanes of one read spread over the LDS banks); a wave scan of the sums names
+// the lane whose bins reach k; its PER bins, one per lane from the top, are scanned
+// again to name the bin. The result is returned in every lane.
 template <int PER>
 __device__ __forceinline__ void wave_find_digit_t(const uint32_t* hist, uint32_t k, int* digit, uint32_t* above) {
+  constexpr int NQ = PER / 4;
   const int lane = threadIdx.x & (kWave - 1);
-  const int lo = (kWave - 1 - lane) * PER;  // first bin of this lane
-  uint32_t v[PER];
-#pragma unroll
-  for (int q = 0; q < PER / 4; ++q) {
-    const uint4 t = *reinterpret_cast<const uint4*>(hist + lo + 4 * q);
-    v[4 * q] = t.x;
-    v[4 * q + 1] = t.y;
-    v[4 * q + 2] = t.z;
-    v[4 * q + 3] = t.w;
-  }
+  const int lo = (kWave - 1 - lane) * PER;
   uint32_t sum = 0;
 #pragma unroll
-  for (int b = 0; b < PER; ++b) sum += v[b];
+  for (int q = 0; q < NQ; ++q) {
+    const uint4 t = *reinterpret_cast<const uint4*>(hist + lo + 4 * ((q + lane) & (NQ - 1)));
+    sum += t.x + t.y + t.z + t.w;
+  }
   const uint32_t incl = wave_incl_scan(sum);
   const uint32_t before = incl - sum;
-  const bool mine = before < k && incl >= k;
-  int d = 0;
-  uint32_t ab = 0;
-  {
-    uint32_t acc = before;
-    bool found = false;
-#pragma unroll
-    for (int b = PER - 1; b >= 0; --b) {
-      if (!found && acc + v[b] >= k) {
-        d = lo + b;
-        ab = acc;
-        found = true;
-      }
-      acc += v[b];
-    }
-  }
-  const uint64_t who = __ballot(mine);
-  const int src = who ? __builtin_ctzll(who) : 0;
-  *digit = __builtin_amdgcn_readlane(d, src);
-  *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+  const uint64_t who = __ballot(before < k && incl >= k);
+  const int src = who ? (int)__builtin_ctzll(who) : kWave - 1;
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)before, src);
+  const int los = (kWave - 1 - src) * PER;
+  const uint32_t c = lane < PER ? hist[los + PER - 1 - lane] : 0u;
+  const uint32_t ci = wave_incl_scan(c);
+  const uint64_t hit = __ballot(lane < PER && base + ci >= k);
+  const int f = hit ? (int)__builtin_ctzll(hit) : PER - 1;
+  *digit = los + PER - 1 - f;
+  *above = base + (uint32_t)__builtin_amdgcn_readlane((int)(ci - c), f);
 }
 
 __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, int nbins, uint32_t k, int* digit,
@@ -317,10 +305,16 @@ __device__ __forceinline__ uint32_t lds_radix_threshold(const uint32_t* u, int n
       const uint32_t mask = pass == 2 ? 1023u : 2047u;
       for (int i = tid; i < kBins; i += NT) h[i] = 0u;
       __syncthreads();
-#pragma unroll 8
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t v = u[i];
-        if (pass == 0 || (v >> (shift + (pass == 2 ? 10 : 11))) == prefix) atomicAdd(&h[(v >> shift) & mask], 1u);
+      // eight keys read before their atomics (the compiler cannot move reads of u
+      // past atomics on h, which may alias)
+      for (int i0 = tid; i0 < n; i0 += 8 * NT) {
+        uint32_t x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = i0 + q * NT < n ? u[i0 + q * NT] : 0u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (i0 + q * NT < n && (pass == 0 || (x[q] >> (shift + (pass == 2 ? 10 : 11))) == prefix))
+            atomicAdd(&h[(x[q] >> shift) & mask], 1u);
       }
       __syncthreads();
     }
@@ -414,6 +408,180 @@ __device__ __forceinline__ void lds_emit(const uint32_t* u, int n, uint32_t thr,
       pos += (uint32_t)__builtin_popcountll(btake);
       tie += (uint32_t)__builtin_popcountll(beq);
     }
+  }
+}
+
+// ---------------------------------------------------------------- top-k in registers
+
+// Exact top-k of n keys (fp32 bit patterns of non-negative scores, so unsigned order
+// is value order; ties to the lower position) held in the registers of a 1024-thread
+// workgroup: wave w holds positions [w * nit * 256, (w + 1) * nit * 256), in nit chunks
+// of 256; lane l holds positions chunk * 256 + 4l + (0..3) of each chunk, so the order
+// (wave, chunk, lane, element) is position order. No pass goes through LDS: the radix
+// histograms take LDS atomics and the emission is ordered by wave scans.
+constexpr int kTopkWaves = 16;
+
+// 256-position chunks per wave for n keys.
+__host__ __device__ constexpr int topk_chunks(int n) { return ((n + kTopkWaves - 1) / kTopkWaves + 255) / 256; }
+
+// Loads this lane's keys src[0..n) (positions past n read as 0): 16-byte loads when src
+// is 16-byte aligned and n a multiple of 4, else 4-byte loads.
+template <int MAXIT, typename T>
+__device__ __forceinline__ void topk_load(const T* __restrict__ src, int n, int nit, uint32_t (&v)[MAXIT][4]) {
+  static_assert(sizeof(T) == 4, "32-bit keys");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+  if (((uintptr_t)src & 15) == 0 && (n & 3) == 0) {
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      const int e = (w * nit + it) * 256 + 4 * lane;
+      uint4 t = make_uint4(0u, 0u, 0u, 0u);
+      if (it < nit && e < n) t = *reinterpret_cast<const uint4*>(s32 + e);
+      v[it][0] = t.x;
+      v[it][1] = t.y;
+      v[it][2] = t.z;
+      v[it][3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = (w * nit + it) * 256 + 4 * lane + c;
+        v[it][c] = it < nit && e < n ? s32[e] : 0u;
+      }
+  }
+}
+
+// Histogram of the digit (x >> shift) & mask over this lane's keys x inside n whose
+// bits above hishift equal prefix (every key when hishift >= 32). Runs of equal digits
+// among a lane's four consecutive keys take one atomic, which thins the same-address
+// atomics of clustered scores.
+template <int MAXIT>
+__device__ __forceinline__ void topk_hist(const uint32_t (&v)[MAXIT][4], int n, int nit, int hishift,
+                                          uint32_t prefix, int shift, uint32_t mask, uint32_t* h) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    if (it >= nit) continue;
+    const int e = (w * nit + it) * 256 + 4 * lane;
+    uint32_t cur = 0xffffffffu, cnt = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t x = v[it][c];
+      const bool in = e + c < n && (hishift >= 32 || (x >> hishift) == prefix);
+      const uint32_t d = (x >> shift) & mask;
+      if (in) {
+        if (d == cur) {
+          ++cnt;
+        } else {
+          if (cnt) atomicAdd(&h[cur], cnt);
+          cur = d;
+          cnt = 1;
+        }
+      }
+    }
+    if (cnt) atomicAdd(&h[cur], cnt);
+  }
+}
+
+// Histogram of the digit (x >> shift) & mask over this lane's keys x inside n whose
+// bits above hishift equal prefix: one atomic per matching key (the later digits,
+// where few keys match and they spread over the bins).
+template <int MAXIT>
+__device__ __forceinline__ void topk_hist_sparse(const uint32_t (&v)[MAXIT][4], int n, int nit, int hishift,
+                                                 uint32_t prefix, int shift, uint32_t mask, uint32_t* h) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    if (it >= nit) continue;
+    const int e = (w * nit + it) * 256 + 4 * lane;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t x = v[it][c];
+      if (e + c < n && (x >> hishift) == prefix) atomicAdd(&h[(x >> shift) & mask], 1u);
+    }
+  }
+}
+
+// Collects, in ascending position order, every key above thr plus the first ties_wanted
+// keys equal to it (all_ties: every key equal to thr is wanted, so the test is x >= thr)
+// into pick_idx[p] = index(chunk, element, position) and pick_val[p] (if not NULL) in
+// LDS, then writes the k picks to out / outs (outs may be NULL) with coalesced stores.
+// wcnt holds kTopkWaves pairs in LDS. Every thread of the workgroup calls it.
+template <int MAXIT, typename IndexF>
+__device__ __forceinline__ void topk_emit(const uint32_t (&v)[MAXIT][4], IndexF index, int n, int nit,
+                                          uint32_t thr, uint32_t ties_wanted, bool all_ties, uint32_t k,
+                                          int32_t* pick_idx, float* pick_val, int32_t* __restrict__ out,
+                                          float* __restrict__ outs, uint32_t (*wcnt)[2]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // with all_ties the keys equal to thr count as above it
+  const uint32_t lo = all_ties ? thr : thr + 1u;
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    if (it >= nit) continue;
+    const int e = (w * nit + it) * 256 + 4 * lane;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      ngt += (e + c < n && v[it][c] >= lo) ? 1u : 0u;
+      if (!all_ties) neq += (e + c < n && v[it][c] == thr) ? 1u : 0u;
+    }
+  }
+  const uint32_t tgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ngt), 63);
+  const uint32_t teq = all_ties ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(neq), 63);
+  if (lane == 0) {
+    wcnt[w][0] = tgt;
+    wcnt[w][1] = teq;
+  }
+  __syncthreads();
+  uint32_t tie = 0, pos = 0;
+  for (int x = 0; x < w; ++x) {
+    const uint32_t take = min(wcnt[x][1], ties_wanted - min(ties_wanted, tie));
+    pos += wcnt[x][0] + take;
+    tie += wcnt[x][1];
+  }
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    if (it >= nit) continue;
+    const int e = (w * nit + it) * 256 + 4 * lane;
+    bool take[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) take[c] = e + c < n && v[it][c] >= lo;
+    if (teq) {  // this wave holds keys equal to the threshold: rank them by position
+      bool eq[4];
+      uint32_t ne = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        eq[c] = e + c < n && v[it][c] == thr;
+        ne += eq[c] ? 1u : 0u;
+      }
+      const uint32_t incl = wave_incl_scan(ne);
+      uint32_t r = tie + incl - ne;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (eq[c]) take[c] = r++ < ties_wanted;
+      tie += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    }
+    uint32_t nt = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nt += take[c] ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan(nt);
+    uint32_t p = pos + incl - nt;
+    pos += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (take[c] && p < k) {
+        pick_idx[p] = index(it, c, e + c);
+        if (pick_val) pick_val[p] = __uint_as_float(v[it][c]);
+      }
+      p += take[c] ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < k; i += kTopkWaves * 64) {
+    out[i] = pick_idx[i];
+    if (outs) outs[i] = pick_val[i];
   }
 }
 

@@ -22,7 +22,8 @@ constexpr int kScoreTok = 1024;
 constexpr int kScoreTokLarge = 2048;
 constexpr int64_t kScoreTokLargeFrom = 262144;
 constexpr int kRadixBins = 2048;
-// Longest sequence whose selection scores one workgroup keeps in LDS (144 KiB).
+// Longest sequence whose selection scores one 1024-thread workgroup keeps in registers
+// (36 per thread) for the one-kernel top-C.
 constexpr int kTopcLdsMaxLen = 36864;
 // Candidates one refine workgroup covers (bf16 MFMA path: 64 per wave; fp32 path).
 constexpr int kRefineTile = 256;

@@ -233,10 +233,12 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
   }
 }
 
-// Exact top-K of the refine scores of one (sequence, KV head): three radix digits,
-// ballot emission. STAGED (C <= kMaxCandidates): scores and candidate indices first
-// copied to LDS with 16-byte loads; otherwise (candidate sets up to the whole sequence)
-// the same passes read them from global memory.
+// Exact top-K of the refine scores of one (sequence, KV head): three radix digits
+// (11, 11, 10 bits of the fp32 pattern, R >= 0), ties to the lower position, ascending
+// output. STAGED (C <= kMaxCandidates): scores and candidate indices stay in registers
+// (topk_load's layout: each wave a contiguous range of positions), the histograms take
+// LDS atomics and the picks are ordered by wave scans in LDS, then written out. Otherwise (candidate sets up to the
+// whole sequence) the passes read them from global memory.
 template <bool STAGED>
 __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __restrict__ cand,
                                                             const float* __restrict__ rscore, int Hkv, int C,
@@ -244,45 +246,75 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
                                                             float* __restrict__ topk_score) {
   constexpr int NT = 1024;
   const int g = blockIdx.x, s = blockIdx.y;
-  extern __shared__ uint32_t sm[];  // STAGED: [C] scores, then [C] candidate indices
   __shared__ uint32_t h[kRadixBins];
   __shared__ uint32_t wcnt[NT / 64][2];
-  __shared__ uint32_t dig[2];
+  __shared__ uint32_t dig[4];
   const int64_t base = ((int64_t)s * Hkv + g) * C;
-  const uint32_t* u = STAGED ? sm : reinterpret_cast<const uint32_t*>(rscore + base);
-  const int32_t* ci = STAGED ? reinterpret_cast<const int32_t*>(sm + C) : cand + base;
-  if (STAGED) {
-    uint32_t* su = sm;
-    int32_t* sc = reinterpret_cast<int32_t*>(sm + C);
-    constexpr int U = 4;
-    const int n4 = C % 4 == 0 ? C / 4 : 0;  // 16-byte loads need 16-byte aligned rows
-    for (int i0 = 0; i0 < n4; i0 += NT * U) {
-      uint4 a[U], b[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int i = i0 + k * NT + threadIdx.x;
-        a[k] = i < n4 ? *reinterpret_cast<const uint4*>(rscore + base + 4 * i) : make_uint4(0, 0, 0, 0);
-        b[k] = i < n4 ? *reinterpret_cast<const uint4*>(cand + base + 4 * i) : make_uint4(0, 0, 0, 0);
+  int32_t* out = topk_idx + ((int64_t)s * Hkv + g) * topk;
+  float* outs = topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr;
+  if constexpr (STAGED) {
+    constexpr int MAXIT = topk_chunks(kMaxCandidates);
+    __shared__ uint32_t h2[kRadixBins], h3[kRadixBins / 2];
+    extern __shared__ int32_t picks[];  // [topk] picks, then [topk] scores when they are wanted
+    const int tid = threadIdx.x, w = tid >> 6;
+    const int nit = topk_chunks(C);
+    uint32_t v[MAXIT][4], ix[MAXIT][4];
+    topk_load<MAXIT>(rscore + base, C, nit, v);
+    topk_load<MAXIT>(cand + base, C, nit, ix);
+    for (int i = tid; i < kRadixBins; i += NT) h[i] = h2[i] = 0u;
+    if (tid < kRadixBins / 2) h3[tid] = 0u;
+    __syncthreads();
+    topk_hist<MAXIT>(v, C, nit, 32, 0u, 21, 2047u, h);  // digit 1 (bits 31..21)
+    __syncthreads();
+    if (w == 0) {
+      int d;
+      uint32_t above;
+      wave_find_digit(h, kRadixBins, (uint32_t)topk, &d, &above);
+      if (tid == 0) {
+        dig[0] = (uint32_t)d;
+        dig[1] = above;
       }
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int i = i0 + k * NT + threadIdx.x;
-        if (i < n4) {
-          reinterpret_cast<uint4*>(su)[i] = a[k];
-          reinterpret_cast<uint4*>(sc)[i] = b[k];
-        }
-      }
-    }
-    for (int i = 4 * n4 + threadIdx.x; i < C; i += NT) {
-      su[i] = __float_as_uint(rscore[base + i]);
-      sc[i] = cand[base + i];
     }
     __syncthreads();
+    const uint32_t d1 = dig[0];
+    uint32_t want = (uint32_t)topk - dig[1];
+    topk_hist_sparse<MAXIT>(v, C, nit, 21, d1, 10, 2047u, h2);  // digit 2 (bits 20..10)
+    __syncthreads();
+    if (w == 0) {
+      int d;
+      uint32_t above;
+      wave_find_digit(h2, kRadixBins, want, &d, &above);
+      if (tid == 0) {
+        dig[2] = (uint32_t)d;
+        dig[3] = above;
+      }
+    }
+    __syncthreads();
+    want -= dig[3];
+    const uint32_t prefix = (d1 << 11) | dig[2];
+    topk_hist_sparse<MAXIT>(v, C, nit, 10, prefix, 0, 1023u, h3);  // digit 3 (bits 9..0)
+    __syncthreads();
+    if (w == 0) {
+      int d;
+      uint32_t above;
+      wave_find_digit(h3, kRadixBins / 2, want, &d, &above);
+      if (tid == 0) {
+        dig[0] = (uint32_t)d;
+        dig[1] = above;
+      }
+    }
+    __syncthreads();
+    const uint32_t thr = (prefix << 10) | dig[0];
+    const uint32_t ties = want - dig[1];
+    topk_emit<MAXIT>(v, [&](int it, int c, int) { return (int32_t)ix[it][c]; }, C, nit, thr, ties,
+                     h3[dig[0]] == ties, (uint32_t)topk, picks, outs ? reinterpret_cast<float*>(picks + topk) : nullptr,
+                     out, outs, wcnt);
+  } else {
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(rscore + base);
+    uint32_t ties;
+    const uint32_t thr = lds_radix_threshold<NT>(u, C, (uint32_t)topk, h, dig, false, &ties);
+    lds_emit<NT / 64>(u, C, thr, ties, cand + base, out, outs, wcnt);
   }
-  uint32_t ties;
-  const uint32_t thr = lds_radix_threshold<NT>(u, C, (uint32_t)topk, h, dig, false, &ties);
-  lds_emit<NT / 64>(u, C, thr, ties, ci, topk_idx + ((int64_t)s * Hkv + g) * topk,
-                    topk_score ? topk_score + ((int64_t)s * Hkv + g) * topk : nullptr, wcnt);
 }
 
 // fp32 path: the same three steps on VALU (stats and scores over kRefineTileF32-candidate
@@ -520,7 +552,7 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
             topk_idx, topk_score);
     return hipGetLastError();
   }
-  const size_t smem = 2 * (size_t)s.C * sizeof(uint32_t);
+  const size_t smem = (size_t)s.topk * sizeof(int32_t) * (topk_score ? 2 : 1);
   hipError_t e = allow_smem((const void*)refine_select_kernel<true>, smem);
   if (e != hipSuccess) return e;
   klaunch(refine_select_kernel<true>, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, s.Hkv, s.C, s.topk,

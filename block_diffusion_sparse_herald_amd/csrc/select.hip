@@ -23,7 +23,8 @@
 //                     the three histograms, ties to the lowest indices, ascending
 //                     indices from the bitmaps (block-wide prefix counts).
 //   topc_lds_kernel   instead of the last three when every sequence's scores fit
-//                     in LDS: digits two and three and the emission on an LDS copy.
+//                     in the registers of one workgroup: digits two and three and
+//                     the emission on the registers.
 // S >= 0, so its IEEE bit pattern orders like its value and radix select is exact.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -701,58 +702,78 @@ __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ sc
   }
 }
 
-// ------------------------------------------------------------------ top-C in LDS
+// ------------------------------------------------------------------ top-C in registers
 
-// One workgroup per (sequence, KV head) whose scores all fit in LDS (the sequences
-// of up to kTopcLdsMaxLen tokens): the first digit comes from the histogram that
-// score_hist_kernel built, digits two and three from histograms of the LDS copy,
-// then the candidates are emitted in ascending order with wave ballots (a wave takes
-// a contiguous range of tokens; one exchange of per-wave counts fixes the tie ranks
-// and output positions). Replaces radix_kernel<2>, radix_kernel<3> and emit_kernel.
+// One 1024-thread workgroup per (sequence, KV head) of up to kTopcLdsMaxLen tokens: the
+// scores stay in registers (each wave a contiguous range of tokens, see topk_load),
+// the first digit comes from the histogram score_hist_kernel built (read by wave 0
+// while the score loads are in flight), digits two and three from LDS histograms of
+// the keys that match the digits found so far, and the candidates are collected in
+// ascending order in LDS through wave scans, then written out. Replaces radix_kernel<2>, radix_kernel<3> and emit_kernel.
 __global__ __launch_bounds__(1024) void topc_lds_kernel(const float* __restrict__ scores,
                                                        const int64_t* __restrict__ seq_start, int Hkv,
                                                        int64_t total, int C, const uint32_t* __restrict__ hist,
                                                        int32_t* __restrict__ cand, float* __restrict__ cand_score) {
-  constexpr int NT = 1024, NW = NT / 64;
-  extern __shared__ uint32_t u[];  // [L] score bit patterns
-  __shared__ uint32_t h[kRadixBins];
-  __shared__ uint32_t wcnt[NW][2];
+  constexpr int MAXIT = topk_chunks(kTopcLdsMaxLen);
+  __shared__ uint32_t h2[kRadixBins], h3[kRadixBins / 2];
+  __shared__ uint32_t wcnt[kTopkWaves][2];
   __shared__ uint32_t dig[4];
+  extern __shared__ int32_t picks[];  // [C] candidates, then [C] scores when they are wanted
   const int g = blockIdx.x, s = blockIdx.y;
   const int64_t j0 = seq_start[s];
   const int L = (int)(seq_start[s + 1] - j0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int nit = topk_chunks(L);
   const float* sc = scores + (int64_t)g * total + j0;
-  const uint32_t* gh = hist + (int64_t)(s * Hkv + g) * 3 * kRadixBins;
 
-  for (int i = tid; i < kRadixBins / 4; i += NT) reinterpret_cast<uint4*>(h)[i] = reinterpret_cast<const uint4*>(gh)[i];
-  // scores -> LDS, 16 bytes per load, eight loads in flight per thread
-  {
-    const bool al = ((uintptr_t)sc & 15) == 0;
-    const int n4 = al ? L / 4 : 0;
-    constexpr int U = 8;
-    for (int i0 = 0; i0 < n4; i0 += NT * U) {
-      uint4 v[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int i = i0 + k * NT + tid;
-        v[k] = i < n4 ? *reinterpret_cast<const uint4*>(sc + 4 * i) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int i = i0 + k * NT + tid;
-        if (i < n4) reinterpret_cast<uint4*>(u)[i] = v[k];
-      }
+  uint32_t v[MAXIT][4];
+  topk_load<MAXIT>(sc, L, nit, v);
+  for (int i = tid; i < kRadixBins; i += 1024) h2[i] = 0u;
+  if (tid < kRadixBins / 2) h3[tid] = 0u;
+  if (w == 0) {  // digit 1 (bits 31..21)
+    int d;
+    uint32_t above;
+    wave_find_digit(hist + (int64_t)(s * Hkv + g) * 3 * kRadixBins, kRadixBins, (uint32_t)C, &d, &above);
+    if (tid == 0) {
+      dig[0] = (uint32_t)d;
+      dig[1] = above;
     }
-    for (int i = 4 * n4 + tid; i < L; i += NT) u[i] = __float_as_uint(sc[i]);
   }
   __syncthreads();
-
-  // digit 1 (bits 31..21) from the global histogram, digits 2 (20..10) and 3 (9..0) here
-  uint32_t ties_wanted;
-  const uint32_t thr = lds_radix_threshold<NT>(u, L, (uint32_t)C, h, dig, true, &ties_wanted);
-  lds_emit<NW>(u, L, thr, ties_wanted, nullptr, cand + (int64_t)(s * Hkv + g) * C,
-               cand_score ? cand_score + (int64_t)(s * Hkv + g) * C : nullptr, wcnt);
+  const uint32_t d1 = dig[0];
+  uint32_t want = (uint32_t)C - dig[1];
+  topk_hist_sparse<MAXIT>(v, L, nit, 21, d1, 10, 2047u, h2);  // digit 2 (bits 20..10)
+  __syncthreads();
+  if (w == 0) {
+    int d;
+    uint32_t above;
+    wave_find_digit(h2, kRadixBins, want, &d, &above);
+    if (tid == 0) {
+      dig[2] = (uint32_t)d;
+      dig[3] = above;
+    }
+  }
+  __syncthreads();
+  want -= dig[3];
+  const uint32_t prefix = (d1 << 11) | dig[2];
+  topk_hist_sparse<MAXIT>(v, L, nit, 10, prefix, 0, 1023u, h3);  // digit 3 (bits 9..0)
+  __syncthreads();
+  if (w == 0) {
+    int d;
+    uint32_t above;
+    wave_find_digit(h3, kRadixBins / 2, want, &d, &above);
+    if (tid == 0) {
+      dig[0] = (uint32_t)d;
+      dig[1] = above;
+    }
+  }
+  __syncthreads();
+  const uint32_t thr = (prefix << 10) | dig[0];
+  const uint32_t ties = want - dig[1];
+  float* outs = cand_score ? cand_score + (int64_t)(s * Hkv + g) * C : nullptr;
+  topk_emit<MAXIT>(v, [](int, int, int pos) { return (int32_t)pos; }, L, nit, thr, ties, h3[dig[0]] == ties,
+                   (uint32_t)C, picks, outs ? reinterpret_cast<float*>(picks + C) : nullptr,
+                   cand + (int64_t)(s * Hkv + g) * C, outs, wcnt);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -850,7 +871,7 @@ hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipSt
 bool topc_in_lds(const Shape& s) { return s.max_len <= kTopcLdsMaxLen; }
 
 hipError_t launch_topc_lds(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score, hipStream_t st) {
-  const size_t smem = (size_t)s.max_len * sizeof(uint32_t);
+  const size_t smem = (size_t)s.C * sizeof(int32_t) * (cand_score ? 2 : 1);
   hipError_t e = allow_smem((const void*)topc_lds_kernel, smem);
   if (e != hipSuccess) return e;
   klaunch(topc_lds_kernel, dim3(s.Hkv, s.nseq), 1024, smem, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.hist,
