@@ -488,9 +488,9 @@ __device__ __forceinline__ void topk_hist(const uint32_t (&v)[MAXIT][4], int n, 
 // Histogram of the digit (x >> shift) & mask over this lane's keys x inside n whose
 // bits above hishift equal prefix: one atomic per matching key (the later digits,
 // where few keys match and they spread over the bins).
-template <int MAXIT>
-__device__ __forceinline__ void topk_hist_sparse(const uint32_t (&v)[MAXIT][4], int n, int nit, int hishift,
-                                                 uint32_t prefix, int shift, uint32_t mask, uint32_t* h) {
+template <int MAXIT, bool FULL>
+__device__ __forceinline__ void topk_hist_sparse_t(const uint32_t (&v)[MAXIT][4], int n, int nit, int hishift,
+                                                   uint32_t prefix, int shift, uint32_t mask, uint32_t* h) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
@@ -499,9 +499,21 @@ __device__ __forceinline__ void topk_hist_sparse(const uint32_t (&v)[MAXIT][4], 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t x = v[it][c];
-      if (e + c < n && (x >> hishift) == prefix) atomicAdd(&h[(x >> shift) & mask], 1u);
+      if ((FULL || e + c < n) && (x >> hishift) == prefix) atomicAdd(&h[(x >> shift) & mask], 1u);
     }
   }
+}
+
+// True when every position this wave holds is below n (no validity tests needed).
+__device__ __forceinline__ bool topk_wave_full(int n, int nit) {
+  return ((threadIdx.x >> 6) + 1) * nit * 256 <= n;
+}
+
+template <int MAXIT>
+__device__ __forceinline__ void topk_hist_sparse(const uint32_t (&v)[MAXIT][4], int n, int nit, int hishift,
+                                                 uint32_t prefix, int shift, uint32_t mask, uint32_t* h) {
+  if (topk_wave_full(n, nit)) topk_hist_sparse_t<MAXIT, true>(v, n, nit, hishift, prefix, shift, mask, h);
+  else topk_hist_sparse_t<MAXIT, false>(v, n, nit, hishift, prefix, shift, mask, h);
 }
 
 // Collects, in ascending position order, every key above thr plus the first ties_wanted
@@ -509,14 +521,11 @@ __device__ __forceinline__ void topk_hist_sparse(const uint32_t (&v)[MAXIT][4], 
 // into pick_idx[p] = index(chunk, element, position) and pick_val[p] (if not NULL) in
 // LDS, then writes the k picks to out / outs (outs may be NULL) with coalesced stores.
 // wcnt holds kTopkWaves pairs in LDS. Every thread of the workgroup calls it.
-template <int MAXIT, typename IndexF>
-__device__ __forceinline__ void topk_emit(const uint32_t (&v)[MAXIT][4], IndexF index, int n, int nit,
-                                          uint32_t thr, uint32_t ties_wanted, bool all_ties, uint32_t k,
-                                          int32_t* pick_idx, float* pick_val, int32_t* __restrict__ out,
-                                          float* __restrict__ outs, uint32_t (*wcnt)[2]) {
+// Per-lane counts of the keys at or above lo (ngt) and equal to thr (neq, unless all_ties).
+template <int MAXIT, bool FULL>
+__device__ __forceinline__ uint2 topk_count_t(const uint32_t (&v)[MAXIT][4], int n, int nit, uint32_t lo, uint32_t thr,
+                                              bool all_ties) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // with all_ties the keys equal to thr count as above it
-  const uint32_t lo = all_ties ? thr : thr + 1u;
   uint32_t ngt = 0, neq = 0;
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
@@ -524,36 +533,34 @@ __device__ __forceinline__ void topk_emit(const uint32_t (&v)[MAXIT][4], IndexF 
     const int e = (w * nit + it) * 256 + 4 * lane;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      ngt += (e + c < n && v[it][c] >= lo) ? 1u : 0u;
-      if (!all_ties) neq += (e + c < n && v[it][c] == thr) ? 1u : 0u;
+      ngt += ((FULL || e + c < n) && v[it][c] >= lo) ? 1u : 0u;
+      if (!all_ties) neq += ((FULL || e + c < n) && v[it][c] == thr) ? 1u : 0u;
     }
   }
-  const uint32_t tgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ngt), 63);
-  const uint32_t teq = all_ties ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(neq), 63);
-  if (lane == 0) {
-    wcnt[w][0] = tgt;
-    wcnt[w][1] = teq;
-  }
-  __syncthreads();
-  uint32_t tie = 0, pos = 0;
-  for (int x = 0; x < w; ++x) {
-    const uint32_t take = min(wcnt[x][1], ties_wanted - min(ties_wanted, tie));
-    pos += wcnt[x][0] + take;
-    tie += wcnt[x][1];
-  }
+  return make_uint2(ngt, neq);
+}
+
+// Collects this wave's picks: pos and tie are the wave's running output position and
+// tie rank (uniform); teq says whether the wave holds keys equal to thr.
+template <int MAXIT, bool FULL, typename IndexF>
+__device__ __forceinline__ void topk_collect_t(const uint32_t (&v)[MAXIT][4], IndexF index, int n, int nit,
+                                               uint32_t lo, uint32_t thr, uint32_t ties_wanted, uint32_t teq,
+                                               uint32_t k, uint32_t pos, uint32_t tie, int32_t* pick_idx,
+                                               float* pick_val) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
     if (it >= nit) continue;
     const int e = (w * nit + it) * 256 + 4 * lane;
     bool take[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) take[c] = e + c < n && v[it][c] >= lo;
+    for (int c = 0; c < 4; ++c) take[c] = (FULL || e + c < n) && v[it][c] >= lo;
     if (teq) {  // this wave holds keys equal to the threshold: rank them by position
       bool eq[4];
       uint32_t ne = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        eq[c] = e + c < n && v[it][c] == thr;
+        eq[c] = (FULL || e + c < n) && v[it][c] == thr;
         ne += eq[c] ? 1u : 0u;
       }
       const uint32_t incl = wave_incl_scan(ne);
@@ -578,6 +585,42 @@ __device__ __forceinline__ void topk_emit(const uint32_t (&v)[MAXIT][4], IndexF 
       p += take[c] ? 1u : 0u;
     }
   }
+}
+
+// Collects, in ascending position order, every key above thr plus the first ties_wanted
+// keys equal to it (all_ties: every key equal to thr is wanted, so the test is x >= thr)
+// into pick_idx[p] = index(chunk, element, position) and pick_val[p] (if not NULL) in
+// LDS, then writes the k picks to out / outs (outs may be NULL) with coalesced stores.
+// wcnt holds kTopkWaves pairs in LDS. Every thread of the workgroup calls it. Waves whose
+// positions all lie below n skip the per-key validity tests.
+template <int MAXIT, typename IndexF>
+__device__ __forceinline__ void topk_emit(const uint32_t (&v)[MAXIT][4], IndexF index, int n, int nit,
+                                          uint32_t thr, uint32_t ties_wanted, bool all_ties, uint32_t k,
+                                          int32_t* pick_idx, float* pick_val, int32_t* __restrict__ out,
+                                          float* __restrict__ outs, uint32_t (*wcnt)[2]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool full = topk_wave_full(n, nit);
+  // with all_ties the keys equal to thr count as above it
+  const uint32_t lo = all_ties ? thr : thr + 1u;
+  const uint2 cnt = full ? topk_count_t<MAXIT, true>(v, n, nit, lo, thr, all_ties)
+                         : topk_count_t<MAXIT, false>(v, n, nit, lo, thr, all_ties);
+  const uint32_t tgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt.x), 63);
+  const uint32_t teq = all_ties ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt.y), 63);
+  if (lane == 0) {
+    wcnt[w][0] = tgt;
+    wcnt[w][1] = teq;
+  }
+  __syncthreads();
+  uint32_t tie = 0, pos = 0;
+  for (int x = 0; x < w; ++x) {
+    const uint32_t take = min(wcnt[x][1], ties_wanted - min(ties_wanted, tie));
+    pos += wcnt[x][0] + take;
+    tie += wcnt[x][1];
+  }
+  if (full)
+    topk_collect_t<MAXIT, true>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
+  else
+    topk_collect_t<MAXIT, false>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
   __syncthreads();
   for (uint32_t i = threadIdx.x; i < k; i += kTopkWaves * 64) {
     out[i] = pick_idx[i];
