@@ -23,7 +23,7 @@ import torch
 
 import oracle.herald_oracle as orc
 from block_diffusion_sparse_herald_amd import herald as H
-from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, Workload, bf16_bits_to_f32, make_batch
+from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_batch
 from block_diffusion_sparse_herald_amd.runner import BlockRunner, batch_to_device, device_tensor
 from parity import ATOL, band_check, max_abs
 
@@ -214,6 +214,40 @@ def test_strict_ties(dtype):
     torch.cuda.synchronize()
     assert (to_np(r.cand) == np.arange(wl.C)).all()
     assert (to_np(r.sel) == np.arange(wl.topk)).all()
+
+
+@pytest.mark.parametrize("name,L,nseq", [("regs_max_L36864", 36864, 1), ("regs_unaligned_L36863", 36863, 2),
+                                         ("radix_L40000", 40000, 1)])
+def test_ties_straddle_threshold(name, L, nseq):
+    """Every even key is one bit-identical key planted along the group's mean query
+    direction, so the top C (C < L/2) lies wholly inside one tie group: candidates are
+    exactly the first C even positions and the subset the first topk of those (ties to
+    the lower index), on the one-workgroup top-C at its longest sequence (all 16 waves
+    full; a second sequence starting at an unaligned offset) and on the radix path."""
+    wl = Workload(name, nseq=nseq, L=L, Hq=4, Hkv=1, d=64, dtype="bf16", B=4, C=5000, topk=2000, T=1,
+                  seed_base=8300)
+    batch = make_batch(wl)
+    scale = orc.default_scale(wl.d)
+    for s in range(nseq):
+        a = int(batch.seq_start[s])
+        q0 = widen(batch.q0[s])
+        u = q0.sum(axis=(0, 1))
+        u /= np.linalg.norm(u)
+        k0 = widen(batch.k_cache[a:a + 1, 0])[0]
+        kdup = f32_to_bf16_bits((4.0 * np.linalg.norm(k0) * u).astype(np.float32))
+        batch.k_cache[a:a + L:2, 0] = kdup
+        cand_o, S = orc.select_merged(q0, widen(batch.k_cache[a:a + L]), wl.C, scale)
+        assert S[0][0::2].min() > S[0][1::2].max(), "planted copies must outscore every other key"
+        assert (cand_o[0] == np.arange(0, 2 * wl.C, 2)).all()
+    dev = batch_to_device(batch)
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
+    r.select(dev["q0"], dev["k_cache"])
+    r.refine(dev["q0"], dev["k_cache"])
+    torch.cuda.synchronize()
+    cand, sel = to_np(r.cand), to_np(r.sel)
+    for s in range(nseq):
+        assert (cand[s, 0] == np.arange(0, 2 * wl.C, 2)).all(), f"{name} seq {s} candidates"
+        assert (sel[s, 0] == np.arange(0, 2 * wl.topk, 2)).all(), f"{name} seq {s} subset"
 
 
 def test_rerun_is_bit_identical():
