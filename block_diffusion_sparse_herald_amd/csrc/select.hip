@@ -590,9 +590,12 @@ __global__ __launch_bounds__(256) void radix_kernel(const float* __restrict__ sc
 
 // One workgroup per (sequence, KV head). Words of the prefix bitmaps are handled in
 // rounds of 4 per thread; ties (keys equal to the threshold) are kept lowest index
-// first, and the final indices come out in ascending order. The picks are collected
-// in LDS and written out (with their scores) by all threads at the end, so the
-// score gathers are independent loads.
+// first, and the final indices come out in ascending order. The picks of a round are
+// not written by the thread that owns their word (selected tokens cluster, so a few
+// threads would own most of them): each word's mask and first output position go to
+// LDS, with an anchor per 64 output slots (the word that holds the slot), and thread t
+// fills slots t, t + 1024, ..., eight at a time: a branch-free binary search between
+// the two anchors around the slot finds its word, a select of the set bits its token.
 __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ scores,
                                                    const int64_t* __restrict__ seq_start, int Hkv, int64_t total,
                                                    int C, int nwords, const uint32_t* __restrict__ hist,
@@ -604,7 +607,10 @@ __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ sc
   const int64_t L = seq_start[s + 1] - j0;
   __shared__ uint32_t hs[3 * kRadixBins];
   __shared__ uint32_t lds[NT / 64 + 4];
-  extern __shared__ int32_t picks[];  // [C]
+  extern __shared__ uint64_t wmask[];  // [NT * WPT] selected bits per word, then [NT * WPT] u32 first positions,
+                                       // then [NT * WPT * 64 / 64 + 1] u32 anchors
+  uint32_t* wpos = reinterpret_cast<uint32_t*>(wmask + NT * WPT);
+  uint32_t* anchor = wpos + NT * WPT;
   const uint32_t* gh = hist + (int64_t)(s * Hkv + g) * 3 * kRadixBins;
   for (int i = threadIdx.x; i < 3 * kRadixBins / 4; i += NT)
     reinterpret_cast<uint4*>(hs)[i] = reinterpret_cast<const uint4*>(gh)[i];
@@ -668,37 +674,86 @@ __global__ __launch_bounds__(1024) void emit_kernel(const float* __restrict__ sc
       my_sel += (uint32_t)__builtin_popcountll(gt[i]);
     }
     uint32_t pos = pos_base + block_exclusive_scan<NT>(my_sel, lds, &tot);
-    pos_base += tot;
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
-      uint64_t x = gt[i];
-      while (x) {
-        const int b = __builtin_ctzll(x);
-        x &= x - 1;
-        if (pos < (uint32_t)C) picks[pos] = (int32_t)(((w0 + i) << 6) + b);
-        ++pos;
+      const uint32_t n = (uint32_t)__builtin_popcountll(gt[i]);
+      wmask[threadIdx.x * WPT + i] = gt[i];
+      wpos[threadIdx.x * WPT + i] = pos;
+      // anchors: the word that holds every 64th slot of the round
+      for (uint32_t a = (pos - pos_base + 63) & ~63u; a < pos - pos_base + n; a += 64)
+        anchor[a >> 6] = threadIdx.x * WPT + i;
+      pos += n;
+    }
+    __syncthreads();
+    const int nwr = (int)min((int64_t)NT * WPT, nw - r0);  // words of this round
+    const uint32_t qend = min(pos_base + tot, (uint32_t)C);
+    constexpr int U = 8;
+    for (uint32_t q0 = pos_base + threadIdx.x; q0 < qend; q0 += NT * U) {
+      int lo[U], hi[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // slot q lies between the anchors of its 64-slot block and of the next one
+        const uint32_t k = (q0 + u * NT - pos_base) >> 6;
+        const bool in = q0 + u * NT < qend;
+        lo[u] = in ? (int)anchor[k] : 0;
+        hi[u] = in && pos_base + (k + 1) * 64 < pos_base + tot ? (int)anchor[k + 1] : nwr - 1;
+        hi[u] = in ? hi[u] : 0;
+      }
+      // the last word whose first position is <= q holds slot q (it cannot be empty:
+      // the next word's first position is above q)
+#pragma unroll 1
+      for (int step = 0; step < 13; ++step) {
+        bool open = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) open |= lo[u] < hi[u];
+        if (!__ballot(open)) break;
+        uint32_t pm[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) pm[u] = wpos[(lo[u] + hi[u] + 1) >> 1];  // all reads of the step together
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int mid = (lo[u] + hi[u] + 1) >> 1;  // == lo once lo == hi: no change then
+          const bool le = pm[u] <= q0 + u * NT;
+          lo[u] = le ? mid : lo[u];
+          hi[u] = le ? hi[u] : mid - 1;
+        }
+      }
+      int32_t idx[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t m = wmask[lo[u]];
+        uint32_t kk = q0 + u * NT - wpos[lo[u]];  // the slot's rank among the word's set bits
+        // select the kk-th set bit: halve the word five times, then the last pair
+        uint32_t x = (uint32_t)m, base = 0;
+        uint32_t c = (uint32_t)__builtin_popcount(x);
+        const bool up = kk >= c;
+        kk = up ? kk - c : kk;
+        x = up ? (uint32_t)(m >> 32) : x;
+        base = up ? 32u : 0u;
+#pragma unroll
+        for (int sh = 16; sh >= 1; sh >>= 1) {
+          c = (uint32_t)__builtin_popcount(x & ((1u << sh) - 1u));
+          const bool hi2 = kk >= c;
+          kk = hi2 ? kk - c : kk;
+          x = hi2 ? x >> sh : x;
+          base += hi2 ? (uint32_t)sh : 0u;
+        }
+        idx[u] = (int32_t)(((r0 + lo[u]) << 6) + base);
+      }
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = (outs && q0 + u * NT < qend) ? sc[idx[u]] : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t q = q0 + u * NT;
+        if (q < qend) {
+          out[q] = idx[u];
+          if (outs) outs[q] = v[u];
+        }
       }
     }
-  }
-  __syncthreads();
-  constexpr int U = 4;
-  for (int p0 = 0; p0 < C; p0 += NT * U) {
-    int32_t j[U];
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = p0 + u * NT + threadIdx.x;
-      j[u] = p < C ? picks[p] : 0;
-      v[u] = (outs && p < C) ? sc[j[u]] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = p0 + u * NT + threadIdx.x;
-      if (p < C) {
-        out[p] = j[u];
-        if (outs) outs[p] = v[u];
-      }
-    }
+    pos_base += tot;
+    __syncthreads();  // the next round rewrites the word masks
   }
 }
 
@@ -881,7 +936,8 @@ hipError_t launch_topc_lds(const Shape& s, const SelectWs& ws, int32_t* cand, fl
 
 hipError_t launch_emit_candidates(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score,
                                   hipStream_t st) {
-  const size_t smem = (size_t)s.C * sizeof(int32_t);
+  // word masks and positions, and one anchor per 64 slots (a round has at most 4096 * 64 slots)
+  const size_t smem = (size_t)1024 * 4 * (sizeof(uint64_t) + sizeof(uint32_t)) + (size_t)(4096 + 1) * sizeof(uint32_t);
   hipError_t e = allow_smem((const void*)emit_kernel, smem);
   if (e != hipSuccess) return e;
   klaunch(emit_kernel, dim3(s.Hkv, s.nseq), 1024, smem, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.nwords,
