@@ -428,12 +428,22 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
       xs[rp][kk] = x0;
       xs[rp + 1][kk] = x1;
     }
-    for (int i = threadIdx.x; i < D * KC; i += 256) {
-      const int e = i / KC, kk = i % KC, key = k0 + kk;
-      float v = 0.f;
-      if (kk < n)
-        v = key < topk ? v_sel[(unit * D + e) * ldv + key] : vb[(((int64_t)s * B + (key - topk)) * Hkv + g) * D + e];
-      vs[e * (KC + 1) + kk] = v;
+    {
+      constexpr int NV = D * KC / 256;  // values per thread: all loads first, then the LDS stores
+      float vv[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int i = threadIdx.x + u * 256, e = i / KC, kk = i % KC, key = k0 + kk;
+        vv[u] = 0.f;
+        if (kk < n)
+          vv[u] = key < topk ? v_sel[(unit * D + e) * ldv + key]
+                             : vb[(((int64_t)s * B + (key - topk)) * Hkv + g) * D + e];
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int i = threadIdx.x + u * 256;
+        vs[(i / KC) * (KC + 1) + i % KC] = vv[u];
+      }
     }
     __syncthreads();
     const float x0 = xs[w][lane], x1 = xs[w][lane + 64];

@@ -317,6 +317,32 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
   }
 }
 
+// fp32 path: candidate key rows of one kRefineTileF32 tile into LDS (row stride LD
+// floats), 256 threads: every candidate index is loaded first, then every row chunk,
+// then the LDS stores, so the loads overlap instead of waiting one by one.
+template <int D, int LD>
+__device__ __forceinline__ void stage_rows_f32(const float* __restrict__ k, const int32_t* __restrict__ cd,
+                                               int64_t j0, int Hkv, int g, int C, int tile, float* dst) {
+  constexpr int NI = kRefineTileF32 * D / 4 / 256;  // 16-byte chunks per thread
+  int32_t idx[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int row = (threadIdx.x + u * 256) / (D / 4);
+    idx[u] = cd[min(tile * kRefineTileF32 + row, C - 1)];
+  }
+  float4 v[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int ch = (threadIdx.x + u * 256) % (D / 4);
+    v[u] = *reinterpret_cast<const float4*>(k + ((j0 + idx[u]) * Hkv + g) * D + 4 * ch);
+  }
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int i = threadIdx.x + u * 256;
+    *reinterpret_cast<float4*>(dst + (i / (D / 4)) * LD + 4 * (i % (D / 4))) = v[u];
+  }
+}
+
 // fp32 path: the same three steps on VALU (stats and scores over kRefineTileF32-candidate
 // tiles, then refine_select_kernel). A logit is one fma chain over the head dimension
 // in index order; fma is symmetric in its two factors, so the two kernels, which read
@@ -389,12 +415,7 @@ __global__ __launch_bounds__(256) void refine_stats_f32_kernel(const float* __re
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t j0 = seq_start[s];
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  for (int i = threadIdx.x; i < kRefineTileF32 * D / 4; i += 256) {
-    const int row = i / (D / 4), ch = i % (D / 4);
-    const int c = min(tile * kRefineTileF32 + row, C - 1);
-    *reinterpret_cast<float4*>(ks + row * D + 4 * ch) =
-        *reinterpret_cast<const float4*>(k + ((j0 + cd[c]) * Hkv + g) * D + 4 * ch);
-  }
+  stage_rows_f32<D, D>(k, cd, j0, Hkv, g, C, tile, ks);
   __syncthreads();
   const int nvalid = min(kRefineTileF32, C - tile * kRefineTileF32);
   for (int r0 = 0; r0 < R; r0 += 64) {
@@ -455,18 +476,16 @@ __global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __r
   const int ci = (w & 1) * 64 + lane, half = w >> 1;
   const int64_t j0 = seq_start[s];
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  for (int i = threadIdx.x; i < kRefineTileF32 * D / 4; i += 256) {
-    const int row = i / (D / 4), ch = i % (D / 4);
-    const int c = min(tile * kRefineTileF32 + row, C - 1);
-    *reinterpret_cast<float4*>(kt + row * KP + 4 * ch) =
-        *reinterpret_cast<const float4*>(k + ((j0 + cd[c]) * Hkv + g) * D + 4 * ch);
-  }
+  stage_rows_f32<D, KP>(k, cd, j0, Hkv, g, C, tile, kt);
   for (int r = threadIdx.x; r < R; r += 256) {
     const float2* st = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);
     float M = -INFINITY, Z = 0.f;
-    for (int t = 0; t < ntile; ++t) {
-      const float2 p = st[t];
-      ms_merge(M, Z, p.x, p.y);
+    for (int t0 = 0; t0 < ntile; t0 += 8) {  // eight tile statistics in flight, merged in tile order
+      float2 p[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[u] = t0 + u < ntile ? st[t0 + u] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ms_merge(M, Z, p[u].x, p[u].y);
     }
     rowM[r] = M;
     rowIZ[r] = 1.f / Z;
@@ -474,11 +493,20 @@ __global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __r
   float acc = 0.f;
   for (int r0 = 0; r0 < R; r0 += 64) {
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * D / 4; i += 256) {
-      const int rr = i / (D / 4), ch = i % (D / 4);
-      const int rq = min(r0 + rr, R - 1);
-      *reinterpret_cast<float4*>(qs + rr * D + 4 * ch) =
-          *reinterpret_cast<const float4*>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + 4 * ch);
+    {
+      constexpr int NQ = 64 * D / 4 / 256;  // 16-byte chunks per thread, all loads first
+      float4 qv[NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int i = threadIdx.x + u * 256, rr = i / (D / 4), ch = i % (D / 4);
+        const int rq = min(r0 + rr, R - 1);
+        qv[u] = *reinterpret_cast<const float4*>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + 4 * ch);
+      }
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int i = threadIdx.x + u * 256;
+        *reinterpret_cast<float4*>(qs + (i / (D / 4)) * D + 4 * (i % (D / 4))) = qv[u];
+      }
     }
     __syncthreads();
     const int rb = half * 32;
