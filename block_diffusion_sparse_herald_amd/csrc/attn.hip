@@ -495,9 +495,12 @@ AttnGeom attn_geom(const Shape& s) {
   // Four query tiles per workgroup; two when few (sequence, KV head) pairs leave the
   // chip idle even with the keys split: twice the workgroups (each pulling the same
   // keys for fewer rows), a larger target for the key split and ranges of 3 blocks.
+  // Long subsets (more than kAttnBlocksPerRange blocks, e.g. attention over a whole
+  // cache) fill the chip through the key split alone and keep four tiles, so the keys
+  // are streamed for half as many row groups.
   a.tpw = std::min(ntiles, 4);
   int target = kAttnTargetWorkgroups, minrange = kAttnMaxStages;
-  if (a.nunits * ((ntiles + 3) / 4) * 5 < kAttnTargetWorkgroups) {
+  if (a.nunits * ((ntiles + 3) / 4) * 5 < kAttnTargetWorkgroups && nblk <= kAttnBlocksPerRange) {
     a.tpw = std::min(ntiles, 2);
     target = kAttnTargetWorkgroupsFew;
     minrange = 3;
