@@ -23,6 +23,8 @@ import json
 import os
 from collections import defaultdict
 
+MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "block_diffusion_sparse_herald_amd", "csrc")
 
@@ -97,19 +99,57 @@ def per_launch_kib(per, prefixes) -> float:
     return total
 
 
+def mfma_summary(workload: str, pmc_dir: str, stats_dir: str, out_dir: str, cmd: str) -> str:
+    """profiles/mfma_util_<workload>.md from a `rocprofv3 --pmc MfmaUtil MfmaFlopsBF16` run:
+    per kernel the mean MFMA busy share of the dispatch (rocprof's MfmaUtil: MFMA busy
+    cycles over active cycles of all SIMDs), the bf16 MFMA flops it issued, and those flops
+    over the kernel's mean duration in the kernel-trace run of the same workload."""
+    vals = defaultdict(lambda: defaultdict(list))
+    with open(_one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))) as fh:
+        for r in csv.DictReader(fh):
+            vals[short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    dur = {n: avg for n, _, avg, _, _, _ in kernel_stats(stats_dir)}
+    md = [f"# MFMA utilisation, workload {workload}", "",
+          "rocprofv3 counters per dispatch (eager launches); duration from the kernel-trace run of the same",
+          f"workload (`kernel_stats_{workload}.md`); bf16 dense MFMA peak {MFMA_PEAK_TFLOPS} TFLOP/s.", "",
+          "Command:", "", "```", cmd, "```", "",
+          "| kernel | dispatches | MfmaUtil % | bf16 MFMA GFLOP per dispatch | mean us | MFMA TFLOP/s | % of peak |",
+          "|---|---|---|---|---|---|---|"]
+    for name in sorted(vals, key=lambda n: -sum(vals[n].get("MfmaFlopsBF16", [0.0]))):
+        fl = vals[name].get("MfmaFlopsBF16", [])
+        ut = vals[name].get("MfmaUtil", [])
+        if not fl or sum(fl) == 0.0:
+            continue
+        gf = sum(fl) / len(fl) / 1e9
+        us = dur.get(name)
+        tf = gf / us * 1e3 if us else float("nan")  # GFLOP per us -> TFLOP/s
+        md.append(f"| `{name}` | {len(fl)} | {sum(ut) / len(ut):.1f} | {gf:.3f} | "
+                  f"{us if us else float('nan'):.2f} | {tf:.1f} | {100.0 * tf / MFMA_PEAK_TFLOPS:.1f} |")
+    path = os.path.join(out_dir, f"mfma_util_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    return path
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", required=True)
     ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-bytes", type=int, required=True)
+    ap.add_argument("--fetch", default="")
+    ap.add_argument("--write", default="")
+    ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--calibration-from", default="",
                     help="take the copy factors from another workload's JSON (for runs without replica copies)")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--stats-cmd", default="")
     ap.add_argument("--pmc-cmd", default="")
+    ap.add_argument("--mfma", default="", help="directory of a `--pmc MfmaUtil MfmaFlopsBF16` run: write only "
+                                                "profiles/mfma_util_<workload>.md")
+    ap.add_argument("--mfma-cmd", default="")
     args = ap.parse_args(argv)
+    if args.mfma:
+        print(mfma_summary(args.workload, args.mfma, args.stats, args.out_dir, args.mfma_cmd))
+        return 0
     os.makedirs(args.out_dir, exist_ok=True)
 
     stats = kernel_stats(args.stats)
