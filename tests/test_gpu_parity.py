@@ -61,6 +61,10 @@ SMALL = {
                              C=700, topk=100, T=1, planted=8, seed_base=8100),
     "lds_scan_g8": Workload("lds_scan_g8", nseq=2, L=131100, Hq=64, Hkv=8, d=128, dtype="bf16", B=2, C=600,
                             topk=64, T=1, planted=8, seed_base=8200),
+    # a sequence of more than 4096 bitmap words (262144 tokens): the radix emission runs
+    # two rounds, the largest candidate set spreads picks over both
+    "radix_two_rounds": Workload("radix_two_rounds", nseq=1, L=300000, Hq=4, Hkv=1, d=64, dtype="bf16", B=4,
+                                 C=16384, topk=2000, T=1, planted=8, seed_base=8400),
     # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
     "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
                            T=2, seed_base=7800),
