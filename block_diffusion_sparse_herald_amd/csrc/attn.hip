@@ -76,9 +76,11 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   const int per = gridDim.x >> 3;
   const int li = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (li >= a.nitems) return;
-  const int rs = li % a.nrs, ksp = (li / a.nrs) % a.nks, unit = li / (a.nrs * a.nks);
+  auto qdiv = [](uint32_t x, uint32_t rcp) { return rcp ? __umulhi(x, rcp) : x; };  // x / d, rcp as in AttnGeom
+  const int q1 = (int)qdiv((uint32_t)li, a.rcp_nrs), q2 = (int)qdiv((uint32_t)q1, a.rcp_nks);
+  const int rs = li - q1 * a.nrs, ksp = q1 - q2 * a.nks, unit = q2;
   const int B = a.B, G = a.G, topk = a.topk;
-  const int s = unit / a.Hkv, g = unit % a.Hkv;
+  const int s = (int)qdiv((uint32_t)unit, a.rcp_hkv), g = unit - s * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, qd = lane >> 4, lr = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = w >> 2, wl = w & 3;
@@ -520,6 +522,14 @@ AttnGeom attn_geom(const Shape& s) {
   // through kAttnMaxStages stages (two blocks in use, the next two in flight)
   a.nst = std::min(a.bps, kAttnMaxStages);
   a.nitems = a.nunits * a.nrs * a.nks;
+  auto rcp = [&](int d) -> uint32_t {
+    if (d <= 1) return 0u;
+    if ((uint64_t)a.nitems * (uint64_t)d >= (1ull << 32)) return 0xffffffffu;  // flagged below
+    return (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d);
+  };
+  a.rcp_nrs = rcp(a.nrs);
+  a.rcp_nks = rcp(a.nks);
+  a.rcp_hkv = rcp(a.Hkv);
   return a;
 }
 
@@ -551,6 +561,9 @@ static hipError_t launch_attn_bf16(const AttnGeom& a, const void* q, const void*
     o_part = static_cast<bf16*>(ws);
     ml_part = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(rows * D * sizeof(bf16)));
   }
+  // more workgroups than the reciprocal decode covers exactly (over 2^32 / 64)
+  if (a.rcp_nrs == 0xffffffffu || a.rcp_nks == 0xffffffffu || a.rcp_hkv == 0xffffffffu)
+    return hipErrorInvalidConfiguration;
   const size_t smem = attn_smem<D>(a);
   hipError_t e = allow_smem((const void*)attn_kernel<D>, smem);
   if (e != hipSuccess) return e;

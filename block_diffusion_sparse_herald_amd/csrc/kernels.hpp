@@ -72,6 +72,10 @@ struct AttnGeom {
   int bps;     // 64-key blocks per key range
   int nst;     // LDS stages (blocks in flight) per workgroup
   int nitems;  // workgroups
+  // multiply-high reciprocals of nrs, nks and Hkv (ceil(2^32 / d), 0 for d = 1): the
+  // kernel decodes its workgroup with one s_mul_hi_u32 per division; exact because
+  // every quotient taken is below nitems and nitems * d < 2^32 (checked by attn_geom)
+  uint32_t rcp_nrs, rcp_nks, rcp_hkv;
 };
 constexpr int kAttnBlocksPerRange = 32;
 constexpr int kAttnTargetWorkgroups = 96;
