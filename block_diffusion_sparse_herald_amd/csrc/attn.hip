@@ -133,9 +133,9 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   // ---- query fragments of this wave's tile
   uint4 qf[KS];
   {
-    const int r = tile * 16 + lr;
+    const int r = tile * 16 + lr, rb = (int)qdiv((uint32_t)r, a.rcp_g);  // block query of row r
     const bf16* qr =
-        has_tile && r < R ? q + (((int64_t)s * B + r / G) * a.Hq + g * G + r % G) * D + qd * 8 : nullptr;
+        has_tile && r < R ? q + (((int64_t)s * B + rb) * a.Hq + g * G + (r - rb * G)) * D + qd * 8 : nullptr;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = qr ? ld16(qr + ks * 32) : make_uint4(0, 0, 0, 0);
   }
@@ -306,7 +306,8 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   const int r = tile * 16 + lr;
   if (a.nks == 1) {
     if (r >= R) return;
-    bf16* orow = out + (((int64_t)s * B + r / G) * a.Hq + g * G + r % G) * D + qd * 4;
+    const int rb = (int)qdiv((uint32_t)r, a.rcp_g);
+    bf16* orow = out + (((int64_t)s * B + rb) * a.Hq + g * G + (r - rb * G)) * D + qd * 4;
     const float inv = 1.f / l;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -333,10 +334,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict
   const int idx = blockIdx.x * 64 + threadIdx.x;
   const int R = a.B * a.G;
   const int per_unit = R * (D / 4);
-  const int unit = idx / per_unit;
+  const int unit = a.rcp_pu ? (int)__umulhi((uint32_t)idx, a.rcp_pu) : idx / per_unit;
   if (unit >= a.nunits) return;
-  const int r = (idx % per_unit) / (D / 4), e = (idx % (D / 4)) * 4;
-  const int s = unit / a.Hkv, g = unit % a.Hkv;
+  const int r = (idx - unit * per_unit) / (D / 4), e = (idx % (D / 4)) * 4;
+  const int s = a.rcp_hkv ? (int)__umulhi((uint32_t)unit, a.rcp_hkv) : unit, g = unit - s * a.Hkv;
   const int64_t base = (int64_t)unit * a.nks * a.rpad + r;
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -375,7 +376,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict
     M = mc;
   }
   const float inv = 1.f / L;
-  *reinterpret_cast<uint2*>(out + (((int64_t)s * a.B + r / a.G) * a.Hq + g * a.G + r % a.G) * D + e) =
+  const int rb = a.rcp_g ? (int)__umulhi((uint32_t)r, a.rcp_g) : r;  // block query of row r
+  *reinterpret_cast<uint2*>(out + (((int64_t)s * a.B + rb) * a.Hq + g * a.G + (r - rb * a.G)) * D + e) =
       make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
@@ -530,6 +532,9 @@ AttnGeom attn_geom(const Shape& s) {
   a.rcp_nrs = rcp(a.nrs);
   a.rcp_nks = rcp(a.nks);
   a.rcp_hkv = rcp(a.Hkv);
+  a.rcp_g = a.G <= 1 ? 0u : (uint32_t)(((1ull << 32) + (uint64_t)a.G - 1) / (uint64_t)a.G);
+  const uint64_t pu = (uint64_t)s.B * s.G * (s.D / 4), nidx = (uint64_t)a.nunits * pu;
+  a.rcp_pu = nidx * pu < (1ull << 32) ? (uint32_t)(((1ull << 32) + pu - 1) / pu) : 0u;
   return a;
 }
 

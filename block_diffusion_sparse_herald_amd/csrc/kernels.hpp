@@ -76,6 +76,9 @@ struct AttnGeom {
   // kernel decodes its workgroup with one s_mul_hi_u32 per division; exact because
   // every quotient taken is below nitems and nitems * d < 2^32 (checked by attn_geom)
   uint32_t rcp_nrs, rcp_nks, rcp_hkv;
+  uint32_t rcp_g;   // ceil(2^32 / G), 0 for G = 1 (exact: query rows r < 2^16)
+  uint32_t rcp_pu;  // ceil(2^32 / (B * G * D / 4)) for the range merge's thread index, 0 when that is
+                    // not exact for every index (the merge then divides)
 };
 constexpr int kAttnBlocksPerRange = 32;
 constexpr int kAttnTargetWorkgroups = 96;
