@@ -28,6 +28,7 @@ constexpr int kTopcLdsMaxLen = 36864;
 // Candidates one refine workgroup covers (bf16 MFMA path: 64 per wave; fp32 path).
 constexpr int kRefineTile = 256;
 constexpr int kRefineTileF32 = 128;
+constexpr int kRefineScoreTileF32 = 64;  // candidates per fp32 score workgroup (one per lane)
 // Keys per attention block and the largest supported candidate count.
 constexpr int kAttnKeyBlock = 64;
 constexpr int kMaxCandidates = 16384;

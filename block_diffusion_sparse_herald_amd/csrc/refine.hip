@@ -317,34 +317,35 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
   }
 }
 
-// fp32 path: candidate key rows of one kRefineTileF32 tile into LDS (row stride LD
-// floats), 256 threads: every candidate index is loaded first, then every row chunk,
+// fp32 path: candidate key rows of one TILE-candidate tile into LDS (row stride LD
+// floats), NT threads: every candidate index is loaded first, then every row chunk,
 // then the LDS stores, so the loads overlap instead of waiting one by one.
-template <int D, int LD>
+template <int D, int LD, int NT, int TILE>
 __device__ __forceinline__ void stage_rows_f32(const float* __restrict__ k, const int32_t* __restrict__ cd,
                                                int64_t j0, int Hkv, int g, int C, int tile, float* dst) {
-  constexpr int NI = kRefineTileF32 * D / 4 / 256;  // 16-byte chunks per thread
+  constexpr int NI = TILE * D / 4 / NT;  // 16-byte chunks per thread
+  static_assert(NI * NT == TILE * D / 4, "whole chunks per thread");
   int32_t idx[NI];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
-    const int row = (threadIdx.x + u * 256) / (D / 4);
-    idx[u] = cd[min(tile * kRefineTileF32 + row, C - 1)];
+    const int row = (threadIdx.x + u * NT) / (D / 4);
+    idx[u] = cd[min(tile * TILE + row, C - 1)];
   }
   float4 v[NI];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
-    const int ch = (threadIdx.x + u * 256) % (D / 4);
+    const int ch = (threadIdx.x + u * NT) % (D / 4);
     v[u] = *reinterpret_cast<const float4*>(k + ((j0 + idx[u]) * Hkv + g) * D + 4 * ch);
   }
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
-    const int i = threadIdx.x + u * 256;
+    const int i = threadIdx.x + u * NT;
     *reinterpret_cast<float4*>(dst + (i / (D / 4)) * LD + 4 * (i % (D / 4))) = v[u];
   }
 }
 
-// fp32 path: the same three steps on VALU (stats and scores over kRefineTileF32-candidate
-// tiles, then refine_select_kernel). A logit is one fma chain over the head dimension
+// fp32 path: the same three steps on VALU (stats over kRefineTileF32-candidate tiles,
+// scores over kRefineScoreTileF32-candidate tiles, then refine_select_kernel). A logit is one fma chain over the head dimension
 // in index order; fma is symmetric in its two factors, so the two kernels, which read
 // the operands from different places, compute the same bits.
 template <int D>
@@ -396,35 +397,38 @@ __device__ __forceinline__ void load_row_f32(const float* __restrict__ src, floa
   }
 }
 
-// Per (query row, tile): (max, sum 2^(x-max)) over the tile's candidates. Lanes are
-// query rows (64 per pass, the row in registers); wave w takes candidates
-// 32w .. 32w+31 of the tile from LDS (broadcast reads); the four waves' pairs are
-// merged in wave order.
+// Per (query row, tile): (max, sum 2^(x-max)) over the tile's candidates. A workgroup
+// takes one tile and 64 query rows (blockIdx.x = pass * ntile + tile); lanes are query
+// rows (the row in registers); wave w of NW takes candidates w * CPW .. +CPW-1 of the
+// tile from LDS (broadcast reads); the waves' pairs are merged in wave order. Eight
+// waves at D = 64; four at D = 128, whose 128-float query row needs the register budget
+// of one wave per SIMD.
 template <int D>
-__global__ __launch_bounds__(256) void refine_stats_f32_kernel(const float* __restrict__ q,
+__global__ __launch_bounds__(D == 128 ? 256 : 512) void refine_stats_f32_kernel(const float* __restrict__ q,
                                                                const float* __restrict__ k,
                                                                const int32_t* __restrict__ cand,
                                                                const int64_t* __restrict__ seq_start, int B, int Hq,
                                                                int Hkv, int G, int C, float scale2, int ntile,
                                                                float2* __restrict__ row_stats) {
-  static_assert(kRefineTileF32 == 128, "four waves of 32 candidates");
+  constexpr int NW = D == 128 ? 4 : 8, CPW = kRefineTileF32 / NW;
+  static_assert(CPW % 4 == 0, "whole groups of four candidates per wave");
   extern __shared__ __align__(16) float ks[];  // [kRefineTileF32][D]
-  __shared__ float2 wstat[4][64];
-  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  __shared__ float2 wstat[NW][64];
+  const int tile = blockIdx.x % ntile, r0 = blockIdx.x / ntile * 64, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t j0 = seq_start[s];
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  stage_rows_f32<D, D>(k, cd, j0, Hkv, g, C, tile, ks);
+  const int r = r0 + lane, rq = min(r, R - 1);
+  float qr[D];
+  load_row_f32<D>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D, qr);
+  stage_rows_f32<D, D, NW * 64, kRefineTileF32>(k, cd, j0, Hkv, g, C, tile, ks);
   __syncthreads();
   const int nvalid = min(kRefineTileF32, C - tile * kRefineTileF32);
-  for (int r0 = 0; r0 < R; r0 += 64) {
-    const int r = r0 + lane, rq = min(r, R - 1);
-    float qr[D];
-    load_row_f32<D>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D, qr);
+  {
     float m = -INFINITY, l = 0.f;
 #pragma unroll 1
-    for (int c0 = w * 32; c0 < w * 32 + 32; c0 += 4) {
+    for (int c0 = w * CPW; c0 < w * CPW + CPW; c0 += 4) {
       float d[4];
       dot4_f32<D>(qr, ks + c0 * D, ks + (c0 + 1) * D, ks + (c0 + 2) * D, ks + (c0 + 3) * D, d);
       float x[4], mg = -INFINITY;
@@ -440,44 +444,44 @@ __global__ __launch_bounds__(256) void refine_stats_f32_kernel(const float* __re
       ms_merge(m, l, mg, lg);
     }
     wstat[w][lane] = make_float2(m, l);
-    __syncthreads();
-    if (threadIdx.x < 64 && r < R) {
-      float M = -INFINITY, Z = 0.f;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64 && r < R) {
+    float M = -INFINITY, Z = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) ms_merge(M, Z, wstat[ww][lane].x, wstat[ww][lane].y);
-      row_stats[(((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1) + tile] = make_float2(M, Z);
-    }
-    __syncthreads();
+    for (int ww = 0; ww < NW; ++ww) ms_merge(M, Z, wstat[ww][lane].x, wstat[ww][lane].y);
+    row_stats[(((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1) + tile] = make_float2(M, Z);
   }
 }
 
-// Per candidate: sum over query rows of 2^(x - M_row) / Z_row. Lanes are candidates
-// (key rows in LDS, padded by four words so that 16 lanes' 16-byte reads cover all
-// banks): waves 0/1 take candidates 0..63 / 64..127 of the tile over the first half
-// of every 64-row pass, waves 2/3 over the second half; the halves are added at the
-// end.
+// Per candidate: sum over query rows of 2^(x - M_row) / Z_row (M_row, Z_row merged over
+// all statistics tiles). A workgroup takes kRefineScoreTileF32 = 64 candidates; lanes
+// are candidates (key rows in LDS, padded by four words so that 16 lanes' 16-byte reads
+// cover all banks); of the eight waves, wave w takes rows 8w .. 8w+7 of every 64-row
+// pass; the eight waves' sums are added in wave order at the end.
 template <int D>
-__global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __restrict__ q,
+__global__ __launch_bounds__(512) void refine_scores_f32_kernel(const float* __restrict__ q,
                                                                 const float* __restrict__ k,
                                                                 const int32_t* __restrict__ cand,
                                                                 const int64_t* __restrict__ seq_start, int B,
                                                                 int Hq, int Hkv, int G, int C, float scale2, int ntile,
                                                                 const float2* __restrict__ row_stats,
                                                                 float* __restrict__ rscore) {
-  constexpr int KP = D + 4;
-  extern __shared__ __align__(16) float qs[];  // [64][D], [kRefineTileF32][KP], rowM[R], rowIZ[R]
-  __shared__ float part[2][kRefineTileF32];
+  constexpr int KP = D + 4, TS = kRefineScoreTileF32;
+  static_assert(TS == 64, "one candidate per lane");
+  extern __shared__ __align__(16) float qs[];  // [64][D], [TS][KP], rowM[R], rowIZ[R]
+  __shared__ float part[8][TS];
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G;
   float* kt = qs + 64 * D;
-  float* rowM = kt + kRefineTileF32 * KP;
+  float* rowM = kt + TS * KP;
   float* rowIZ = rowM + R;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int ci = (w & 1) * 64 + lane, half = w >> 1;
+  const int ci = lane;
   const int64_t j0 = seq_start[s];
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  stage_rows_f32<D, KP>(k, cd, j0, Hkv, g, C, tile, kt);
-  for (int r = threadIdx.x; r < R; r += 256) {
+  stage_rows_f32<D, KP, 512, TS>(k, cd, j0, Hkv, g, C, tile, kt);
+  for (int r = threadIdx.x; r < R; r += 512) {
     const float2* st = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);
     float M = -INFINITY, Z = 0.f;
     for (int t0 = 0; t0 < ntile; t0 += 8) {  // eight tile statistics in flight, merged in tile order
@@ -494,24 +498,24 @@ __global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __r
   for (int r0 = 0; r0 < R; r0 += 64) {
     __syncthreads();
     {
-      constexpr int NQ = 64 * D / 4 / 256;  // 16-byte chunks per thread, all loads first
+      constexpr int NQ = 64 * D / 4 / 512;  // 16-byte chunks per thread, all loads first
       float4 qv[NQ];
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        const int i = threadIdx.x + u * 256, rr = i / (D / 4), ch = i % (D / 4);
+        const int i = threadIdx.x + u * 512, rr = i / (D / 4), ch = i % (D / 4);
         const int rq = min(r0 + rr, R - 1);
         qv[u] = *reinterpret_cast<const float4*>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + 4 * ch);
       }
 #pragma unroll
       for (int u = 0; u < NQ; ++u) {
-        const int i = threadIdx.x + u * 256;
+        const int i = threadIdx.x + u * 512;
         *reinterpret_cast<float4*>(qs + (i / (D / 4)) * D + 4 * (i % (D / 4))) = qv[u];
       }
     }
     __syncthreads();
-    const int rb = half * 32;
-#pragma unroll 1
-    for (int j = rb; j < rb + 32; j += 4) {
+    const int rb = w * 8;
+#pragma unroll
+    for (int j = rb; j < rb + 8; j += 4) {
       float d[4];
       dot4_lds_f32<D>(kt + ci * KP, qs + j * D, qs + (j + 1) * D, qs + (j + 2) * D, qs + (j + 3) * D, d);
 #pragma unroll
@@ -521,11 +525,16 @@ __global__ __launch_bounds__(256) void refine_scores_f32_kernel(const float* __r
       }
     }
   }
-  part[half][ci] = acc;
+  part[w][ci] = acc;
   __syncthreads();
-  if (threadIdx.x < kRefineTileF32) {
-    const int cc = tile * kRefineTileF32 + threadIdx.x;
-    if (cc < C) rscore[((int64_t)s * Hkv + g) * C + cc] = part[0][threadIdx.x] + part[1][threadIdx.x];
+  if (threadIdx.x < TS) {
+    const int cc = tile * TS + threadIdx.x;
+    if (cc < C) {
+      float sum = part[0][threadIdx.x];
+#pragma unroll
+      for (int ww = 1; ww < 8; ++ww) sum += part[ww][threadIdx.x];
+      rscore[((int64_t)s * Hkv + g) * C + cc] = sum;
+    }
   }
 }
 
@@ -590,10 +599,12 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
 
 hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
                              bool stats, hipStream_t st) {
-  dim3 grid(ws.ntile, s.Hkv, s.nseq);
+  // stats: one workgroup per (tile, 64-row pass); scores: one per 64-candidate tile, over all rows
+  const int npass = (s.B * s.G + 63) / 64;
+  const dim3 grid(stats ? ws.ntile * npass : (s.C + kRefineScoreTileF32 - 1) / kRefineScoreTileF32, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
   const size_t smem = stats ? (size_t)kRefineTileF32 * s.D * sizeof(float)
-                            : ((size_t)64 * s.D + (size_t)kRefineTileF32 * (s.D + 4) + 2 * (size_t)s.B * s.G) *
+                            : ((size_t)64 * s.D + (size_t)kRefineScoreTileF32 * (s.D + 4) + 2 * (size_t)s.B * s.G) *
                                   sizeof(float);
   const void* kern = stats ? (s.D == 128 ? (const void*)refine_stats_f32_kernel<128>
                                          : (const void*)refine_stats_f32_kernel<64>)
@@ -608,14 +619,14 @@ hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const
       klaunch(refine_stats_f32_kernel<128>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
                                                              s.C, scale2, ws.ntile, ws.row_stats);
     else
-      klaunch(refine_stats_f32_kernel<64>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
+      klaunch(refine_stats_f32_kernel<64>, grid, 512, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
                                                             s.C, scale2, ws.ntile, ws.row_stats);
   } else {
     if (s.D == 128)
-      klaunch(refine_scores_f32_kernel<128>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
+      klaunch(refine_scores_f32_kernel<128>, grid, 512, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
                                                               s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
     else
-      klaunch(refine_scores_f32_kernel<64>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
+      klaunch(refine_scores_f32_kernel<64>, grid, 512, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
                                                              s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
   }
   return hipGetLastError();
