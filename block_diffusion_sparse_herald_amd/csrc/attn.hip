@@ -504,7 +504,7 @@ AttnGeom attn_geom(const Shape& s) {
   // are streamed for half as many row groups.
   a.tpw = std::min(ntiles, 4);
   int target = kAttnTargetWorkgroups, minrange = kAttnMaxStages;
-  if (a.nunits * ((ntiles + 3) / 4) * 5 < kAttnTargetWorkgroups && nblk <= kAttnBlocksPerRange) {
+  if (a.nunits * ((ntiles + 3) / 4) * 5 < kAttnFewPairs && nblk <= kAttnBlocksPerRange) {
     a.tpw = std::min(ntiles, 2);
     target = kAttnTargetWorkgroupsFew;
     minrange = 3;

@@ -82,7 +82,8 @@ struct AttnGeom {
                     // not exact for every index (the merge then divides)
 };
 constexpr int kAttnBlocksPerRange = 32;
-constexpr int kAttnTargetWorkgroups = 96;
+constexpr int kAttnTargetWorkgroups = 256;  // one per compute unit
+constexpr int kAttnFewPairs = 96;  // below this (pairs x four-tile row groups x 5) the few-pairs geometry applies
 constexpr int kAttnTargetWorkgroupsFew = 192;  // with two query tiles per workgroup
 constexpr int kAttnMaxStages = 4;
 

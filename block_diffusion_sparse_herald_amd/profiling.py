@@ -9,8 +9,9 @@ FETCH_SIZE pass; one WRITE_SIZE pass), and writes
   profiles/hbm_traffic_<W>.json  HBM bytes per launch of the profiled kernels.
 The counters read in KiB per dispatch; each is scaled by what it reads for a copy of
 known size (the benchmark's K/V replica copies, `--copy-bytes` each), so the figures
-are bytes as the copy defines them. The JSON records a digest of the kernel sources;
-bench.py reports the traffic only while the sources are unchanged.
+are bytes as the copy defines them. The JSON records a digest of the kernel sources
+(with the header that fixes the launch geometry); bench.py reports the traffic only
+while they are unchanged.
 """
 
 from __future__ import annotations
@@ -30,12 +31,12 @@ CSRC = os.path.join(ROOT, "block_diffusion_sparse_herald_amd", "csrc")
 
 # profiled kernel (as the benchmark names it) -> (kernel name prefixes, source files)
 KERNELS = {
-    "attn_kernel+attn_combine_kernel": (["herald::attn_kernel", "herald::attn_combine_kernel"], ["attn.hip", "common.hpp"]),
-    "attn_kernel": (["herald::attn_kernel"], ["attn.hip", "common.hpp"]),
-    "scan": (["herald::scan_"], ["select.hip", "common.hpp"]),  # whichever scan kernel the workload uses
-    "refine_stats": (["herald::refine_stats_kernel"], ["refine.hip", "common.hpp"]),
-    "refine_scores": (["herald::refine_scores_kernel"], ["refine.hip", "common.hpp"]),
-    "gather": (["herald::gather_kernel"], ["gather.hip", "common.hpp"]),
+    "attn_kernel+attn_combine_kernel": (["herald::attn_kernel", "herald::attn_combine_kernel"], ["attn.hip", "common.hpp", "kernels.hpp"]),
+    "attn_kernel": (["herald::attn_kernel"], ["attn.hip", "common.hpp", "kernels.hpp"]),
+    "scan": (["herald::scan_"], ["select.hip", "common.hpp", "kernels.hpp"]),  # whichever scan kernel the workload uses
+    "refine_stats": (["herald::refine_stats_kernel"], ["refine.hip", "common.hpp", "kernels.hpp"]),
+    "refine_scores": (["herald::refine_scores_kernel"], ["refine.hip", "common.hpp", "kernels.hpp"]),
+    "gather": (["herald::gather_kernel"], ["gather.hip", "common.hpp", "kernels.hpp"]),
 }
 
 
