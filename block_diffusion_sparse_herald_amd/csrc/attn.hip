@@ -324,34 +324,37 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   }
 }
 
-// Merges the key ranges of one (sequence, KV head): 4 output dimensions per thread,
-// the ranges taken 8 at a time (loads first) with a running (max, sum).
+// Merges the key ranges of one (sequence, KV head): 8 output dimensions per thread
+// (16-byte loads and stores), the ranges taken 8 at a time (loads first) with a
+// running (max, sum).
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict__ o_part,
-                                                          const float2* __restrict__ ml_part, AttnGeom a,
-                                                          bf16* __restrict__ out) {
-  constexpr int CH = 8;
-  const int idx = blockIdx.x * 64 + threadIdx.x;
+__global__ __launch_bounds__(kAttnCombineThreads) void attn_combine_kernel(const bf16* __restrict__ o_part,
+                                                                           const float2* __restrict__ ml_part,
+                                                                           AttnGeom a, bf16* __restrict__ out) {
+  constexpr int CH = 8, TPR = D / 8;  // threads per output row
+  const int idx = blockIdx.x * kAttnCombineThreads + threadIdx.x;
   const int R = a.B * a.G;
-  const int per_unit = R * (D / 4);
+  const int per_unit = R * TPR;
   const int unit = a.rcp_pu ? (int)__umulhi((uint32_t)idx, a.rcp_pu) : idx / per_unit;
   if (unit >= a.nunits) return;
-  const int r = (idx - unit * per_unit) / (D / 4), e = (idx % (D / 4)) * 4;
+  const int r = (idx - unit * per_unit) / TPR, e = (idx % TPR) * 8;
   const int s = a.rcp_hkv ? (int)__umulhi((uint32_t)unit, a.rcp_hkv) : unit, g = unit - s * a.Hkv;
   const int64_t base = (int64_t)unit * a.nks * a.rpad + r;
   float M = -INFINITY, L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int k0 = 0; k0 < a.nks; k0 += CH) {
     float2 p[CH];
-    uint2 vb[CH];
+    uint4 vb[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       p[j] = make_float2(-INFINITY, 0.f);
-      vb[j] = make_uint2(0, 0);
+      vb[j] = make_uint4(0, 0, 0, 0);
       if (k0 + j < a.nks) {
         const int64_t row = base + (int64_t)(k0 + j) * a.rpad;
         p[j] = ml_part[row];
-        vb[j] = *reinterpret_cast<const uint2*>(o_part + row * D + e);
+        vb[j] = *reinterpret_cast<const uint4*>(o_part + row * D + e);
       }
     }
     float mc = M;
@@ -359,26 +362,27 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const bf16* __restrict
     for (int j = 0; j < CH; ++j) mc = fmaxf(mc, p[j].x);
     const float alpha = fast_exp2(M - mc);  // 0 on the first chunk (M = -inf)
     L *= alpha;
-    acc.x *= alpha;
-    acc.y *= alpha;
-    acc.z *= alpha;
-    acc.w *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       if (p[j].x == -INFINITY) continue;
       const float wgt = fast_exp2(p[j].x - mc);
       L += wgt * p[j].y;
-      acc.x += wgt * bf16_lo(vb[j].x);
-      acc.y += wgt * bf16_hi(vb[j].x);
-      acc.z += wgt * bf16_lo(vb[j].y);
-      acc.w += wgt * bf16_hi(vb[j].y);
+      const uint32_t w4[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wgt * bf16_lo(w4[i]);
+        acc[2 * i + 1] += wgt * bf16_hi(w4[i]);
+      }
     }
     M = mc;
   }
   const float inv = 1.f / L;
   const int rb = a.rcp_g ? (int)__umulhi((uint32_t)r, a.rcp_g) : r;  // block query of row r
-  *reinterpret_cast<uint2*>(out + (((int64_t)s * a.B + rb) * a.Hq + g * a.G + (r - rb * a.G)) * D + e) =
-      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  *reinterpret_cast<uint4*>(out + (((int64_t)s * a.B + rb) * a.Hq + g * a.G + (r - rb * a.G)) * D + e) =
+      make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                 pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
 // fp32 path: a workgroup takes four query rows of one (sequence, KV head) and walks
@@ -533,7 +537,7 @@ AttnGeom attn_geom(const Shape& s) {
   a.rcp_nks = rcp(a.nks);
   a.rcp_hkv = rcp(a.Hkv);
   a.rcp_g = a.G <= 1 ? 0u : (uint32_t)(((1ull << 32) + (uint64_t)a.G - 1) / (uint64_t)a.G);
-  const uint64_t pu = (uint64_t)s.B * s.G * (s.D / 4), nidx = (uint64_t)a.nunits * pu;
+  const uint64_t pu = (uint64_t)s.B * s.G * (s.D / 8), nidx = (uint64_t)a.nunits * pu;
   a.rcp_pu = nidx * pu < (1ull << 32) ? (uint32_t)(((1ull << 32) + pu - 1) / pu) : 0u;
   return a;
 }
@@ -583,12 +587,12 @@ hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t 
   const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
   const bf16* o_part = static_cast<const bf16*>(ws);
   const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(bf16)));
-  const int64_t n = (int64_t)a.nunits * a.B * a.G * (s.D / 4);
-  const dim3 grid((unsigned)((n + 63) / 64));
+  const int64_t n = (int64_t)a.nunits * a.B * a.G * (s.D / 8);
+  const dim3 grid((unsigned)((n + kAttnCombineThreads - 1) / kAttnCombineThreads));
   if (s.D == 128)
-    klaunch(attn_combine_kernel<128>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
+    klaunch(attn_combine_kernel<128>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
   else
-    klaunch(attn_combine_kernel<64>, grid, 64, 0, st, o_part, ml_part, a, (bf16*)out);
+    klaunch(attn_combine_kernel<64>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
   return hipGetLastError();
 }
 

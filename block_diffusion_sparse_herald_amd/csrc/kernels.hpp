@@ -78,7 +78,7 @@ struct AttnGeom {
   // every quotient taken is below nitems and nitems * d < 2^32 (checked by attn_geom)
   uint32_t rcp_nrs, rcp_nks, rcp_hkv;
   uint32_t rcp_g;   // ceil(2^32 / G), 0 for G = 1 (exact: query rows r < 2^16)
-  uint32_t rcp_pu;  // ceil(2^32 / (B * G * D / 4)) for the range merge's thread index, 0 when that is
+  uint32_t rcp_pu;  // ceil(2^32 / (B * G * D / 8)) for the range merge's thread index, 0 when that is
                     // not exact for every index (the merge then divides)
 };
 constexpr int kAttnBlocksPerRange = 32;
@@ -86,6 +86,7 @@ constexpr int kAttnTargetWorkgroups = 256;  // one per compute unit
 constexpr int kAttnFewPairs = 96;  // below this (pairs x four-tile row groups x 5) the few-pairs geometry applies
 constexpr int kAttnTargetWorkgroupsFew = 192;  // with two query tiles per workgroup
 constexpr int kAttnMaxStages = 4;
+constexpr int kAttnCombineThreads = 64;   // range-merge workgroup (8 output dims per thread)
 
 // select
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);
