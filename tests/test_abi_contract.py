@@ -209,6 +209,25 @@ def test_attn_splits_reported(lib):
     assert H.herald_attn_splits(prob(dtype=H.HERALD_F32)) == 1
 
 
+@pytest.mark.parametrize("kw,splits", [
+    # 1 x 32K, 32/8/128: few (sequence, KV head) pairs, 17 blocks in ranges of 3
+    (dict(seq_start=[0, 32768], Hq=32, Hkv=8, C=4096, topk=1024), 6),
+    # 16 x 32K: 256 workgroups without a split
+    (dict(seq_start=[32768 * i for i in range(17)], Hq=32, Hkv=8, C=4096, topk=1024), 1),
+    # 4 x 128K: aimed at one workgroup per compute unit, 17 blocks in 4 ranges
+    (dict(seq_start=[131072 * i for i in range(5)], Hq=32, Hkv=8, C=8192, topk=1024), 4),
+    # 8 ragged sequences, 28/4/128, K = 2048: 33 blocks, at most 32 per range
+    (dict(seq_start=[0, 16384, 40000, 65536, 90000, 120000, 150000, 200000, 240000], Hq=28, Hkv=4, C=4096,
+          topk=2048), 2),
+    # dense attention over a whole 32K cache: 513 blocks, at most 32 per range
+    (dict(seq_start=[0, 32768], Hq=32, Hkv=8, C=32768, topk=32768), 17),
+])
+def test_attn_split_geometry(lib, kw, splits):
+    """Key ranges the attention call splits each (sequence, KV head) into, for the
+    benchmark workloads' shapes (host-side geometry only)."""
+    assert H.herald_attn_splits(prob(**kw)) == splits
+
+
 def test_product_path_never_imports_the_oracle():
     pkg = os.path.join(ROOT, "block_diffusion_sparse_herald_amd")
     pat = re.compile(r"^\s*(import\s+oracle|from\s+oracle|from\s+\.+\s*import\s+oracle)|herald_oracle|#include.*oracle",
