@@ -7,9 +7,13 @@ synthetic tensors already resident in HBM. To keep the 256 MiB Infinity Cache
 from serving the scan, the K/V cache is replicated until the replicas span at
 least 512 MiB and consecutive steps rotate through them.
 
-Prints one JSON line. `roofline` is for the kernel that takes the most time per
-step, timed with HIP events recorded by the library around that kernel on the
-stream it runs on. `cpu_baseline` times the CPU oracle on a bounded sample.
+Prints one JSON line. The K timed steps run REPEATS times; `value` and
+`ms_per_step` are the median run. `roofline` is for the kernel that takes the most
+time per step, timed with HIP events recorded by the library around that kernel on
+the stream it runs on. `fractions` puts the whole step against its roofline time
+(`block`), the scan against HBM peak and attention against MFMA peak.
+`cpu_baseline` times the CPU oracle on a bounded sample: on every core of the host
+share (one worker process per core) and on one core, with the CPU model.
 
 `--method offload` runs the HERALD path as a two-stream pipeline over a pinned-host
 KV pool: while stream A runs block i's T attention steps on one of two sparse pools,
@@ -47,6 +51,7 @@ METRIC = "blocks/sec (select+refine+T-step sparse attn) at L=32K; % HBM/MFMA pea
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
+REPEATS = 5  # timed runs of K steps; value and per-launch figures are their medians
 
 
 def log(*a):
@@ -88,10 +93,59 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(wl, batch, budget_s: float):
-    """The CPU oracle, one BLAS thread, whole blocks of sequence 0 until the time budget is used."""
-    import numpy as np
+# ---------------------------------------------------------------- CPU oracle baseline
+#
+# The oracle (numpy fp64, one BLAS thread per worker) on whole blocks of sequence 0.
+# Worker processes are forked right after the inputs are drawn, before this process
+# touches the GPU, and inherit sequence 0's arrays; they sit idle while the GPU runs.
+
+_CPU_ARGS = None  # (args tuple for herald_block, C, topk, scale), set before the fork
+
+
+def _cpu_init():
     from threadpoolctl import threadpool_limits
+
+    threadpool_limits(limits=1)
+
+
+def _cpu_blocks(budget_s: float):
+    """Whole blocks until budget_s has passed: (blocks, seconds)."""
+    import oracle.herald_oracle as orc
+
+    args, C, topk, scale = _CPU_ARGS
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.herald_block(*args, C, topk, scale)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            return n, time.perf_counter() - t0
+
+
+def host_cores() -> int:
+    """Cores this process may use, capped at 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_prepare(wl, batch):
+    """Sets the oracle's inputs (sequence 0, widened to fp64) and forks the worker pool."""
+    global _CPU_ARGS
+    import multiprocessing as mp
+
+    import numpy as np
 
     import oracle.herald_oracle as orc
     from block_diffusion_sparse_herald_amd.inputs import bf16_bits_to_f32
@@ -100,20 +154,47 @@ def cpu_baseline(wl, batch, budget_s: float):
         return (bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
 
     a, e = int(batch.seq_start[0]), int(batch.seq_start[1])
-    args = (w(batch.q0[0]), w(batch.k_cache[a:e]), w(batch.v_cache[a:e]), w(batch.q_steps[:, 0]),
-            w(batch.kb_steps[:, 0]), w(batch.vb_steps[:, 0]))
-    n = 0
+    _CPU_ARGS = ((w(batch.q0[0]), w(batch.k_cache[a:e]), w(batch.v_cache[a:e]), w(batch.q_steps[:, 0]),
+                  w(batch.kb_steps[:, 0]), w(batch.vb_steps[:, 0])), wl.C, wl.topk, orc.default_scale(wl.d))
+    cores = host_cores()
+    return mp.get_context("fork").Pool(cores, initializer=_cpu_init), cores, e - a
+
+
+def cpu_baseline(wl, pool, cores: int, L0: int, budget_s: float):
+    """Oracle blocks/s on every core (one block stream per worker process) and on one core."""
+    one_n, one_t = pool.apply(_cpu_blocks, (budget_s,))
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while True:
-            orc.herald_block(*args, wl.C, wl.topk, orc.default_scale(wl.d))
-            n += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "blocks/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} whole block(s) of sequence 0 (L={e - a}, select+refine+gather+{wl.T} attention steps), "
-                      f"numpy fp64, 1 thread, {dt:.1f} s"}
+    res = pool.map(_cpu_blocks, [budget_s] * cores, chunksize=1)
+    wall = time.perf_counter() - t0
+    n_all = sum(n for n, _ in res)
+    what = f"whole blocks of sequence 0 (L={L0}, select+refine+gather+{wl.T} attention steps), numpy fp64"
+    return {"value": n_all / wall, "unit": "blocks/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_all} {what}, {cores} worker processes x 1 thread, {wall:.1f} s wall",
+            "one_core": {"value": one_n / one_t, "unit": "blocks/s", "cores": 1,
+                         "sample": f"{one_n} {what}, 1 thread, {one_t:.1f} s"},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "note": "the oracle as written (plain fp64 numpy), not a tuned CPU implementation"}
+
+
+def block_roofline(wl, lengths, esz: int, mfma_peak: float) -> dict:
+    """Roofline time of one step (one block per sequence): the scan streams the K cache;
+    refine contracts B*G query rows with C candidate rows; the gather reads and writes the
+    subset; each of the T attention steps streams the subset and the step's tensors. Each
+    term is the larger of its bytes / HBM peak and flops / MFMA peak."""
+    bw = HBM_PEAK_GBS * 1e9
+    fl = mfma_peak * 1e12
+    n = wl.nseq
+    scan_b = int(sum(lengths)) * wl.Hkv * wl.d * esz
+    ref_b = n * (wl.Hkv * wl.C * wl.d * esz + wl.B * wl.Hq * wl.d * esz)
+    ref_f = 2.0 * n * wl.B * wl.Hq * wl.C * wl.d
+    gat_b = 4 * n * wl.Hkv * wl.topk * wl.d * esz
+    att_b = esz * n * (2 * wl.Hkv * wl.topk * wl.d + 2 * wl.B * wl.Hq * wl.d + 2 * wl.B * wl.Hkv * wl.d)
+    att_f = 4.0 * n * wl.B * wl.Hq * (wl.topk + wl.B) * wl.d
+    t = scan_b / bw + max(ref_b / bw, ref_f / fl) + gat_b / bw + wl.T * max(att_b / bw, att_f / fl)
+    return {"t_roof_us": round(t * 1e6, 3), "blocks_per_s": round(n / t, 1),
+            "terms_us": {"scan": round(scan_b / bw * 1e6, 3), "refine": round(max(ref_b / bw, ref_f / fl) * 1e6, 3),
+                         "gather": round(gat_b / bw * 1e6, 3),
+                         "attention": round(wl.T * max(att_b / bw, att_f / fl) * 1e6, 3)}}
 
 
 def main(argv=None):
@@ -122,7 +203,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa32x8_L32768_b1")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle time per cpu_baseline leg (all cores, then one core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step directly instead of replaying graphs")
     ap.add_argument("--method", choices=["herald", "pipelined", "offload", "compressed", "dense", "mage"],
@@ -145,13 +227,17 @@ def main(argv=None):
     from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, make_batch
     from block_diffusion_sparse_herald_amd.runner import BlockRunner
 
+    wl = WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name}: generating inputs")
+    batch = make_batch(wl)
+    # the CPU oracle's worker processes are forked now, before anything touches the GPU
+    pool = None
+    if args.method == "herald" and not args.no_cpu_baseline:
+        pool, cores, L0 = cpu_prepare(wl, batch)
     # Device memory, streams, events and graphs come straight from the HIP runtime the
     # library links (no PyTorch in this process).
     hip = Hip()
     H.load()
-    wl = WORKLOADS[args.workload]
-    log(f"[bench] workload {wl.name}: generating inputs")
-    batch = make_batch(wl)
     dev = {n: DevArray.from_host(hip, getattr(batch, n))
            for n in ["q0", "k_cache", "v_cache", "q_steps", "kb_steps", "vb_steps"]}
     cache_bytes = dev["k_cache"].nbytes + dev["v_cache"].nbytes
@@ -254,24 +340,29 @@ def main(argv=None):
                 step(i + 1)
                 hip.sync()
         log("[bench] graph replays match eager steps")
-    t_start, t_end = hip.event(), hip.event()
-    hip.sync()
-    w0 = time.perf_counter()
-    hip.record(t_start, stream)
-    for i in range(args.steps):
-        if graphs:
-            hip.launch(graphs[i], stream)
-        else:
-            step(i, timed, evs[i])
-    hip.record(t_end, stream)
-    hip.sync()
-    wall = time.perf_counter() - w0
-    ms = hip.elapsed_ms(t_start, t_end)
+    # REPEATS timed runs of exactly K steps each; the reported figures are their medians
+    reps_ms, reps_dom = [], []
+    for rep in range(REPEATS):
+        t_start, t_end = hip.event(), hip.event()
+        hip.sync()
+        w0 = time.perf_counter()
+        hip.record(t_start, stream)
+        for i in range(args.steps):
+            if graphs:
+                hip.launch(graphs[i], stream)
+            else:
+                step(i, timed, evs[i])
+        hip.record(t_end, stream)
+        hip.sync()
+        wall = time.perf_counter() - w0
+        reps_ms.append(hip.elapsed_ms(t_start, t_end))
+        reps_dom.append(float(np.mean([hip.elapsed_ms(a, b) * 1e3 for a, b in evs])) / nper)
+        log(f"[bench] run {rep}: {args.steps} steps in {reps_ms[-1]:.3f} ms (wall {wall * 1e3:.1f} ms); "
+            f"{reps_ms[-1] / args.steps * 1e3:.1f} us/step; {timed}: {reps_dom[-1]:.2f} us per launch")
+    ms = float(np.median(reps_ms))
     ms_per_step = ms / args.steps
     blocks_per_s = wl.nseq * args.steps / (ms / 1e3)
-    dom_us = float(np.mean([hip.elapsed_ms(a, b) * 1e3 for a, b in evs])) / nper
-    log(f"[bench] {args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); {ms_per_step * 1e3:.1f} us/step; "
-        f"{timed}: {dom_us:.2f} us per launch")
+    dom_us = float(np.median(reps_dom))
 
     bound, work = kernel_work(wl, batch.lengths)[dominant]
     if bound == "hbm":
@@ -285,6 +376,23 @@ def main(argv=None):
     roofline = {"kernel": rkernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(rkernel, wl.name),
                 "avg_launch_us": round(dom_us, 3)}
+    # the whole step against its roofline, and the two targeted kernels against their peaks
+    esz = 2 if wl.dtype == "bf16" else 4
+    mpeak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    broof = block_roofline(wl, batch.lengths, esz, mpeak)
+    broof["frac"] = round(blocks_per_s / broof["blocks_per_s"], 4)
+    work = kernel_work(wl, batch.lengths)
+    scan_us = per_launch_us.get("scan")
+    attn_us = dom_us if timed == "attn_op" else per_launch_us["attn"] + per_launch_us.get("attn_combine", 0.0)
+    attn_flop = 4.0 * wl.nseq * wl.B * wl.Hq * (wl.topk + wl.B) * wl.d
+    fractions = {
+        "block": broof,
+        "scan_hbm": None if scan_us is None else {
+            "us": round(scan_us, 3), "GB_s": round(work["scan"][1] / scan_us / 1e3, 1),
+            "frac": round(work["scan"][1] / scan_us / 1e3 / HBM_PEAK_GBS, 4)},
+        "attn_mfma": {"us": round(attn_us, 3), "TFLOP_s": round(attn_flop / attn_us / 1e6, 2),
+                      "frac": round(attn_flop / attn_us / 1e6 / mpeak, 4), "peak_TFLOP_s": mpeak},
+    }
 
     result = {
         "metric": METRIC,
@@ -305,11 +413,15 @@ def main(argv=None):
         "tokens_per_s": round(blocks_per_s * wl.B, 1),
         "launch": "eager" if args.eager else "hip_graph_per_step",
         "per_launch_us": {k: round(v, 2) for k, v in per_launch_us.items()},
+        "repeats": {"n": REPEATS, "ms_per_step": [round(x / args.steps, 4) for x in reps_ms], "value": "median"},
         "roofline": roofline,
+        "fractions": fractions,
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(wl, batch, args.cpu_budget)
+    if pool is not None:
+        log(f"[bench] timing the CPU oracle ({cores} worker processes, then 1)")
+        result["cpu_baseline"] = cpu_baseline(wl, pool, cores, L0, args.cpu_budget)
+        pool.close()
+        pool.join()
     print(json.dumps(result), flush=True)
     return 0
 

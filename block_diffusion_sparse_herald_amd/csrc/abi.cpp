@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <string>
 
@@ -110,6 +111,7 @@ herald_status make_shape(const herald_problem* p, Shape* s) {
   if (p->num_candidates < 1) return fail(HERALD_ERR_INVALID_ARG, "num_candidates = %d < 1", p->num_candidates);
   if (p->topk < 1 || p->topk > p->num_candidates)
     return fail(HERALD_ERR_INVALID_ARG, "topk = %d outside [1, num_candidates = %d]", p->topk, p->num_candidates);
+  if (p->topk > kMaxTopk) return fail(HERALD_ERR_UNSUPPORTED, "topk = %d exceeds %d", p->topk, kMaxTopk);
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
     return fail(HERALD_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (!p->seq_start_host) return fail(HERALD_ERR_INVALID_ARG, "seq_start_host is NULL");
@@ -243,6 +245,13 @@ herald_status check_select_shape(const Shape& s) {
   return HERALD_OK;
 }
 
+herald_status check_attn_shape(const Shape& s) {
+  if (!attn_fits(s))
+    return fail(HERALD_ERR_UNSUPPORTED, "attention work split of %d sequences x %d KV heads x %d keys is too large",
+                s.nseq, s.Hkv, s.topk + s.B);
+  return HERALD_OK;
+}
+
 herald_status check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return HERALD_OK;
   if (!ws) return fail(HERALD_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -266,7 +275,10 @@ herald_status herald_workspace_size(const herald_problem* p, int op, size_t* byt
       carve_select(s, nullptr, &n);
       break;
     case HERALD_OP_REFINE: carve_refine(s, nullptr, &n); break;
-    case HERALD_OP_ATTN: n = attn_ws_bytes(s); break;
+    case HERALD_OP_ATTN:
+      HERALD_TRY(check_attn_shape(s));
+      n = attn_ws_bytes(s);
+      break;
     case HERALD_OP_SELECT_COMPRESSED:
       HERALD_TRY(check_select_shape(s));
       carve_compressed(p, s, 2, nullptr, &n);  // stride 2 has the most compressed rows
@@ -277,6 +289,11 @@ herald_status herald_workspace_size(const herald_problem* p, int op, size_t* byt
   if (s.nseq == 0) n = 0;
   *bytes = n;
   return ok();
+}
+
+size_t herald_workspace_bytes(const herald_problem* p, int op) {
+  size_t n = 0;
+  return herald_workspace_size(p, op, &n) == HERALD_OK ? n : SIZE_MAX;
 }
 
 int64_t herald_vsel_ld(int32_t topk) { return topk < 1 ? 0 : vsel_ld(topk); }
@@ -419,8 +436,15 @@ herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const
   HERALD_TRY(check_ptr(k_sel, "k_sel"));
   HERALD_TRY(check_ptr(v_sel, "v_sel"));
   if (src_is_host < 0 || src_is_host > 2) return fail(HERALD_ERR_INVALID_ARG, "src_is_host must be 0, 1 or 2");
+  // the device and GPU-read paths take an optional status word in ws
+  int32_t* status = nullptr;
+  if (src_is_host != 1 && ws) {
+    if (ws_bytes < sizeof(int32_t)) return fail(HERALD_ERR_WORKSPACE, "status word needs 4 bytes, ws has %zu", ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return fail(HERALD_ERR_INVALID_ARG, "status word is not 4-byte aligned");
+    status = static_cast<int32_t*>(ws);
+  }
   if (src_is_host == 0) {
-    HERALD_LAUNCH(7, stream, launch_gather(s, k_src, v_src, topk_idx, k_sel, v_sel, stream));
+    HERALD_LAUNCH(7, stream, launch_gather(s, k_src, v_src, topk_idx, k_sel, v_sel, status, stream));
     if (done) HERALD_HIP(hipEventRecord(done, stream));
     return ok();
   }
@@ -436,7 +460,7 @@ herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const
       }
       dev[i] = a.devicePointer;
     }
-    HERALD_LAUNCH(7, stream, launch_gather(s, dev[0], dev[1], topk_idx, k_sel, v_sel, stream));
+    HERALD_LAUNCH(7, stream, launch_gather(s, dev[0], dev[1], topk_idx, k_sel, v_sel, status, stream));
     if (done) HERALD_HIP(hipEventRecord(done, stream));
     return ok();
   }
@@ -487,6 +511,7 @@ herald_status herald_block_attn(const herald_problem* p, const void* q, const vo
   HERALD_TRY(check_ptr(k_sel, "k_sel"));
   HERALD_TRY(check_ptr(v_sel, "v_sel"));
   HERALD_TRY(check_ptr(out, "out"));
+  HERALD_TRY(check_attn_shape(s));
   HERALD_TRY(check_ws(ws, ws_bytes, attn_ws_bytes(s)));
   HERALD_LAUNCH(8, stream, launch_attn(s, q, k_blk, v_blk, k_sel, v_sel, out, ws, stream));
   if (attn_splits(s) > 1) HERALD_LAUNCH(9, stream, launch_attn_combine(s, ws, out, stream));

@@ -26,7 +26,9 @@
 // when a row's max grows by more than 8 (base 2): probabilities then stay below
 // 2^8, exact in fp32 and bf16 range, and both sums use the same reference.
 // With several key ranges each workgroup writes a partial (fp32 max and sum, the
-// unnormalised output in bf16) that attn_combine_kernel merges.
+// unnormalised output in fp32) that attn_combine_kernel merges; the output is rounded
+// to bf16 once, at the end. The running sum adds the probabilities as rounded to bf16
+// for the second product, so the applied weights are normalised exactly.
 // fp32 path (attn_f32_kernel): four query rows per workgroup, VALU, keys in chunks of 128.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -53,7 +55,7 @@ template <int D>
 __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kb,
                                                    const bf16* __restrict__ vb, const bf16* __restrict__ k_sel,
                                                    const bf16* __restrict__ v_sel, AttnGeom a, float scale2,
-                                                   bf16* __restrict__ out, bf16* __restrict__ o_part,
+                                                   bf16* __restrict__ out, float* __restrict__ o_part,
                                                    float2* __restrict__ ml_part) {
   constexpr int NW = 8;              // waves: two groups of four
   constexpr int KB = kAttnKeyBlock;  // 64
@@ -249,21 +251,27 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
       m = mn;
     }
     float p[4][4];
-    float ps = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        p[mt][t] = fast_exp2(fmaf(sacc[mt][t], scale2, -m));
-        ps += p[mt][t];
-      }
-    l += ps;
+      for (int t = 0; t < 4; ++t) p[mt][t] = fast_exp2(fmaf(sacc[mt][t], scale2, -m));
     uint4 bp[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
       bp[h2] = make_uint4(pack_bf16x2(p[2 * h2][0], p[2 * h2][1]), pack_bf16x2(p[2 * h2][2], p[2 * h2][3]),
                           pack_bf16x2(p[2 * h2 + 1][0], p[2 * h2 + 1][1]),
                           pack_bf16x2(p[2 * h2 + 1][2], p[2 * h2 + 1][3]));
+    // the normaliser sums the probabilities as the product below uses them (rounded to
+    // bf16), so the weights applied to the values sum to one exactly: a query whose
+    // attention falls on a few keys gets their values back without the weights' rounding
+    float ps = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint32_t w4[4] = {bp[h2].x, bp[h2].y, bp[h2].z, bp[h2].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps += bf16_lo(w4[i]) + bf16_hi(w4[i]);
+    }
+    l += ps;
 
     // ---- O^T += V^T P^T over the two 32-key halves of the block
 #pragma unroll
@@ -315,20 +323,19 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
           make_uint2(pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv));
   } else {
     const int64_t prow = ((int64_t)unit * a.nks + ksp) * a.rpad + r;
-    bf16* orow = o_part + prow * D + qd * 4;
+    float* orow = o_part + prow * D + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<uint2*>(orow + dt * 16) =
-          make_uint2(pack_bf16x2(o[dt][0], o[dt][1]), pack_bf16x2(o[dt][2], o[dt][3]));
+      *reinterpret_cast<float4*>(orow + dt * 16) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
     if (qd == 0) ml_part[prow] = make_float2(m, l);
   }
 }
 
 // Merges the key ranges of one (sequence, KV head): 8 output dimensions per thread
-// (16-byte loads and stores), the ranges taken 8 at a time (loads first) with a
-// running (max, sum).
+// (two 16-byte fp32 loads per range, one 16-byte bf16 store), the ranges taken 8 at a
+// time (loads first) with a running (max, sum).
 template <int D>
-__global__ __launch_bounds__(kAttnCombineThreads) void attn_combine_kernel(const bf16* __restrict__ o_part,
+__global__ __launch_bounds__(kAttnCombineThreads) void attn_combine_kernel(const float* __restrict__ o_part,
                                                                            const float2* __restrict__ ml_part,
                                                                            AttnGeom a, bf16* __restrict__ out) {
   constexpr int CH = 8, TPR = D / 8;  // threads per output row
@@ -346,15 +353,16 @@ __global__ __launch_bounds__(kAttnCombineThreads) void attn_combine_kernel(const
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int k0 = 0; k0 < a.nks; k0 += CH) {
     float2 p[CH];
-    uint4 vb[CH];
+    float4 va[CH], vc[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       p[j] = make_float2(-INFINITY, 0.f);
-      vb[j] = make_uint4(0, 0, 0, 0);
+      va[j] = vc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (k0 + j < a.nks) {
         const int64_t row = base + (int64_t)(k0 + j) * a.rpad;
         p[j] = ml_part[row];
-        vb[j] = *reinterpret_cast<const uint4*>(o_part + row * D + e);
+        va[j] = *reinterpret_cast<const float4*>(o_part + row * D + e);
+        vc[j] = *reinterpret_cast<const float4*>(o_part + row * D + e + 4);
       }
     }
     float mc = M;
@@ -369,12 +377,9 @@ __global__ __launch_bounds__(kAttnCombineThreads) void attn_combine_kernel(const
       if (p[j].x == -INFINITY) continue;
       const float wgt = fast_exp2(p[j].x - mc);
       L += wgt * p[j].y;
-      const uint32_t w4[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+      const float x8[8] = {va[j].x, va[j].y, va[j].z, va[j].w, vc[j].x, vc[j].y, vc[j].z, vc[j].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wgt * bf16_lo(w4[i]);
-        acc[2 * i + 1] += wgt * bf16_hi(w4[i]);
-      }
+      for (int i = 0; i < 8; ++i) acc[i] += wgt * x8[i];
     }
     M = mc;
   }
@@ -519,7 +524,7 @@ AttnGeom attn_geom(const Shape& s) {
   // range is bound by memory latency: with few (sequence, KV head) pairs the keys are
   // split into ranges of about kAttnMaxStages blocks, to spread them over enough
   // workgroups (the ranges are then merged by attn_combine_kernel).
-  const int groups = a.nunits * a.nrs;
+  const int groups = std::max(1, a.nunits * a.nrs);  // an empty batch (nseq = 0) launches nothing
   const int spread = std::min((target + groups - 1) / groups, (nblk + minrange - 1) / minrange);
   const int nks = std::max((nblk + kAttnBlocksPerRange - 1) / kAttnBlocksPerRange, spread);
   a.bps = (nblk + nks - 1) / nks;
@@ -527,10 +532,12 @@ AttnGeom attn_geom(const Shape& s) {
   // a range of at most kAttnMaxStages blocks is fetched at once; longer ranges cycle
   // through kAttnMaxStages stages (two blocks in use, the next two in flight)
   a.nst = std::min(a.bps, kAttnMaxStages);
-  a.nitems = a.nunits * a.nrs * a.nks;
+  // workgroup count in 64 bits: attn_fits refuses the shape before it could overflow
+  const int64_t nitems = (int64_t)a.nunits * a.nrs * a.nks;
+  a.nitems = nitems < (int64_t(1) << 31) ? (int)nitems : -1;
   auto rcp = [&](int d) -> uint32_t {
     if (d <= 1) return 0u;
-    if ((uint64_t)a.nitems * (uint64_t)d >= (1ull << 32)) return 0xffffffffu;  // flagged below
+    if ((uint64_t)nitems * (uint64_t)d >= (1ull << 32)) return 0xffffffffu;  // flagged by attn_fits
     return (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d);
   };
   a.rcp_nrs = rcp(a.nrs);
@@ -542,6 +549,12 @@ AttnGeom attn_geom(const Shape& s) {
   return a;
 }
 
+bool attn_fits(const Shape& s) {
+  if (!s.bf16 || s.nseq == 0) return true;
+  const AttnGeom a = attn_geom(s);
+  return a.nitems > 0 && a.rcp_nrs != 0xffffffffu && a.rcp_nks != 0xffffffffu && a.rcp_hkv != 0xffffffffu;
+}
+
 int attn_splits(const Shape& s) { return s.bf16 ? attn_geom(s).nks : 1; }
 
 size_t attn_ws_bytes(const Shape& s) {
@@ -549,7 +562,7 @@ size_t attn_ws_bytes(const Shape& s) {
   const AttnGeom a = attn_geom(s);
   if (a.nks == 1) return 0;
   const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
-  return align256(rows * s.D * sizeof(bf16)) + align256(rows * sizeof(float2));
+  return align256(rows * s.D * sizeof(float)) + align256(rows * sizeof(float2));
 }
 
 template <int D>
@@ -563,15 +576,15 @@ template <int D>
 static hipError_t launch_attn_bf16(const AttnGeom& a, const void* q, const void* kb, const void* vb,
                                    const void* k_sel, const void* v_sel, void* out, void* ws, float scale2,
                                    hipStream_t st) {
-  bf16* o_part = nullptr;
+  float* o_part = nullptr;
   float2* ml_part = nullptr;
   if (a.nks > 1) {
     const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
-    o_part = static_cast<bf16*>(ws);
-    ml_part = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(rows * D * sizeof(bf16)));
+    o_part = static_cast<float*>(ws);
+    ml_part = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(rows * D * sizeof(float)));
   }
-  // more workgroups than the reciprocal decode covers exactly (over 2^32 / 64)
-  if (a.rcp_nrs == 0xffffffffu || a.rcp_nks == 0xffffffffu || a.rcp_hkv == 0xffffffffu)
+  // more workgroups than the reciprocal decode covers exactly (refused by attn_fits on the host)
+  if (a.nitems <= 0 || a.rcp_nrs == 0xffffffffu || a.rcp_nks == 0xffffffffu || a.rcp_hkv == 0xffffffffu)
     return hipErrorInvalidConfiguration;
   const size_t smem = attn_smem<D>(a);
   hipError_t e = allow_smem((const void*)attn_kernel<D>, smem);
@@ -585,8 +598,8 @@ static hipError_t launch_attn_bf16(const AttnGeom& a, const void* q, const void*
 hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t st) {
   const AttnGeom a = attn_geom(s);
   const size_t rows = (size_t)a.nunits * a.nks * a.rpad;
-  const bf16* o_part = static_cast<const bf16*>(ws);
-  const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(bf16)));
+  const float* o_part = static_cast<const float*>(ws);
+  const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(float)));
   const int64_t n = (int64_t)a.nunits * a.B * a.G * (s.D / 8);
   const dim3 grid((unsigned)((n + kAttnCombineThreads - 1) / kAttnCombineThreads));
   if (s.D == 128)

@@ -14,11 +14,14 @@ namespace herald {
 // One workgroup per 64 picks of one (sequence, KV head). PACKED selects where row i
 // of the group comes from: the cache by index (device path) or packed
 // [nseq][Hkv][topk][D] buffers (host-pool path, after their copy to the device).
+// On the indexed path an index outside [0, L_s) is never dereferenced: its K and V
+// rows are written as zeros and, when `status` is not NULL, *status is set to 1.
 template <typename T, int D, bool PACKED>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      const int32_t* __restrict__ idx,
                                                      const int64_t* __restrict__ seq_start, int Hkv, int topk,
-                                                     int64_t ldv, T* __restrict__ k_sel, T* __restrict__ v_sel) {
+                                                     int64_t ldv, T* __restrict__ k_sel, T* __restrict__ v_sel,
+                                                     int32_t* __restrict__ status) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int CPR = D / EPL;  // 16-byte chunks per row
   constexpr int LDT = D + EPL;  // padded LDS row (elements)
@@ -27,22 +30,30 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k, co
   const int i0 = blk * 64;
   const int64_t unit = (int64_t)s * Hkv + g;
   const int64_t j0 = PACKED ? 0 : seq_start[s];
-
-  auto src_row = [&](const T* base, int i) -> const T* {
-    if (PACKED) return base + (unit * topk + i) * D;
-    return base + ((j0 + idx[unit * topk + i]) * Hkv + g) * D;
-  };
+  const int64_t L = PACKED ? 0 : seq_start[s + 1] - j0;
 
   // K rows (copied straight through) and V rows (staged in LDS): all loads first
   constexpr int NPT = 64 * CPR / 256;  // 16-byte chunks per thread, each of K and V
   uint4 kv[NPT], vv[NPT];
+  bool bad = false;
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
     const int c = threadIdx.x + u * 256;
     const int i = min(i0 + c / CPR, topk - 1), ch = c % CPR;
-    kv[u] = ld16(src_row(k, i) + ch * EPL);
-    vv[u] = ld16(src_row(v, i) + ch * EPL);
+    int64_t row;
+    bool ok = true;
+    if (PACKED) {
+      row = unit * topk + i;
+    } else {
+      const int32_t j = idx[unit * topk + i];
+      ok = j >= 0 && j < L;
+      row = (j0 + (ok ? j : 0)) * Hkv + g;
+    }
+    bad |= !ok;
+    kv[u] = ok ? ld16(k + row * D + ch * EPL) : make_uint4(0, 0, 0, 0);
+    vv[u] = ok ? ld16(v + row * D + ch * EPL) : make_uint4(0, 0, 0, 0);
   }
+  if (!PACKED && bad && status) *status = 1;
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
     const int c = threadIdx.x + u * 256;
@@ -69,36 +80,36 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k, co
 
 template <bool PACKED>
 static hipError_t gather_dispatch(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel,
-                                  void* v_sel, hipStream_t st) {
+                                  void* v_sel, int32_t* status, hipStream_t st) {
   dim3 grid((s.topk + 63) / 64, s.Hkv, s.nseq);
   const int64_t ldv = vsel_ld(s.topk);
   if (s.bf16) {
     if (s.D == 128)
       klaunch(gather_kernel<bf16, 128, PACKED>, grid, 256, 0, st, (const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
-                                                             s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel);
+                                                             s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel, status);
     else
       klaunch(gather_kernel<bf16, 64, PACKED>, grid, 256, 0, st, (const bf16*)k, (const bf16*)v, idx, s.seq_start, s.Hkv,
-                                                            s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel);
+                                                            s.topk, ldv, (bf16*)k_sel, (bf16*)v_sel, status);
   } else {
     if (s.D == 128)
       klaunch(gather_kernel<float, 128, PACKED>, grid, 256, 0, st, (const float*)k, (const float*)v, idx, s.seq_start,
-                                                              s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel);
+                                                              s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel, status);
     else
       klaunch(gather_kernel<float, 64, PACKED>, grid, 256, 0, st, (const float*)k, (const float*)v, idx, s.seq_start,
-                                                             s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel);
+                                                             s.Hkv, s.topk, ldv, (float*)k_sel, (float*)v_sel, status);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
-                         hipStream_t st) {
-  return gather_dispatch<false>(s, k, v, idx, k_sel, v_sel, st);
+                         int32_t* status, hipStream_t st) {
+  return gather_dispatch<false>(s, k, v, idx, k_sel, v_sel, status, st);
 }
 
 // Host-pool path: `packed_k` / `packed_v` hold the picked rows as [nseq][Hkv][topk][D].
 hipError_t launch_layout_packed(const Shape& s, const void* packed_k, const void* packed_v, void* k_sel, void* v_sel,
                                 hipStream_t st) {
-  return gather_dispatch<true>(s, packed_k, packed_v, nullptr, k_sel, v_sel, st);
+  return gather_dispatch<true>(s, packed_k, packed_v, nullptr, k_sel, v_sel, nullptr, st);
 }
 
 }  // namespace herald

@@ -32,6 +32,9 @@ constexpr int kRefineScoreTileF32 = 64;  // candidates per fp32 score workgroup 
 // Keys per attention block and the largest supported candidate count.
 constexpr int kAttnKeyBlock = 64;
 constexpr int kMaxCandidates = 16384;
+// Largest subset size: every index arithmetic on a subset row offset (pick * head_dim,
+// d-row offsets of the d-major V pool) stays inside int32.
+constexpr int kMaxTopk = 1 << 24;
 
 struct Shape {
   int nseq, B, Hq, Hkv, D, G, C, topk;
@@ -113,11 +116,14 @@ hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const
                              bool stats, hipStream_t st);
 // gather
 hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
-                         hipStream_t st);
+                         int32_t* status, hipStream_t st);
 hipError_t launch_layout_packed(const Shape& s, const void* packed_k, const void* packed_v, void* k_sel, void* v_sel,
                                 hipStream_t st);
 // attention
 AttnGeom attn_geom(const Shape& s);
+// False when the attention work split has too many workgroups for the kernel's 32-bit
+// workgroup decode (checked on the host before any launch).
+bool attn_fits(const Shape& s);
 int attn_splits(const Shape& s);
 size_t attn_ws_bytes(const Shape& s);
 hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void* vb, const void* k_sel,

@@ -38,7 +38,7 @@ KERNEL_IDS = {
 }
 
 EXPORTED = [
-    "herald_workspace_size", "herald_vsel_ld", "herald_select_merged", "herald_select_query", "herald_refine_topk",
+    "herald_workspace_size", "herald_workspace_bytes", "herald_vsel_ld", "herald_select_merged", "herald_select_query", "herald_refine_topk",
     "herald_gather_kv", "herald_block_attn", "herald_last_error", "herald_set_kernel_events",
     "herald_attn_splits", "herald_compressed_rows", "herald_compress_keys", "herald_select_compressed",
 ]
@@ -83,6 +83,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.POINTER(herald_problem)
     sig = {
         "herald_workspace_size": ([P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+        "herald_workspace_bytes": ([P, ctypes.c_int], ctypes.c_size_t),
         "herald_vsel_ld": ([ctypes.c_int32], ctypes.c_int64),
         "herald_select_merged": ([P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "herald_select_query": ([P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
@@ -172,6 +173,14 @@ def herald_workspace_size(problem: Problem, op: int) -> int:
     n = ctypes.c_size_t(0)
     _check(load().herald_workspace_size(problem.ref, op, ctypes.byref(n)), "herald_workspace_size")
     return n.value
+
+
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+def herald_workspace_bytes(problem: Problem, op: int) -> int:
+    """The workspace size as the C call returns it: SIZE_MAX on error (no exception)."""
+    return int(load().herald_workspace_bytes(problem.ref, op))
 
 
 def herald_vsel_ld(topk: int) -> int:

@@ -77,7 +77,8 @@ typedef enum herald_op {
  *   nseq >= 0 (0 makes every call a no-op); 1 <= block_size <= 64;
  *   num_kv_heads >= 1; num_q_heads = G * num_kv_heads with 1 <= G <= 8;
  *   block_size * G <= 256; head_dim in {64, 128};
- *   1 <= topk <= num_candidates <= L_s <= 2^30 for every s; herald_select_merged (and
+ *   1 <= topk <= num_candidates <= L_s <= 2^30 for every s, topk <= 2^24
+ *   (HERALD_ERR_UNSUPPORTED above); herald_select_merged (and
  *   its workspace query) also needs num_candidates <= 16384 (HERALD_ERR_UNSUPPORTED
  *   otherwise). The other calls take any candidate count and subset size up to the
  *   shortest sequence, which expresses the exact baselines: refine over every key of
@@ -102,8 +103,15 @@ typedef struct herald_problem {
   const int64_t* seq_start_dev;
 } herald_problem;
 
-/* Bytes of device workspace `op` needs for problem `p` (written to *bytes). */
+/* Bytes of device workspace `op` needs for problem `p` (written to *bytes). Errors
+ * as the op itself reports them for the problem (HERALD_ERR_INVALID_ARG for an
+ * invalid problem or op, HERALD_ERR_UNSUPPORTED for a shape the op does not take). */
 herald_status herald_workspace_size(const herald_problem* p, int op, size_t* bytes);
+
+/* The same size as a return value: the workspace query in the form the caller sizes
+ * allocations with. Returns SIZE_MAX where herald_workspace_size returns an error
+ * (herald_last_error() then names it); 0 is a valid size (no workspace needed). */
+size_t herald_workspace_bytes(const herald_problem* p, int op);
 
 /* Leading dimension (elements) of each d-row of v_sel: topk rounded up to 64. */
 int64_t herald_vsel_ld(int32_t topk);
@@ -190,8 +198,12 @@ herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, 
  *   k_sel     [nseq][Hkv][topk][d]               device, written
  *   v_sel     [nseq][Hkv][d][herald_vsel_ld(topk)] device, written: V stored d-major
  *             (entry [s][g][e][i] = V[row of pick i][g][e]); padding columns are zero
- * Device path (src_is_host = 0): one kernel on `stream`; host_staging, host_idx and
- * ws may be NULL; `done`, when not NULL, is recorded after it.
+ * Device path (src_is_host = 0): one kernel on `stream`; host_staging and host_idx
+ * may be NULL; `done`, when not NULL, is recorded after it. An index outside
+ * [0, L_s) is never dereferenced: the kernel writes zero K and V rows for it. ws is
+ * then an optional status word (NULL, or a device int32, ws_bytes >= 4, 4-byte
+ * aligned) that the kernel sets to 1 when it met such an index; the caller clears it
+ * beforehand and reads it after the stream has passed the call.
  * Host-pool path (src_is_host = 1): `stream` should be a side stream. The call
  * copies topk_idx to host_idx (pinned, nseq*Hkv*topk int32), waits for `stream`,
  * packs the picked rows of k_src and v_src into host_staging (pinned,
@@ -204,8 +216,9 @@ herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, 
  * contiguous row), with no host work and no synchronisation, so it can run on a side
  * stream while the other stream computes, and be captured into a graph. k_src and
  * v_src must be pinned host memory (HERALD_ERR_INVALID_ARG otherwise, checked with
- * hipPointerGetAttributes); host_staging, host_idx and ws may be NULL; `done`, when
- * not NULL, is recorded after the kernel.
+ * hipPointerGetAttributes); host_staging and host_idx may be NULL; ws is the optional
+ * status word of the device path (out-of-range indices read nothing, as there);
+ * `done`, when not NULL, is recorded after the kernel.
  */
 herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const void* v_src,
                                int32_t src_is_host, const int32_t* topk_idx, void* k_sel, void* v_sel,
@@ -224,6 +237,8 @@ herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const
  *   ws     workspace of herald_workspace_size(HERALD_OP_ATTN) bytes, device: partial
  *          results when the subset is long enough to be split into key ranges;
  *          NULL allowed when that size is 0
+ * HERALD_ERR_UNSUPPORTED when the batch's work split exceeds the kernel's 32-bit
+ * workgroup numbering (far beyond any realistic batch; checked on the host).
  */
 herald_status herald_block_attn(const herald_problem* p, const void* q, const void* k_blk, const void* v_blk,
                                 const void* k_sel, const void* v_sel, void* out, void* ws, size_t ws_bytes,

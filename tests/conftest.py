@@ -4,8 +4,10 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-if ROOT not in sys.path:
-    sys.path.insert(0, ROOT)
+HERE = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, HERE):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
 
 
 def pytest_configure(config):
@@ -23,3 +25,15 @@ def gpu_lib():
 
     herald.load()
     return herald
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst attention error per workload against its tolerance (GPU parity runs)."""
+    from parity import MARGINS
+
+    if not MARGINS:
+        return
+    terminalreporter.section("attention parity margins (max abs error vs the oracle / tolerance)")
+    for name, (err, tol, count) in sorted(MARGINS.items()):
+        terminalreporter.write_line(f"{name}: {err:.3g} / {tol:g} ({err / tol:.1%} of the tolerance, "
+                                    f"{count} outputs)")

@@ -11,10 +11,23 @@ on the GPU's own selected subset.
 
 from __future__ import annotations
 
+import threading
+
 import numpy as np
 
 BAND = 1e-3
 ATOL = {"bf16": 2e-2, "f32": 1e-4}
+
+# worst attention error seen per workload: name -> (max abs error, tolerance, outputs compared);
+# printed in the test session's terminal summary so the margin to the tolerance is on record
+MARGINS: dict = {}
+_MARGINS_LOCK = threading.Lock()  # sequences are checked from a thread pool
+
+
+def record_margin(name: str, err: float, tol: float, count: int) -> None:
+    with _MARGINS_LOCK:
+        old = MARGINS.get(name, (0.0, tol, 0))
+        MARGINS[name] = (max(old[0], err), tol, old[2] + count)
 
 
 def band_check(gpu_idx: np.ndarray, score: np.ndarray, k: int, domain: np.ndarray | None = None, what: str = ""):

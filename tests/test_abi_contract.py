@@ -74,6 +74,52 @@ def test_workspace_sizes(lib):
     assert status_of(H.herald_workspace_size, p, 99) == H.HERALD_ERR_INVALID_ARG
 
 
+def test_workspace_bytes_matches_workspace_size(lib):
+    """herald_workspace_bytes returns what herald_workspace_size writes, SIZE_MAX on error."""
+    for p in (prob(), prob(seq_start=[0, 32768], Hq=32, Hkv=8, C=4096, topk=1024), prob(dtype=H.HERALD_F32),
+              prob(seq_start=[0])):
+        for op in (H.HERALD_OP_SELECT, H.HERALD_OP_REFINE, H.HERALD_OP_ATTN, H.HERALD_OP_GATHER_HOST,
+                   H.HERALD_OP_SELECT_COMPRESSED):
+            assert H.herald_workspace_bytes(p, op) == H.herald_workspace_size(p, op)
+    assert H.herald_workspace_bytes(prob(), 99) == H.SIZE_MAX
+    assert "unknown op" in H.herald_last_error()
+    assert H.herald_workspace_bytes(prob(Hq=9), H.HERALD_OP_REFINE) == H.SIZE_MAX
+    big = prob(C=30000, topk=30000, seq_start=[0, 30000, 61000])
+    assert H.herald_workspace_bytes(big, H.HERALD_OP_SELECT) == H.SIZE_MAX  # selection takes C <= 16384
+
+
+def test_subset_and_work_split_bounds(lib):
+    """Subsets beyond 2^24 keys and attention work splits beyond the kernel's 32-bit
+    workgroup numbering are refused on the host, before any launch."""
+    n = 1 << 24
+    ok = prob(seq_start=[0, n], B=1, Hq=8, Hkv=8, C=n, topk=n)
+    assert H.herald_workspace_size(ok, H.HERALD_OP_ATTN) > 0
+    over = prob(seq_start=[0, n + 1], B=1, Hq=8, Hkv=8, C=n + 1, topk=n + 1)
+    assert status_of(H.herald_workspace_size, over, H.HERALD_OP_ATTN) == H.HERALD_ERR_UNSUPPORTED
+    assert status_of(H.herald_block_attn, over, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == \
+        H.HERALD_ERR_UNSUPPORTED
+    assert status_of(H.herald_gather_kv, over, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, None, 0, 0, None) == \
+        H.HERALD_ERR_UNSUPPORTED
+    # 200 sequences x 8 KV heads, 8193 key ranges each: 13.1M workgroups, beyond the decode
+    wide = prob(seq_start=[i * n for i in range(201)], B=1, Hq=8, Hkv=8, C=n, topk=n)
+    assert status_of(H.herald_workspace_size, wide, H.HERALD_OP_ATTN) == H.HERALD_ERR_UNSUPPORTED
+    assert H.herald_workspace_bytes(wide, H.HERALD_OP_ATTN) == H.SIZE_MAX
+    assert status_of(H.herald_block_attn, wide, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == \
+        H.HERALD_ERR_UNSUPPORTED
+    assert H.herald_workspace_size(wide, H.HERALD_OP_REFINE) > 0  # the other calls are not limited by it
+
+
+def test_gather_status_word_checks(lib):
+    """The device and GPU-read gathers take an optional 4-byte status word in ws."""
+    p = prob()
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, FAKE, 3, 0, None) == \
+        H.HERALD_ERR_WORKSPACE
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, FAKE + 2, 4, 0, None) == \
+        H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_gather_kv, p, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, None, FAKE, 3, 0, None) == \
+        H.HERALD_ERR_WORKSPACE
+
+
 def test_vsel_ld(lib):
     assert H.herald_vsel_ld(1) == 64
     assert H.herald_vsel_ld(64) == 64
@@ -206,6 +252,8 @@ def test_kernel_events_argument_checks(lib):
 
 def test_attn_splits_reported(lib):
     assert 1 <= H.herald_attn_splits(prob()) <= 32
+    assert H.herald_attn_splits(prob(seq_start=[0])) >= 1  # empty batch: host geometry must not divide by zero
+    assert H.herald_workspace_size(prob(seq_start=[0]), H.HERALD_OP_ATTN) == 0
     assert H.herald_attn_splits(prob(dtype=H.HERALD_F32)) == 1
 
 

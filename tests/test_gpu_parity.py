@@ -10,12 +10,15 @@ Stage by stage, on seeded inputs that span several tiles and ragged tails:
      2e-2 (bf16) / 1e-4 (fp32);
   P5 planted keys are selected; P6 strict ties; P7 bit-identical reruns.
 Full-size workloads run in the launch configuration the benchmark times and are
-checked on sampled sequences and steps.
+checked on every sequence and every denoising step (the oracle runs per sequence in
+a thread pool; numpy releases the interpreter lock in its loops).
 """
 
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -25,7 +28,9 @@ import oracle.herald_oracle as orc
 from block_diffusion_sparse_herald_amd import herald as H
 from block_diffusion_sparse_herald_amd.inputs import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_batch
 from block_diffusion_sparse_herald_amd.runner import BlockRunner, batch_to_device, device_tensor
-from parity import ATOL, band_check, max_abs
+from threadpoolctl import threadpool_limits
+
+from parity import ATOL, band_check, max_abs, record_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -176,8 +181,18 @@ def check_sequence(run: Run, s: int, steps, stage_isolated: bool = True):
         err = max_abs(widen(run.out[t][s]), want)
         worst = max(worst, err)
         assert err <= ATOL[wl.dtype], f"{wl.name} s{s} t{t}: attention max abs error {err}"
+    record_margin(wl.name, worst, ATOL[wl.dtype], len(steps) * run.out[steps[0]][s].size if steps else 0)
     log(f"  {wl.name} s{s}: band {band}, attention max abs err {worst:.3g}")
     return cand_o
+
+
+def oracle_pool(n: int) -> ThreadPoolExecutor:
+    """Threads for per-sequence oracle checks (at most the 16 cores a one-GPU share has)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return ThreadPoolExecutor(max_workers=max(1, min(n, cores, 16)))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -267,7 +282,10 @@ def test_rerun_is_bit_identical():
         assert np.array_equal(a.out[t], b.out[t])
 
 
-def test_host_pool_gather_matches_device_gather():
+def test_host_pool_gathers_match_the_oracle():
+    """Both host-pool paths (host-packed and GPU-read) and the device path are each
+    compared bit for bit with the oracle's gather of the cache rows (V transposed into
+    the d-major pool, padding zero)."""
     wl = SMALL["ragged_g7_L1500-6000"]
     run = Run(wl, steps=[])
     r = run.runner
@@ -279,30 +297,82 @@ def test_host_pool_gather_matches_device_gather():
     staging = torch.empty(2 * n * wl.d, dtype=kh.dtype, pin_memory=True)
     host_idx = torch.empty(n, dtype=torch.int32, pin_memory=True)
     ws = torch.empty(H.herald_workspace_size(r.problem, H.HERALD_OP_GATHER_HOST), dtype=torch.uint8, device="cuda")
-    k_sel = torch.zeros_like(r.k_sel)
-    v_sel = torch.full_like(r.v_sel, 7.0)
     side = torch.cuda.Stream()
     done = torch.cuda.Event()
     done.record(side)  # creates the event
-    side.wait_stream(torch.cuda.current_stream())
-    H.herald_gather_kv(r.problem, kh, vh, 1, r.sel, k_sel, v_sel, staging, host_idx, ws, stream=side, done=done)
-    torch.cuda.current_stream().wait_event(done)
-    torch.cuda.synchronize()
-    assert torch.equal(k_sel.view(torch.int16), r.k_sel.view(torch.int16))
-    assert torch.equal(v_sel.view(torch.int16), r.v_sel.view(torch.int16))
-    # the GPU reading the pinned pool itself (no staging, no host work), on the side stream
-    k_sel.zero_()
-    v_sel.fill_(7.0)
-    side.wait_stream(torch.cuda.current_stream())
-    H.herald_gather_kv(r.problem, kh, vh, 2, r.sel, k_sel, v_sel, None, None, None, stream=side, done=done)
-    torch.cuda.current_stream().wait_event(done)
-    torch.cuda.synchronize()
-    assert torch.equal(k_sel.view(torch.int16), r.k_sel.view(torch.int16))
-    assert torch.equal(v_sel.view(torch.int16), r.v_sel.view(torch.int16))
-    # device memory is refused on that path
+
+    def check(k_sel, v_sel, what):
+        ks, vs = to_np(k_sel), to_np(v_sel)
+        for s in range(wl.nseq):
+            a, e = int(run.batch.seq_start[s]), int(run.batch.seq_start[s + 1])
+            want_k, want_v = orc.gather_kv(run.batch.k_cache[a:e], run.batch.v_cache[a:e], run.sel[s])
+            for g in range(wl.Hkv):
+                assert np.array_equal(ks[s, g], want_k[g]), f"{what}: k_sel s{s} g{g}"
+                assert np.array_equal(vs[s, g, :, :wl.topk], want_v[g].T), f"{what}: v_sel s{s} g{g}"
+                assert not vs[s, g, :, wl.topk:].any(), f"{what}: v_sel padding s{s} g{g}"
+
+    check(r.k_sel, r.v_sel, "device gather")
+    for src_is_host in (1, 2):
+        k_sel = torch.zeros_like(r.k_sel)
+        v_sel = torch.full_like(r.v_sel, 7.0)
+        side.wait_stream(torch.cuda.current_stream())
+        if src_is_host == 1:
+            H.herald_gather_kv(r.problem, kh, vh, 1, r.sel, k_sel, v_sel, staging, host_idx, ws, stream=side,
+                               done=done)
+        else:  # the GPU reading the pinned pool itself (no staging, no host work), on the side stream
+            H.herald_gather_kv(r.problem, kh, vh, 2, r.sel, k_sel, v_sel, None, None, None, stream=side, done=done)
+        torch.cuda.current_stream().wait_event(done)
+        torch.cuda.synchronize()
+        check(k_sel, v_sel, f"host-pool gather (src_is_host = {src_is_host})")
+    # device memory is refused on the GPU-read path
     with pytest.raises(H.HeraldError):
         H.herald_gather_kv(r.problem, run.dev["k_cache"], run.dev["v_cache"], 2, r.sel, k_sel, v_sel, None, None,
                            None, stream=side)
+
+
+@pytest.mark.parametrize("src_is_host", [0, 2])
+def test_gather_out_of_range_indices(src_is_host):
+    """Indices outside [0, L_s) are never dereferenced: their rows come out zero and the
+    status word is set; in-range indices leave it clear. Device and GPU-read paths."""
+    wl = SMALL["gqa32x8_L5000_b2"]
+    batch = make_batch(wl, steps=1)
+    dev = batch_to_device(batch)
+    r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype)
+    L = batch.lengths
+    rng = np.random.default_rng(5)
+    sel = np.stack([np.stack([np.sort(rng.choice(int(L[s]), wl.topk, replace=False)) for _ in range(wl.Hkv)])
+                    for s in range(wl.nseq)]).astype(np.int32)
+    bad = sel.copy()
+    bad[0, 1, 3] = -1
+    bad[1, 0, 7] = int(L[1])  # one past the end of sequence 1
+    bad[1, 3, wl.topk - 1] = 2**31 - 1
+    if src_is_host:
+        k_src = torch.empty(dev["k_cache"].shape, dtype=dev["k_cache"].dtype, pin_memory=True)
+        v_src = torch.empty(dev["v_cache"].shape, dtype=dev["v_cache"].dtype, pin_memory=True)
+        k_src.copy_(dev["k_cache"].cpu())
+        v_src.copy_(dev["v_cache"].cpu())
+    else:
+        k_src, v_src = dev["k_cache"], dev["v_cache"]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for idx, want_status in ((sel, 0), (bad, 1)):
+        k_sel = torch.full_like(r.k_sel, 3.0)
+        v_sel = torch.full_like(r.v_sel, 3.0)
+        status.zero_()
+        H.herald_gather_kv(r.problem, k_src, v_src, src_is_host, torch.from_numpy(idx).cuda(), k_sel, v_sel,
+                           None, None, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == want_status
+        ks, vs = to_np(k_sel), to_np(v_sel)
+        for s in range(wl.nseq):
+            a = int(batch.seq_start[s])
+            for g in range(wl.Hkv):
+                ok = (idx[s, g] >= 0) & (idx[s, g] < L[s])
+                rows = np.zeros((wl.topk, wl.d), dtype=np.uint16)
+                rows[ok] = batch.k_cache[a + idx[s, g][ok], g]
+                assert np.array_equal(ks[s, g], rows), f"k_sel s{s} g{g}"
+                vrows = np.zeros((wl.topk, wl.d), dtype=np.uint16)
+                vrows[ok] = batch.v_cache[a + idx[s, g][ok], g]
+                assert np.array_equal(vs[s, g, :, :wl.topk], vrows.T), f"v_sel s{s} g{g}"
 
 
 def test_kernel_events_time_the_scan():
@@ -327,19 +397,31 @@ FULL = ["tiny_f32_L4096", "gqa32x8_L32768_b1", "gqa32x8_L32768_b16", "gqa32x8_L1
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
-    """Full-size workload, bench launch configuration; oracle on the first and last sequence and step."""
+def test_full_size(name):
+    """Full-size workload in the benchmark's launch configuration: every sequence and
+    every denoising step against the oracle (P1-P5), then the oracle's own candidates of
+    every sequence through the GPU refine (stage-isolated P2)."""
     wl = WORKLOADS[name]
     log(f"[full] {name}: generating")
-    steps = sorted({0, wl.T - 1})
-    run = Run(wl, steps=steps)
-    seqs = sorted({0, wl.nseq - 1})
-    if name == "gqa28x4_ragged16k-64k_b8":
-        L = run.batch.lengths
-        seqs = sorted({int(np.argmin(L)), int(np.argmax(L))})
-    for s in seqs:
-        log(f"[full] {name}: oracle on sequence {s}")
-        check_sequence(run, s, steps)
+    run = Run(wl)
+    log(f"[full] {name}: oracle on {wl.nseq} sequence(s) x {wl.T} step(s)")
+    with oracle_pool(wl.nseq) as ex, threadpool_limits(limits=1):
+        cands = list(ex.map(lambda s: check_sequence(run, s, run.steps), range(wl.nseq)))
+    cand_dev = torch.from_numpy(np.stack(cands).astype(np.int32)).cuda()
+    run.runner.refine(run.dev["q0"], run.dev["k_cache"], cand=cand_dev)
+    torch.cuda.synchronize()
+    sel = to_np(run.runner.sel).astype(np.int64)
+    scale = orc.default_scale(wl.d)
+
+    def isolated(s):
+        q0, k, _ = run.seq(s)
+        R = orc.refine_scores(q0, k, cands[s], scale)
+        for g in range(wl.Hkv):
+            band_check(sel[s, g], R[g], wl.topk, domain=cands[s][g], what=f"{name} s{s} g{g} refine stage-isolated")
+
+    log(f"[full] {name}: stage-isolated refine")
+    with oracle_pool(wl.nseq) as ex, threadpool_limits(limits=1):
+        list(ex.map(isolated, range(wl.nseq)))
     del run
     torch.cuda.empty_cache()
 
