@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -262,6 +263,36 @@ herald_status check_ws(void* ws, size_t have, size_t need) {
 
 }  // namespace
 
+// Scratch of herald_block_attn_static: one array per GPU the library runs on, held
+// until the process ends. Host code never uses its name as an address (that would be
+// the host-side shadow); static_scratch looks up the device address once per device.
+static __device__ __align__(256) unsigned char scratch[HERALD_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on the first call on each
+// device, with that device current).
+herald_status static_scratch(void** out) {
+  int dev = -1;
+  HERALD_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HERALD_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HERALD_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(HERALD_ERR_HIP, "hipGetSymbolAddress returned NULL for the static scratch");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HERALD_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 herald_status herald_workspace_size(const herald_problem* p, int op, size_t* bytes) {
@@ -499,23 +530,49 @@ herald_status herald_gather_kv(const herald_problem* p, const void* k_src, const
   return ok();
 }
 
-herald_status herald_block_attn(const herald_problem* p, const void* q, const void* k_blk, const void* v_blk,
-                                const void* k_sel, const void* v_sel, void* out, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
-  Shape s;
-  HERALD_TRY(make_shape(p, &s));
-  if (s.nseq == 0) return ok();
+// Validation shared by both attention entry points (host memory only).
+static herald_status attn_validate(const herald_problem* p, Shape* s, const void* q, const void* k_blk,
+                                   const void* v_blk, const void* k_sel, const void* v_sel, const void* out) {
+  HERALD_TRY(make_shape(p, s));
+  if (s->nseq == 0) return HERALD_OK;
   HERALD_TRY(check_ptr(q, "q"));
   HERALD_TRY(check_ptr(k_blk, "k_blk"));
   HERALD_TRY(check_ptr(v_blk, "v_blk"));
   HERALD_TRY(check_ptr(k_sel, "k_sel"));
   HERALD_TRY(check_ptr(v_sel, "v_sel"));
   HERALD_TRY(check_ptr(out, "out"));
-  HERALD_TRY(check_attn_shape(s));
-  HERALD_TRY(check_ws(ws, ws_bytes, attn_ws_bytes(s)));
+  return check_attn_shape(*s);
+}
+
+static herald_status attn_launch(const Shape& s, const void* q, const void* k_blk, const void* v_blk,
+                                 const void* k_sel, const void* v_sel, void* out, void* ws, hipStream_t stream) {
   HERALD_LAUNCH(8, stream, launch_attn(s, q, k_blk, v_blk, k_sel, v_sel, out, ws, stream));
   if (attn_splits(s) > 1) HERALD_LAUNCH(9, stream, launch_attn_combine(s, ws, out, stream));
   return ok();
+}
+
+herald_status herald_block_attn(const herald_problem* p, const void* q, const void* k_blk, const void* v_blk,
+                                const void* k_sel, const void* v_sel, void* out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  Shape s;
+  HERALD_TRY(attn_validate(p, &s, q, k_blk, v_blk, k_sel, v_sel, out));
+  if (s.nseq == 0) return ok();
+  HERALD_TRY(check_ws(ws, ws_bytes, attn_ws_bytes(s)));
+  return attn_launch(s, q, k_blk, v_blk, k_sel, v_sel, out, ws, stream);
+}
+
+herald_status herald_block_attn_static(const herald_problem* p, const void* q, const void* k_blk, const void* v_blk,
+                                       const void* k_sel, const void* v_sel, void* out, hipStream_t stream) {
+  Shape s;
+  HERALD_TRY(attn_validate(p, &s, q, k_blk, v_blk, k_sel, v_sel, out));
+  if (s.nseq == 0) return ok();
+  const size_t need = attn_ws_bytes(s);
+  if (need > HERALD_STATIC_SCRATCH_BYTES)
+    return fail(HERALD_ERR_UNSUPPORTED, "the split attention needs %zu bytes of scratch; the static buffer holds %zu",
+                need, (size_t)HERALD_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) HERALD_TRY(static_scratch(&ws));
+  return attn_launch(s, q, k_blk, v_blk, k_sel, v_sel, out, ws, stream);
 }
 
 const char* herald_last_error(void) { return g_error.c_str(); }

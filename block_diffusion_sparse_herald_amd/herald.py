@@ -39,7 +39,7 @@ KERNEL_IDS = {
 
 EXPORTED = [
     "herald_workspace_size", "herald_workspace_bytes", "herald_vsel_ld", "herald_select_merged", "herald_select_query", "herald_refine_topk",
-    "herald_gather_kv", "herald_block_attn", "herald_last_error", "herald_set_kernel_events",
+    "herald_gather_kv", "herald_block_attn", "herald_block_attn_static", "herald_last_error", "herald_set_kernel_events",
     "herald_attn_splits", "herald_compressed_rows", "herald_compress_keys", "herald_select_compressed",
 ]
 
@@ -94,6 +94,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "herald_gather_kv": ([P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp],
                              ctypes.c_int),
         "herald_block_attn": ([P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "herald_block_attn_static": ([P, _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
         "herald_last_error": ([], ctypes.c_char_p),
         "herald_set_kernel_events": ([ctypes.c_int32, _vp, _vp], ctypes.c_int),
         "herald_attn_splits": ([P], ctypes.c_int32),
@@ -244,6 +245,16 @@ def herald_block_attn(problem: Problem, q, k_blk, v_blk, k_sel, v_sel, out, ws, 
                                     _ptr(out), _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes,
                                     _stream(stream)),
            "herald_block_attn")
+
+
+HERALD_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def herald_block_attn_static(problem: Problem, q, k_blk, v_blk, k_sel, v_sel, out, stream=None) -> None:
+    """herald_block_attn with its partial results in the library's static device scratch."""
+    _check(load().herald_block_attn_static(problem.ref, _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_sel), _ptr(v_sel),
+                                           _ptr(out), _stream(stream)),
+           "herald_block_attn_static")
 
 
 def herald_last_error() -> str:

@@ -244,6 +244,24 @@ herald_status herald_block_attn(const herald_problem* p, const void* q, const vo
                                 const void* k_sel, const void* v_sel, void* out, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/*
+ * herald_block_attn without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, kernels, results and errors as herald_block_attn,
+ * minus ws / ws_bytes: the split-range partial results go to a static device array of
+ * HERALD_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on until
+ * the process ends. The call allocates nothing. A problem whose attention workspace
+ * (herald_workspace_size(HERALD_OP_ATTN)) exceeds that size is refused with
+ * HERALD_ERR_UNSUPPORTED before any HIP call. Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (concurrent streams, or threads) race and give
+ * undefined results; calls ordered on one stream do not. The first call on a device
+ * looks up the array's device address (hipGetSymbolAddress) with that device current.
+ */
+#define HERALD_STATIC_SCRATCH_BYTES (16u << 20)
+herald_status herald_block_attn_static(const herald_problem* p, const void* q, const void* k_blk,
+                                       const void* v_blk, const void* k_sel, const void* v_sel, void* out,
+                                       hipStream_t stream);
+
 /* Message for the last non-OK status on the calling thread ("" if none). Valid
  * until the next call on this thread. */
 const char* herald_last_error(void);

@@ -109,6 +109,28 @@ def test_subset_and_work_split_bounds(lib):
     assert H.herald_workspace_size(wide, H.HERALD_OP_REFINE) > 0  # the other calls are not limited by it
 
 
+def test_block_attn_static_contract(lib):
+    """The allocation-free attention validates like herald_block_attn and refuses, before any
+    HIP call, a problem whose attention workspace exceeds its static scratch."""
+    p = prob()
+    assert status_of(H.herald_block_attn_static, p, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0) == H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_block_attn_static, p, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == \
+        H.HERALD_ERR_INVALID_ARG
+    assert status_of(H.herald_block_attn_static, prob(Hq=9), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == \
+        H.HERALD_ERR_INVALID_ARG
+    H.herald_block_attn_static(prob(seq_start=[0]), None, None, None, None, None, None, 0)  # empty batch: no-op
+    # dense attention over whole 32K caches: the split partials outgrow the static buffer
+    n = 1
+    while True:
+        big = prob(seq_start=[32768 * i for i in range(n + 1)], Hq=32, Hkv=8, C=32768, topk=32768)
+        if H.herald_workspace_size(big, H.HERALD_OP_ATTN) > H.HERALD_STATIC_SCRATCH_BYTES:
+            break
+        n += 1
+    assert status_of(H.herald_block_attn_static, big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == \
+        H.HERALD_ERR_UNSUPPORTED
+    assert "static" in H.herald_last_error()
+
+
 def test_gather_status_word_checks(lib):
     """The device and GPU-read gathers take an optional 4-byte status word in ws."""
     p = prob()
