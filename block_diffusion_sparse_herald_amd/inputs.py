@@ -44,6 +44,7 @@ __all__ = [
     "WORKLOADS",
     "Batch",
     "make_batch",
+    "make_blocks",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
 ]
@@ -146,6 +147,17 @@ class Batch:
         return a.astype(np.float64)
 
 
+def _channel_scales(wl: Workload, gen: np.random.Generator):
+    """Per-channel scales of Q, K and V (one vector per head per tensor), ones unless channel_scaled."""
+    if wl.law == "channel_scaled":
+        sq = gen.uniform(0.5, 2.0, size=(wl.Hq, wl.d)).astype(np.float32)
+        sk = gen.uniform(0.5, 2.0, size=(wl.Hkv, wl.d)).astype(np.float32)
+        sv = gen.uniform(0.5, 2.0, size=(wl.Hkv, wl.d)).astype(np.float32)
+        return sq, sk, sv
+    return (np.ones((wl.Hq, wl.d), np.float32), np.ones((wl.Hkv, wl.d), np.float32),
+            np.ones((wl.Hkv, wl.d), np.float32))
+
+
 def _lengths(wl: Workload) -> np.ndarray:
     if wl.L_min is None:
         return np.full(wl.nseq, wl.L, dtype=np.int64)
@@ -183,14 +195,7 @@ def make_batch(wl: Workload, steps: Optional[int] = None) -> Batch:
         streams = dict(zip(names, np.random.SeedSequence(wl.seed_base + s).spawn(len(names))))
         gen = {n: np.random.Generator(np.random.PCG64(ss)) for n, ss in streams.items()}
 
-        if wl.law == "channel_scaled":
-            sq = gen["scale"].uniform(0.5, 2.0, size=(wl.Hq, wl.d)).astype(np.float32)
-            sk = gen["scale"].uniform(0.5, 2.0, size=(wl.Hkv, wl.d)).astype(np.float32)
-            sv = gen["scale"].uniform(0.5, 2.0, size=(wl.Hkv, wl.d)).astype(np.float32)
-        else:
-            sq = np.ones((wl.Hq, wl.d), np.float32)
-            sk = np.ones((wl.Hkv, wl.d), np.float32)
-            sv = np.ones((wl.Hkv, wl.d), np.float32)
+        sq, sk, sv = _channel_scales(wl, gen["scale"])
 
         qs = finish(gen["q"].standard_normal((wl.B, wl.Hq, wl.d), dtype=np.float32) * sq)
         q0[s] = qs
@@ -236,3 +241,34 @@ def make_batch(wl: Workload, steps: Optional[int] = None) -> Batch:
             vb_steps[t, s] = finish(st.standard_normal((wl.B, wl.Hkv, wl.d), dtype=np.float32) * sv)
 
     return Batch(wl, seq_start, q0, k_cache, v_cache, q_steps, kb_steps, vb_steps, planted)
+
+
+def make_blocks(wl: Workload, batch: Batch, nblocks: int) -> list:
+    """Inputs of nblocks consecutive blocks over the batch's cache: block 0 is the batch's own
+    (q0, q_steps, kb_steps, vb_steps); block i >= 1 draws its own queries and per-step
+    in-block keys and values, with the sequence's channel scales, from a stream named by
+    (seed_base + s, block i). The cache is the same for every block. Each entry is a dict
+    with "q0" [nseq][B][Hq][d] and "q_steps", "kb_steps", "vb_steps" [T][nseq][B][H][d]."""
+    blocks = [{"q0": batch.q0, "q_steps": batch.q_steps, "kb_steps": batch.kb_steps, "vb_steps": batch.vb_steps}]
+    bf16 = wl.dtype == "bf16"
+    T = batch.q_steps.shape[0]
+
+    def finish(x: np.ndarray) -> np.ndarray:
+        return f32_to_bf16_bits(x) if bf16 else x.astype(np.float32)
+
+    for i in range(1, nblocks):
+        q0 = np.empty_like(batch.q0)
+        q_steps, kb_steps, vb_steps = (np.empty_like(a) for a in (batch.q_steps, batch.kb_steps, batch.vb_steps))
+        for s in range(wl.nseq):
+            names = ["q", "k", "v", "scale", "plant", "outlier", "drift", "steps"]
+            scale_ss = np.random.SeedSequence(wl.seed_base + s).spawn(len(names))[names.index("scale")]
+            sq, sk, sv = _channel_scales(wl, np.random.Generator(np.random.PCG64(scale_ss)))
+            st = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed_base + s, 7_000_000 + i])))
+            q0[s] = finish(st.standard_normal((wl.B, wl.Hq, wl.d), dtype=np.float32) * sq)
+            for t in range(T):
+                q_steps[t, s] = q0[s] if t == 0 else finish(st.standard_normal((wl.B, wl.Hq, wl.d),
+                                                                               dtype=np.float32) * sq)
+                kb_steps[t, s] = finish(st.standard_normal((wl.B, wl.Hkv, wl.d), dtype=np.float32) * sk)
+                vb_steps[t, s] = finish(st.standard_normal((wl.B, wl.Hkv, wl.d), dtype=np.float32) * sv)
+        blocks.append({"q0": q0, "q_steps": q_steps, "kb_steps": kb_steps, "vb_steps": vb_steps})
+    return blocks

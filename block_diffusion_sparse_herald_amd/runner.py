@@ -109,3 +109,116 @@ class BlockRunner:
         self.gather(k_cache, v_cache, stream=stream)
         for t in range(q_steps.shape[0]):
             self.attn(q_steps[t], kb_steps[t], vb_steps[t], None if outs is None else outs[t], stream)
+
+
+def _pick(x, i: int):
+    """Copy i % len(x) of a list of copies, or x itself."""
+    return x[i % len(x)] if isinstance(x, (list, tuple)) else x
+
+
+class StreamOps:
+    """Streams and events of the caller's runtime: new_event() -> event,
+    record(event, stream), wait(stream, event) (the stream waits for the event's work)."""
+
+    def __init__(self, new_event: Callable, record: Callable, wait: Callable):
+        self.new_event, self.record, self.wait = new_event, record, wait
+
+    @staticmethod
+    def torch() -> "StreamOps":
+        import torch
+
+        return StreamOps(torch.cuda.Event, lambda ev, st: ev.record(st), lambda st, ev: st.wait_event(ev))
+
+    @staticmethod
+    def hip(hip) -> "StreamOps":
+        return StreamOps(hip.event, lambda ev, st: hip.record(ev, st), lambda st, ev: hip.wait(st, ev))
+
+
+class SpeculativePipeline:
+    """The per-block path as a two-stream pipeline over two sparse KV pools.
+
+    Block i's candidates come from the previous block's queries merged into one per head
+    (the speculative search; block 0 searches with its own), its final subset from
+    refining those candidates with block i's own queries, gathered into pool i % 2; then
+    its T attention steps read that pool. The `search` stream runs block i+1's search
+    while the `denoise` stream runs block i's steps. With overlap_refine False, block
+    i+1's refine and gather wait for block i's last step (in a decoder the next block's
+    queries exist only then); with True they follow its search on the search stream (the
+    next block's queries taken as given), so the fetch into the other pool also overlaps
+    block i. A pool is refilled only after the steps of the block two before are done.
+    """
+
+    def __init__(self, r: BlockRunner, alloc: Callable, ops: StreamOps, src_is_host: int = 0,
+                 overlap_refine: bool = False):
+        self.r, self.ops, self.src_is_host, self.overlap_refine = r, ops, src_is_host, overlap_refine
+        el = np.uint16 if r.dtype == H.HERALD_BF16 else np.float32
+        self.sel = [r.sel, alloc((r.nseq, r.Hkv, r.topk), np.int32)]
+        self.pools = [(r.k_sel, r.v_sel), (alloc((r.nseq, r.Hkv, r.topk, r.d), el), alloc((r.nseq, r.Hkv, r.d, r.ldv), el))]
+        self.fetched = [ops.new_event(), ops.new_event()]   # pool p holds its block's subset
+        self.consumed = [ops.new_event(), ops.new_event()]  # pool p's block finished its steps
+
+    def run(self, blocks, k_cache, k_src, v_src, denoise, search, outs=None, cands=None, sels=None):
+        """blocks[i]: dict of device tensors or addresses "q0" [nseq][B][Hq][d] and lists
+        "q_steps", "kb_steps", "vb_steps" (one per step). k_cache: device K cache for the
+        search and refine; k_src, v_src: where the gather reads the subset (the device cache,
+        or a pinned host pool when src_is_host = 2); each may also be a list of copies, block
+        i using copy i % len. outs[i][t] receives block i's step t (default: the runner's
+        output); cands[i] / sels[i], when given, receive block i's candidates / final subset
+        (default: the runner's buffers, reused)."""
+        r, ops, n = self.r, self.ops, len(blocks)
+
+        def search_block(i):
+            cand = r.cand if cands is None else cands[i]
+            H.herald_select_merged(r.problem, blocks[max(i - 1, 0)]["q0"], _pick(k_cache, i), cand, r.cand_score,
+                                   r.ws["select"], stream=search)
+
+        def refine_fetch(i):
+            p = i % 2
+            cand = r.cand if cands is None else cands[i]
+            sel = self.sel[p] if sels is None else sels[i]
+            H.herald_refine_topk(r.problem, blocks[i]["q0"], _pick(k_cache, i), cand, sel, r.sel_score,
+                                 r.ws["refine"], stream=search)
+            if i >= 2:
+                ops.wait(search, self.consumed[p])  # block i-2 is done with this pool
+            H.herald_gather_kv(r.problem, _pick(k_src, i), _pick(v_src, i), self.src_is_host, sel, self.pools[p][0],
+                               self.pools[p][1], stream=search)
+            ops.record(self.fetched[p], search)
+
+        def denoise_block(i):
+            p = i % 2
+            ops.wait(denoise, self.fetched[p])
+            b = blocks[i]
+            for t in range(len(b["q_steps"])):
+                out = r.out if outs is None else outs[i][t]
+                H.herald_block_attn(r.problem, b["q_steps"][t], b["kb_steps"][t], b["vb_steps"][t], self.pools[p][0],
+                                    self.pools[p][1], out, r.ws["attn"], stream=denoise)
+            ops.record(self.consumed[p], denoise)
+
+        search_block(0)
+        refine_fetch(0)
+        for i in range(n):
+            denoise_block(i)
+            if i + 1 < n:
+                search_block(i + 1)  # overlaps block i's steps
+                if not self.overlap_refine:
+                    ops.wait(search, self.consumed[i % 2])
+                refine_fetch(i + 1)
+
+    def run_serial(self, blocks, k_cache, k_src, v_src, stream, outs=None, cands=None, sels=None):
+        """The same calls, in the same order per block, on one stream (the reference schedule)."""
+        r, n = self.r, len(blocks)
+        for i in range(n):
+            p = i % 2
+            cand = r.cand if cands is None else cands[i]
+            sel = self.sel[p] if sels is None else sels[i]
+            H.herald_select_merged(r.problem, blocks[max(i - 1, 0)]["q0"], _pick(k_cache, i), cand, r.cand_score,
+                                   r.ws["select"], stream=stream)
+            H.herald_refine_topk(r.problem, blocks[i]["q0"], _pick(k_cache, i), cand, sel, r.sel_score,
+                                 r.ws["refine"], stream=stream)
+            H.herald_gather_kv(r.problem, _pick(k_src, i), _pick(v_src, i), self.src_is_host, sel, self.pools[p][0],
+                               self.pools[p][1], stream=stream)
+            b = blocks[i]
+            for t in range(len(b["q_steps"])):
+                out = r.out if outs is None else outs[i][t]
+                H.herald_block_attn(r.problem, b["q_steps"][t], b["kb_steps"][t], b["vb_steps"][t], self.pools[p][0],
+                                    self.pools[p][1], out, r.ws["attn"], stream=stream)
