@@ -177,11 +177,11 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
   // The query fragments (and in-block rows) are the only loads the compiler tracks.
-  // When blocks are refilled inside the loop, waiting for them here, once, keeps the
-  // compiler from placing that wait inside the loop, where (the direct-to-LDS transfers
-  // being invisible to it) it would be a full vmcnt(0) that also drains every block
-  // prefetched since. When every block is fetched up front it costs more than it saves.
-  if (nb > nst) wait_vm<0>();
+  // Waiting for them here, once, on every path, keeps the compiler from placing that
+  // wait inside the loop, where (the direct-to-LDS transfers being invisible to it) it
+  // would be a full vmcnt(0) in every round, draining the blocks prefetched for the
+  // next round before this one computes.
+  wait_vm<0>();
 
   for (int j = 0; j < nb; j += 2) {
     // wait for this wave's loads of the subset blocks among j, j + 1
