@@ -28,7 +28,9 @@
 // With several key ranges each workgroup writes a partial (fp32 max and sum, the
 // unnormalised output in fp32) that attn_combine_kernel merges; the output is rounded
 // to bf16 once, at the end. The running sum adds the probabilities as rounded to bf16
-// for the second product, so the applied weights are normalised exactly.
+// for the second product, so the applied weights are normalised up to fp32 rounding.
+// Built with -fno-honor-nans (non-finite inputs are outside the contract): the max
+// reductions then need no NaN-quieting operations.
 // fp32 path (attn_f32_kernel): four query rows per workgroup, VALU, keys in chunks of 128.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -262,16 +264,18 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
                           pack_bf16x2(p[2 * h2 + 1][0], p[2 * h2 + 1][1]),
                           pack_bf16x2(p[2 * h2 + 1][2], p[2 * h2 + 1][3]));
     // the normaliser sums the probabilities as the product below uses them (rounded to
-    // bf16), so the weights applied to the values sum to one exactly: a query whose
-    // attention falls on a few keys gets their values back without the weights' rounding
-    float ps = 0.f;
+    // bf16), so the weights applied to the values sum to one up to fp32 rounding: a query
+    // whose attention falls on a few keys gets their values back without the weights'
+    // bf16 rounding. Two dot2 chains of four pairs each.
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const uint32_t w4[4] = {bp[h2].x, bp[h2].y, bp[h2].z, bp[h2].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ps += bf16_lo(w4[i]) + bf16_hi(w4[i]);
+      ps0 = add_bf16x2(bp[h2].x, ps0);
+      ps1 = add_bf16x2(bp[h2].y, ps1);
+      ps0 = add_bf16x2(bp[h2].z, ps0);
+      ps1 = add_bf16x2(bp[h2].w, ps1);
     }
-    l += ps;
+    l += ps0 + ps1;
 
     // ---- O^T += V^T P^T over the two 32-key halves of the block
 #pragma unroll
