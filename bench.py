@@ -374,8 +374,12 @@ def main(argv=None):
         achieved = work / (dom_us * 1e-6) / 1e12
         peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
         unit = "TFLOP/s"
-    rkernel = ("attn_kernel+attn_combine_kernel" if r.attn_splits > 1 else "attn_kernel") if timed == "attn_op" \
-        else dominant
+    if timed != "attn_op":
+        rkernel = dominant
+    elif wl.dtype == "f32":
+        rkernel = "attn_f32_kernel"
+    else:
+        rkernel = "attn_kernel+attn_combine_kernel" if r.attn_splits > 1 else "attn_kernel"
     roofline = {"kernel": rkernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(rkernel, wl.name),
                 "avg_launch_us": round(dom_us, 3)}
