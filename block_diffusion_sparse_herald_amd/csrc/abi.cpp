@@ -229,7 +229,7 @@ herald_status check_compression(int ksize, int stride) {
 RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
   Carver c{static_cast<char*>(ws)};
   RefineWs w;
-  const int tile = s.bf16 ? kRefineTile : kRefineTileF32;
+  const int tile = refine_tile_of(s);
   w.ntile = (s.C + tile - 1) / tile;
   w.row_stats = c.take<float2>((size_t)s.nseq * s.Hkv * ((w.ntile + 1) & ~1) * s.B * s.G);
   w.rscore = c.take<float>((size_t)s.nseq * s.Hkv * s.C);
@@ -444,13 +444,8 @@ herald_status herald_refine_topk(const herald_problem* p, const void* q_refine, 
   carve_refine(s, nullptr, &need);
   HERALD_TRY(check_ws(ws, ws_bytes, need));
   const RefineWs w = carve_refine(s, ws, &need);
-  if (s.bf16) {
-    HERALD_LAUNCH(4, stream, launch_refine_stats(s, q_refine, k_cache, cand_idx, w, stream));
-    HERALD_LAUNCH(5, stream, launch_refine_scores(s, q_refine, k_cache, cand_idx, w, stream));
-  } else {
-    HERALD_LAUNCH(4, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, true, stream));
-    HERALD_LAUNCH(5, stream, launch_refine_f32(s, q_refine, k_cache, cand_idx, w, false, stream));
-  }
+  HERALD_LAUNCH(4, stream, launch_refine_stats(s, q_refine, k_cache, cand_idx, w, stream));
+  HERALD_LAUNCH(5, stream, launch_refine_scores(s, q_refine, k_cache, cand_idx, w, stream));
   HERALD_LAUNCH(6, stream, launch_refine_select(s, cand_idx, w, topk_idx, topk_score, stream));
   return ok();
 }

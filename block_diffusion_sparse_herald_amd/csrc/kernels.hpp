@@ -26,9 +26,6 @@ constexpr int kRadixBins = 2048;
 // (36 per thread) for the one-kernel top-C.
 constexpr int kTopcLdsMaxLen = 36864;
 // Candidates one refine workgroup covers (bf16 MFMA path: 64 per wave; fp32 path).
-constexpr int kRefineTile = 256;
-constexpr int kRefineTileF32 = 128;
-constexpr int kRefineScoreTileF32 = 64;  // candidates per fp32 score workgroup (one per lane)
 // Keys per attention block and the largest supported candidate count.
 constexpr int kAttnKeyBlock = 64;
 constexpr int kMaxCandidates = 16384;
@@ -112,8 +109,8 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
                                 const RefineWs& ws, hipStream_t st);
 hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
                                 float* topk_score, hipStream_t st);
-hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
-                             bool stats, hipStream_t st);
+// candidates per refine workgroup (256 for bf16, 64 for fp32)
+int refine_tile_of(const Shape& s);
 // gather
 hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
                          int32_t* status, hipStream_t st);

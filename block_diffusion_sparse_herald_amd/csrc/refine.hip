@@ -6,89 +6,127 @@
 //   R_g[c] = sum_{b, h in g} 2^(x[b,h,c] - M[b,h]) / Z[b,h],
 //   x = scale * log2(e) * <q[b][h], K[cand_c][g]>.
 //
-// bf16 path, two launches over the same (sequence, KV head, 256-candidate tile)
-// grid; both compute x with identical MFMA code, so the logits agree bit for bit:
+// Two launches over the same (sequence, KV head, candidate tile) grid; both compute x
+// with identical MFMA code, so the logits agree bit for bit:
 //   refine_stats_kernel   per row (b,h): (max, sum 2^(x-max)) over the tile
 //                         (stored row-major: a row's tiles are contiguous).
 //   refine_scores_kernel  per row: normalisers from all tiles; per candidate: the
 //                         sum over rows, in a fixed order (each lane over its row's
 //                         tiles, then over the 16 lanes of a row with DPP shifts).
-// A workgroup covers kRefineTile candidates, each wave 64 of them (four 16-candidate
-// MFMA tiles). The candidate key rows, gathered from the cache by index, go straight
-// into registers as the A operand; the group's B*G query rows, shared by the waves,
-// are streamed into LDS with direct-to-LDS loads and read as the B operand
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulate). Only the query rows take LDS (32 KiB
-// at B*G = 128, d = 128), so several workgroups share a compute unit and one's loads
-// overlap another's products.
+// A workgroup of four waves covers 256 candidates (bf16: four 16-candidate MFMA tiles
+// per wave) or 64 (fp32: one tile per wave). The candidate key rows, gathered from the
+// cache by index, go straight into registers as the A operand; the group's B*G query
+// rows, shared by the waves, are streamed into LDS with direct-to-LDS loads and read as
+// the B operand (v_mfma_f32_16x16x32_bf16 or v_mfma_f32_16x16x4_f32, fp32 accumulate).
+// Only the query rows take LDS (32 KiB at B*G = 128, d = 128 in bf16), so several
+// workgroups share a compute unit and one's loads overlap another's products.
 // refine_select_kernel then takes, per (sequence, KV head), the exact top-K of R
 // in LDS (three radix digits on the fp32 bit pattern, R >= 0), ties to the lower
 // cache index, ascending output.
-// fp32 path: the same stats / scores / select steps, with the logits on VALU.
+// fp32 path: the same kernels on v_mfma_f32_16x16x4_f32 (fp32 products and sums),
+// 64-candidate tiles.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace herald {
 
-// 16-byte chunk c of an LDS row r (query row or candidate key row) is stored at chunk
-// c ^ refine_swz(r): the 16 rows one MFMA fragment read touches hit distinct banks.
-template <int D>
+// Candidate tiles (16 candidates each) per wave: 4 for bf16, 1 for fp32, whose MFMA
+// does an eighth of the bf16 work per instruction (workgroups of 256 and 64
+// candidates).
+template <typename T>
+constexpr int refine_mt() { return sizeof(T) == 2 ? 4 : 1; }
+template <typename T>
+constexpr int refine_tile() { return 4 * 16 * refine_mt<T>(); }
+
+// 16-byte chunk c of an LDS query row r is stored at chunk c ^ refine_swz(r): the 16
+// rows one MFMA fragment read touches hit distinct banks.
+template <typename T, int D>
 __device__ __forceinline__ int refine_swz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return sizeof(T) == 4 || D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
-template <int D>
-__device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[4][D / 32], const bf16* qs, int rt, int lane,
-                                                   f32x4_t (&acc)[4]) {
-  uint4 bq[D / 32];
+// Operand layout of both products (v_mfma_f32_16x16x32_bf16, v_mfma_f32_16x16x4_f32):
+// lane l supplies row l % 16 of A (a candidate key) and column l % 16 of B (a query row)
+// at the contraction slots of lane group l / 16, and holds D[4 (l / 16) + i][l % 16].
+// Each lane keeps D / 4 elements of its key row (D * sizeof(T) / 64 16-byte chunks per
+// candidate tile). bf16: chunk ks of lane group j covers dimensions 32 ks + 8 j .. +8,
+// one MFMA. fp32: lane group j covers dimensions j D/4 .. (j + 1) D/4 - 1, chunk c of it
+// four MFMAs, one dimension each; the query side uses the same assignment, so the
+// contraction runs over every dimension once.
+template <typename T, int D>
+struct RefineFrag {
+  static constexpr int NC = D * (int)sizeof(T) / 64;  // 16-byte chunks per lane per candidate tile
+  static constexpr int EPC = 16 / (int)sizeof(T);     // elements per chunk
+  // element offset of chunk c of lane group j within a row
+  __device__ static constexpr int off(int j, int c) { return sizeof(T) == 2 ? c * 32 + j * 8 : j * (D / 4) + c * 4; }
+};
+
+template <typename T, int D, int MT>
+__device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[MT][RefineFrag<T, D>::NC], const T* qs, int rt,
+                                                   int lane, f32x4_t (&acc)[MT]) {
+  using F = RefineFrag<T, D>;
+  uint4 bq[F::NC];
   const int r = rt * 16 + (lane & 15);
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    bq[ks] = *reinterpret_cast<const uint4*>(qs + r * D + ((ks * 4 + (lane >> 4)) ^ refine_swz<D>(r)) * 8);
+  for (int c = 0; c < F::NC; ++c)
+    bq[c] = *reinterpret_cast<const uint4*>(qs + r * D + ((F::off(lane >> 4, c) / F::EPC) ^ refine_swz<T, D>(r)) * F::EPC);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) acc[mt] = mfma16x16x32(a[mt][ks], bq[ks], acc[mt]);
+    for (int c = 0; c < F::NC; ++c) {
+      if constexpr (sizeof(T) == 2) {
+        acc[mt] = mfma16x16x32(a[mt][c], bq[c], acc[mt]);
+      } else {
+        const uint32_t av[4] = {a[mt][c].x, a[mt][c].y, a[mt][c].z, a[mt][c].w};
+        const uint32_t bv[4] = {bq[c].x, bq[c].y, bq[c].z, bq[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[e]), __uint_as_float(bv[e]), acc[mt], 0,
+                                                         0, 0);
+      }
+    }
   }
 }
 
 // Shared prologue of both refine kernels, in two parts. refine_issue_rows: the
 // group's query rows go to LDS with coalesced direct-to-LDS loads (rows past R re-read
-// query row 0, masked later), and each wave loads the MFMA fragments of its 64
+// query row 0, masked later), and each wave loads the MFMA fragments of its MT * 16
 // candidate key rows straight into registers, gathered from the cache by index
 // (candidates past C re-read the last one, masked later); every lane reads 16 bytes of
-// a row per load, a load covers 64 contiguous bytes of 16 rows. refine_wait_rows:
-// once both have landed, the workgroup may read the query rows.
-template <int D>
-__device__ __forceinline__ void refine_issue_rows(const bf16* __restrict__ q, const bf16* __restrict__ k,
+// a row per load. refine_wait_rows: once both have landed, the workgroup may read the
+// query rows.
+template <typename T, int D, int MT>
+__device__ __forceinline__ void refine_issue_rows(const T* __restrict__ q, const T* __restrict__ k,
                                                   const int32_t* __restrict__ cand, int64_t j0, int s, int g, int B,
-                                                  int Hq, int Hkv, int G, int C, int R, int RT, int ctile, bf16* qs,
-                                                  uint4 (&a)[4][D / 32]) {
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR; // rows per load instruction
-  constexpr int NW = kRefineTile / 64;
+                                                  int Hq, int Hkv, int G, int C, int R, int RT, int ctile, T* qs,
+                                                  uint4 (&a)[MT][RefineFrag<T, D>::NC]) {
+  using F = RefineFrag<T, D>;
+  constexpr int CPR = D / F::EPC;  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;    // rows per load instruction
+  constexpr int NW = 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rr = lane / CPR, p = lane % CPR;
   // query rows: the waves take turns by instruction
   for (int r0 = w * RPI; r0 < RT * 16; r0 += NW * RPI) {
     const int r = r0 + rr;
     const int rq = r < R ? r : 0;
-    const bf16* src = q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + (p ^ refine_swz<D>(r)) * 8;
+    const T* src = q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + (p ^ refine_swz<T, D>(r)) * F::EPC;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)(qs + r0 * D), 16, 0, 0);
   }
-  // candidate key fragments of wave w: rows w*64 + mt*16 + (lane & 15) of the tile
+  // candidate key fragments of wave w: rows (w * MT + mt) * 16 + (lane & 15) of the tile
   const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  const bf16* rows[4];
+  const T* rows[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int c = min(ctile * kRefineTile + w * 64 + mt * 16 + (lane & 15), C - 1);
-    rows[mt] = k + ((j0 + cd[c]) * Hkv + g) * D + (lane >> 4) * 8;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int c = min(ctile * refine_tile<T>() + (w * MT + mt) * 16 + (lane & 15), C - 1);
+    rows[mt] = k + ((j0 + cd[c]) * Hkv + g) * D;
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) a[mt][ks] = *reinterpret_cast<const uint4*>(rows[mt] + ks * 32);
+    for (int c = 0; c < F::NC; ++c) a[mt][c] = *reinterpret_cast<const uint4*>(rows[mt] + F::off(lane >> 4, c));
 }
 
 __device__ __forceinline__ void refine_wait_rows() {
@@ -96,32 +134,31 @@ __device__ __forceinline__ void refine_wait_rows() {
   __syncthreads();
 }
 
-template <int D>
-__global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* __restrict__ q,
-                                                                   const bf16* __restrict__ k,
-                                                                   const int32_t* __restrict__ cand,
-                                                                   const int64_t* __restrict__ seq_start, int B,
-                                                                   int Hq, int Hkv, int G, int C, float scale2,
-                                                                   int ntile, float2* __restrict__ row_stats) {
+template <typename T, int D>
+__global__ __launch_bounds__(256) void refine_stats_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const int32_t* __restrict__ cand,
+                                                           const int64_t* __restrict__ seq_start, int B, int Hq,
+                                                           int Hkv, int G, int C, float scale2, int ntile,
+                                                           float2* __restrict__ row_stats) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NW = kRefineTile / 64;
+  constexpr int NW = 4, MT = refine_mt<T>();
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G, RT = (R + 15) / 16;
-  bf16* qs = reinterpret_cast<bf16*>(smem);                     // [RT*16][D]
+  T* qs = reinterpret_cast<T*>(smem);                           // [RT*16][D]
   float2* wstat = reinterpret_cast<float2*>(qs + RT * 16 * D);  // [NW][RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int cbase = tile * kRefineTile + w * 64;
-  uint4 a[4][D / 32];
-  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
+  const int cbase = tile * refine_tile<T>() + w * MT * 16;
+  uint4 a[MT][RefineFrag<T, D>::NC];
+  refine_issue_rows<T, D, MT>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
   refine_wait_rows();
 
-  const bool full = cbase + 64 <= C;  // no candidate of this wave past C
+  const bool full = cbase + MT * 16 <= C;  // no candidate of this wave past C
   for (int rt = 0; rt < RT; ++rt) {
-    f32x4_t acc[4];
-    refine_tile_logits<D>(a, qs, rt, lane, acc);
+    f32x4_t acc[MT];
+    refine_tile_logits<T, D, MT>(a, qs, rt, lane, acc);
     if (!full) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (cbase + mt * 16 + (lane >> 4) * 4 + i >= C) acc[mt][i] = -INFINITY;
@@ -129,7 +166,7 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
     // the row max on the raw products (scale2 > 0), the logits as one fma each
     float mr = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mr = fmaxf(mr, acc[mt][i]);
     mr = xmax4(mr);
@@ -137,7 +174,7 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
     float l = 0.f;
     if (mr != -INFINITY) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) l += fast_exp2(fmaf(acc[mt][i], scale2, -m));
     }
@@ -145,7 +182,7 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
     if (lane < 16) wstat[w * RT * 16 + rt * 16 + lane] = make_float2(m, l);
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += kRefineTile) {
+  for (int r = threadIdx.x; r < R; r += NW * 64) {
     float M = -INFINITY, Z = 0.f;
     for (int ww = 0; ww < NW; ++ww) {
       const float2 p = wstat[ww * RT * 16 + r];
@@ -155,27 +192,27 @@ __global__ __launch_bounds__(kRefineTile) void refine_stats_kernel(const bf16* _
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* __restrict__ q,
-                                                                    const bf16* __restrict__ k,
-                                                                    const int32_t* __restrict__ cand,
-                                                                    const int64_t* __restrict__ seq_start, int B,
-                                                                    int Hq, int Hkv, int G, int C, float scale2,
-                                                                    int ntile, const float2* __restrict__ row_stats,
-                                                                    float* __restrict__ rscore) {
+template <typename T, int D>
+__global__ __launch_bounds__(256) void refine_scores_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                            const int32_t* __restrict__ cand,
+                                                            const int64_t* __restrict__ seq_start, int B, int Hq,
+                                                            int Hkv, int G, int C, float scale2, int ntile,
+                                                            const float2* __restrict__ row_stats,
+                                                            float* __restrict__ rscore) {
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int MT = refine_mt<T>();
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G, RT = (R + 15) / 16;
-  bf16* qs = reinterpret_cast<bf16*>(smem);               // [RT*16][D]
+  T* qs = reinterpret_cast<T*>(smem);                        // [RT*16][D]
   float* rowM = reinterpret_cast<float*>(qs + RT * 16 * D);  // [RT*16]
-  float* rowIZ = rowM + RT * 16;                            // [RT*16]
+  float* rowIZ = rowM + RT * 16;                             // [RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int cbase = tile * kRefineTile + w * 64;
-  uint4 a[4][D / 32];
-  refine_issue_rows<D>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
+  const int cbase = tile * refine_tile<T>() + w * MT * 16;
+  uint4 a[MT][RefineFrag<T, D>::NC];
+  refine_issue_rows<T, D, MT>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
   // per-row normalisers over all tiles, merged in tile order while the rows stream in
   // (a row's tile statistics are contiguous; 16 tiles per batch of loads)
-  for (int r = threadIdx.x; r < RT * 16; r += kRefineTile) {
+  for (int r = threadIdx.x; r < RT * 16; r += 256) {
     float M = -INFINITY, Z = 0.f;
     if (r < R) {
       const float2* rs = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);  // 16-byte aligned rows
@@ -202,29 +239,29 @@ __global__ __launch_bounds__(kRefineTile) void refine_scores_kernel(const bf16* 
   }
   refine_wait_rows();
 
-  float rs[4][4];
+  float rs[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) rs[mt][i] = 0.f;
   for (int rt = 0; rt < RT; ++rt) {
-    f32x4_t acc[4];
-    refine_tile_logits<D>(a, qs, rt, lane, acc);
+    f32x4_t acc[MT];
+    refine_tile_logits<T, D, MT>(a, qs, rt, lane, acc);
     const int r = rt * 16 + (lane & 15);
     const float M = rowM[r], iz = rowIZ[r];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[mt][i] = fmaf(fast_exp2(fmaf(acc[mt][i], scale2, -M)), iz, rs[mt][i]);
   }
   // each lane summed its query row over the row tiles; now sum the 16 rows of a lane row
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) rs[mt][i] = row_sum16_last(rs[mt][i]);
   if ((lane & 15) == 15) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = cbase + mt * 16 + (lane >> 4) * 4 + i;
@@ -317,269 +354,51 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
   }
 }
 
-// fp32 path: candidate key rows of one TILE-candidate tile into LDS (row stride LD
-// floats), NT threads: every candidate index is loaded first, then every row chunk,
-// then the LDS stores, so the loads overlap instead of waiting one by one.
-template <int D, int LD, int NT, int TILE>
-__device__ __forceinline__ void stage_rows_f32(const float* __restrict__ k, const int32_t* __restrict__ cd,
-                                               int64_t j0, int Hkv, int g, int C, int tile, float* dst) {
-  constexpr int NI = TILE * D / 4 / NT;  // 16-byte chunks per thread
-  static_assert(NI * NT == TILE * D / 4, "whole chunks per thread");
-  int32_t idx[NI];
-#pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int row = (threadIdx.x + u * NT) / (D / 4);
-    idx[u] = cd[min(tile * TILE + row, C - 1)];
-  }
-  float4 v[NI];
-#pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int ch = (threadIdx.x + u * NT) % (D / 4);
-    v[u] = *reinterpret_cast<const float4*>(k + ((j0 + idx[u]) * Hkv + g) * D + 4 * ch);
-  }
-#pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int i = threadIdx.x + u * NT;
-    *reinterpret_cast<float4*>(dst + (i / (D / 4)) * LD + 4 * (i % (D / 4))) = v[u];
-  }
-}
-
-// fp32 path: the same three steps on VALU (stats over kRefineTileF32-candidate tiles,
-// scores over kRefineScoreTileF32-candidate tiles, then refine_select_kernel). A logit is one fma chain over the head dimension
-// in index order; fma is symmetric in its two factors, so the two kernels, which read
-// the operands from different places, compute the same bits.
-template <int D>
-__device__ __forceinline__ void dot4_f32(const float (&reg)[D], const float* o0, const float* o1, const float* o2,
-                                         const float* o3, float (&d)[4]) {
-  d[0] = d[1] = d[2] = d[3] = 0.f;
-#pragma unroll
-  for (int e = 0; e < D; e += 4) {
-    const float4 a = *reinterpret_cast<const float4*>(o0 + e);
-    const float4 b = *reinterpret_cast<const float4*>(o1 + e);
-    const float4 c = *reinterpret_cast<const float4*>(o2 + e);
-    const float4 f = *reinterpret_cast<const float4*>(o3 + e);
-    d[0] = fmaf(reg[e + 3], a.w, fmaf(reg[e + 2], a.z, fmaf(reg[e + 1], a.y, fmaf(reg[e], a.x, d[0]))));
-    d[1] = fmaf(reg[e + 3], b.w, fmaf(reg[e + 2], b.z, fmaf(reg[e + 1], b.y, fmaf(reg[e], b.x, d[1]))));
-    d[2] = fmaf(reg[e + 3], c.w, fmaf(reg[e + 2], c.z, fmaf(reg[e + 1], c.y, fmaf(reg[e], c.x, d[2]))));
-    d[3] = fmaf(reg[e + 3], f.w, fmaf(reg[e + 2], f.z, fmaf(reg[e + 1], f.y, fmaf(reg[e], f.x, d[3]))));
-  }
-}
-
-// The same chains with both operands in LDS: one row p (per lane) against four rows
-// o0..o3 (broadcast).
-template <int D>
-__device__ __forceinline__ void dot4_lds_f32(const float* p, const float* o0, const float* o1, const float* o2,
-                                             const float* o3, float (&d)[4]) {
-  d[0] = d[1] = d[2] = d[3] = 0.f;
-#pragma unroll 4
-  for (int e = 0; e < D; e += 4) {
-    const float4 r = *reinterpret_cast<const float4*>(p + e);
-    const float4 a = *reinterpret_cast<const float4*>(o0 + e);
-    const float4 b = *reinterpret_cast<const float4*>(o1 + e);
-    const float4 c = *reinterpret_cast<const float4*>(o2 + e);
-    const float4 f = *reinterpret_cast<const float4*>(o3 + e);
-    d[0] = fmaf(r.w, a.w, fmaf(r.z, a.z, fmaf(r.y, a.y, fmaf(r.x, a.x, d[0]))));
-    d[1] = fmaf(r.w, b.w, fmaf(r.z, b.z, fmaf(r.y, b.y, fmaf(r.x, b.x, d[1]))));
-    d[2] = fmaf(r.w, c.w, fmaf(r.z, c.z, fmaf(r.y, c.y, fmaf(r.x, c.x, d[2]))));
-    d[3] = fmaf(r.w, f.w, fmaf(r.z, f.z, fmaf(r.y, f.y, fmaf(r.x, f.x, d[3]))));
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_row_f32(const float* __restrict__ src, float (&reg)[D]) {
-#pragma unroll
-  for (int e = 0; e < D; e += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(src + e);
-    reg[e] = v.x;
-    reg[e + 1] = v.y;
-    reg[e + 2] = v.z;
-    reg[e + 3] = v.w;
-  }
-}
-
-// Per (query row, tile): (max, sum 2^(x-max)) over the tile's candidates. A workgroup
-// takes one tile and 64 query rows (blockIdx.x = pass * ntile + tile); lanes are query
-// rows (the row in registers); wave w of NW takes candidates w * CPW .. +CPW-1 of the
-// tile from LDS (broadcast reads); the waves' pairs are merged in wave order. Eight
-// waves at D = 64; four at D = 128, whose 128-float query row needs the register budget
-// of one wave per SIMD.
-template <int D>
-__global__ __launch_bounds__(D == 128 ? 256 : 512) void refine_stats_f32_kernel(const float* __restrict__ q,
-                                                               const float* __restrict__ k,
-                                                               const int32_t* __restrict__ cand,
-                                                               const int64_t* __restrict__ seq_start, int B, int Hq,
-                                                               int Hkv, int G, int C, float scale2, int ntile,
-                                                               float2* __restrict__ row_stats) {
-  constexpr int NW = D == 128 ? 4 : 8, CPW = kRefineTileF32 / NW;
-  static_assert(CPW % 4 == 0, "whole groups of four candidates per wave");
-  extern __shared__ __align__(16) float ks[];  // [kRefineTileF32][D]
-  __shared__ float2 wstat[NW][64];
-  const int tile = blockIdx.x % ntile, r0 = blockIdx.x / ntile * 64, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t j0 = seq_start[s];
-  const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  const int r = r0 + lane, rq = min(r, R - 1);
-  float qr[D];
-  load_row_f32<D>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D, qr);
-  stage_rows_f32<D, D, NW * 64, kRefineTileF32>(k, cd, j0, Hkv, g, C, tile, ks);
-  __syncthreads();
-  const int nvalid = min(kRefineTileF32, C - tile * kRefineTileF32);
-  {
-    float m = -INFINITY, l = 0.f;
-#pragma unroll 1
-    for (int c0 = w * CPW; c0 < w * CPW + CPW; c0 += 4) {
-      float d[4];
-      dot4_f32<D>(qr, ks + c0 * D, ks + (c0 + 1) * D, ks + (c0 + 2) * D, ks + (c0 + 3) * D, d);
-      float x[4], mg = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[u] = c0 + u < nvalid ? d[u] * scale2 : -INFINITY;
-        mg = fmaxf(mg, x[u]);
-      }
-      if (mg == -INFINITY) continue;
-      float lg = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) lg += fast_exp2(x[u] - mg);
-      ms_merge(m, l, mg, lg);
-    }
-    wstat[w][lane] = make_float2(m, l);
-  }
-  __syncthreads();
-  if (threadIdx.x < 64 && r < R) {
-    float M = -INFINITY, Z = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) ms_merge(M, Z, wstat[ww][lane].x, wstat[ww][lane].y);
-    row_stats[(((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1) + tile] = make_float2(M, Z);
-  }
-}
-
-// Per candidate: sum over query rows of 2^(x - M_row) / Z_row (M_row, Z_row merged over
-// all statistics tiles). A workgroup takes kRefineScoreTileF32 = 64 candidates; lanes
-// are candidates (key rows in LDS, padded by four words so that 16 lanes' 16-byte reads
-// cover all banks); of the eight waves, wave w takes rows 8w .. 8w+7 of every 64-row
-// pass; the eight waves' sums are added in wave order at the end.
-template <int D>
-__global__ __launch_bounds__(512) void refine_scores_f32_kernel(const float* __restrict__ q,
-                                                                const float* __restrict__ k,
-                                                                const int32_t* __restrict__ cand,
-                                                                const int64_t* __restrict__ seq_start, int B,
-                                                                int Hq, int Hkv, int G, int C, float scale2, int ntile,
-                                                                const float2* __restrict__ row_stats,
-                                                                float* __restrict__ rscore) {
-  constexpr int KP = D + 4, TS = kRefineScoreTileF32;
-  static_assert(TS == 64, "one candidate per lane");
-  extern __shared__ __align__(16) float qs[];  // [64][D], [TS][KP], rowM[R], rowIZ[R]
-  __shared__ float part[8][TS];
-  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G;
-  float* kt = qs + 64 * D;
-  float* rowM = kt + TS * KP;
-  float* rowIZ = rowM + R;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int ci = lane;
-  const int64_t j0 = seq_start[s];
-  const int32_t* cd = cand + ((int64_t)s * Hkv + g) * C;
-  stage_rows_f32<D, KP, 512, TS>(k, cd, j0, Hkv, g, C, tile, kt);
-  for (int r = threadIdx.x; r < R; r += 512) {
-    const float2* st = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);
-    float M = -INFINITY, Z = 0.f;
-    for (int t0 = 0; t0 < ntile; t0 += 8) {  // eight tile statistics in flight, merged in tile order
-      float2 p[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) p[u] = t0 + u < ntile ? st[t0 + u] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) ms_merge(M, Z, p[u].x, p[u].y);
-    }
-    rowM[r] = M;
-    rowIZ[r] = 1.f / Z;
-  }
-  float acc = 0.f;
-  for (int r0 = 0; r0 < R; r0 += 64) {
-    __syncthreads();
-    {
-      constexpr int NQ = 64 * D / 4 / 512;  // 16-byte chunks per thread, all loads first
-      float4 qv[NQ];
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const int i = threadIdx.x + u * 512, rr = i / (D / 4), ch = i % (D / 4);
-        const int rq = min(r0 + rr, R - 1);
-        qv[u] = *reinterpret_cast<const float4*>(q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + 4 * ch);
-      }
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const int i = threadIdx.x + u * 512;
-        *reinterpret_cast<float4*>(qs + (i / (D / 4)) * D + 4 * (i % (D / 4))) = qv[u];
-      }
-    }
-    __syncthreads();
-    const int rb = w * 8;
-#pragma unroll
-    for (int j = rb; j < rb + 8; j += 4) {
-      float d[4];
-      dot4_lds_f32<D>(kt + ci * KP, qs + j * D, qs + (j + 1) * D, qs + (j + 2) * D, qs + (j + 3) * D, d);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + j + u;
-        if (r < R) acc += fast_exp2(d[u] * scale2 - rowM[r]) * rowIZ[r];
-      }
-    }
-  }
-  part[w][ci] = acc;
-  __syncthreads();
-  if (threadIdx.x < TS) {
-    const int cc = tile * TS + threadIdx.x;
-    if (cc < C) {
-      float sum = part[0][threadIdx.x];
-#pragma unroll
-      for (int ww = 1; ww < 8; ++ww) sum += part[ww][threadIdx.x];
-      rscore[((int64_t)s * Hkv + g) * C + cc] = sum;
-    }
-  }
-}
-
 // ------------------------------------------------------------------ launchers
 
 static size_t refine_smem(const Shape& s, bool stats) {
   const int RT = (s.B * s.G + 15) / 16;
-  const size_t rows = (size_t)RT * 16 * s.D * sizeof(bf16);
-  return rows + (stats ? (size_t)(kRefineTile / 64) * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
+  const size_t rows = (size_t)RT * 16 * s.D * (s.bf16 ? 2 : 4);
+  return rows + (stats ? (size_t)4 * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
 }
+
+template <typename T, int D>
+static hipError_t launch_refine_t(const Shape& s, const void* q, const void* k, const int32_t* cand,
+                                  const RefineWs& ws, bool stats, hipStream_t st) {
+  const dim3 grid(ws.ntile, s.Hkv, s.nseq);
+  const float scale2 = s.scale * kLog2e;
+  const size_t smem = refine_smem(s, stats);
+  const void* kern = stats ? (const void*)refine_stats_kernel<T, D> : (const void*)refine_scores_kernel<T, D>;
+  hipError_t e = allow_smem(kern, smem);
+  if (e != hipSuccess) return e;
+  if (stats)
+    klaunch(refine_stats_kernel<T, D>, grid, 256, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B, s.Hq,
+            s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
+  else
+    klaunch(refine_scores_kernel<T, D>, grid, 256, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B, s.Hq,
+            s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
+  return hipGetLastError();
+}
+
+static hipError_t launch_refine(const Shape& s, const void* q, const void* k, const int32_t* cand,
+                                const RefineWs& ws, bool stats, hipStream_t st) {
+  if (s.bf16)
+    return s.D == 128 ? launch_refine_t<bf16, 128>(s, q, k, cand, ws, stats, st)
+                      : launch_refine_t<bf16, 64>(s, q, k, cand, ws, stats, st);
+  return s.D == 128 ? launch_refine_t<float, 128>(s, q, k, cand, ws, stats, st)
+                    : launch_refine_t<float, 64>(s, q, k, cand, ws, stats, st);
+}
+
+int refine_tile_of(const Shape& s) { return s.bf16 ? refine_tile<bf16>() : refine_tile<float>(); }
 
 hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
                                hipStream_t st) {
-  dim3 grid(ws.ntile, s.Hkv, s.nseq);
-  const float scale2 = s.scale * kLog2e;
-  const size_t smem = refine_smem(s, true);
-  const void* kern = s.D == 128 ? (const void*)refine_stats_kernel<128> : (const void*)refine_stats_kernel<64>;
-  hipError_t e = allow_smem(kern, smem);
-  if (e != hipSuccess) return e;
-  if (s.D == 128)
-    klaunch(refine_stats_kernel<128>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
-                                                      s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
-  else
-    klaunch(refine_stats_kernel<64>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B, s.Hq,
-                                                     s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
-  return hipGetLastError();
+  return launch_refine(s, q, k, cand, ws, true, st);
 }
 
 hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, const int32_t* cand,
                                 const RefineWs& ws, hipStream_t st) {
-  dim3 grid(ws.ntile, s.Hkv, s.nseq);
-  const float scale2 = s.scale * kLog2e;
-  const size_t smem = refine_smem(s, false);
-  const void* kern = s.D == 128 ? (const void*)refine_scores_kernel<128> : (const void*)refine_scores_kernel<64>;
-  hipError_t e = allow_smem(kern, smem);
-  if (e != hipSuccess) return e;
-  if (s.D == 128)
-    klaunch(refine_scores_kernel<128>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
-                                                       s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
-                                                       ws.rscore);
-  else
-    klaunch(refine_scores_kernel<64>, grid, kRefineTile, smem, st, (const bf16*)q, (const bf16*)k, cand, s.seq_start, s.B,
-                                                      s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats,
-                                                      ws.rscore);
-  return hipGetLastError();
+  return launch_refine(s, q, k, cand, ws, false, st);
 }
 
 hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
@@ -594,41 +413,6 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
   if (e != hipSuccess) return e;
   klaunch(refine_select_kernel<true>, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, s.Hkv, s.C, s.topk,
           topk_idx, topk_score);
-  return hipGetLastError();
-}
-
-hipError_t launch_refine_f32(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
-                             bool stats, hipStream_t st) {
-  // stats: one workgroup per (tile, 64-row pass); scores: one per 64-candidate tile, over all rows
-  const int npass = (s.B * s.G + 63) / 64;
-  const dim3 grid(stats ? ws.ntile * npass : (s.C + kRefineScoreTileF32 - 1) / kRefineScoreTileF32, s.Hkv, s.nseq);
-  const float scale2 = s.scale * kLog2e;
-  const size_t smem = stats ? (size_t)kRefineTileF32 * s.D * sizeof(float)
-                            : ((size_t)64 * s.D + (size_t)kRefineScoreTileF32 * (s.D + 4) + 2 * (size_t)s.B * s.G) *
-                                  sizeof(float);
-  const void* kern = stats ? (s.D == 128 ? (const void*)refine_stats_f32_kernel<128>
-                                         : (const void*)refine_stats_f32_kernel<64>)
-                           : (s.D == 128 ? (const void*)refine_scores_f32_kernel<128>
-                                         : (const void*)refine_scores_f32_kernel<64>);
-  hipError_t e = allow_smem(kern, smem);
-  if (e != hipSuccess) return e;
-  const float* qf = (const float*)q;
-  const float* kf = (const float*)k;
-  if (stats) {
-    if (s.D == 128)
-      klaunch(refine_stats_f32_kernel<128>, grid, 256, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
-                                                             s.C, scale2, ws.ntile, ws.row_stats);
-    else
-      klaunch(refine_stats_f32_kernel<64>, grid, 512, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
-                                                            s.C, scale2, ws.ntile, ws.row_stats);
-  } else {
-    if (s.D == 128)
-      klaunch(refine_scores_f32_kernel<128>, grid, 512, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
-                                                              s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
-    else
-      klaunch(refine_scores_f32_kernel<64>, grid, 512, smem, st, qf, kf, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G,
-                                                             s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
-  }
   return hipGetLastError();
 }
 

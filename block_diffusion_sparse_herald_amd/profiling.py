@@ -37,10 +37,8 @@ KERNELS = {
     "refine_stats": (["herald::refine_stats_kernel"], ["refine.hip", "common.hpp", "kernels.hpp"]),
     "refine_scores": (["herald::refine_scores_kernel"], ["refine.hip", "common.hpp", "kernels.hpp"]),
     "gather": (["herald::gather_kernel"], ["gather.hip", "common.hpp", "kernels.hpp"]),
-    # the fp32 path (VALU kernels)
+    # the fp32 attention (VALU kernel); the fp32 refine runs the refine kernels above
     "attn_f32_kernel": (["herald::attn_f32_kernel"], ["attn.hip", "common.hpp", "kernels.hpp"]),
-    "refine_stats_f32": (["herald::refine_stats_f32_kernel"], ["refine.hip", "common.hpp", "kernels.hpp"]),
-    "refine_scores_f32": (["herald::refine_scores_f32_kernel"], ["refine.hip", "common.hpp", "kernels.hpp"]),
 }
 
 
