@@ -31,7 +31,8 @@
 // for the second product, so the applied weights are normalised up to fp32 rounding.
 // Built with -fno-honor-nans (non-finite inputs are outside the contract): the max
 // reductions then need no NaN-quieting operations.
-// fp32 path (attn_f32_kernel): four query rows per workgroup, VALU, keys in chunks of 128.
+// fp32 path (attn_f32_kernel): one 16-row query tile per workgroup, eight waves over the
+// key tiles, v_mfma_f32_16x16x4_f32, partial results merged through LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -218,10 +219,14 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
     f32x4_t sacc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // wave priority up while a product's MFMAs issue: the SIMD's other wave, in its
+    // softmax, then fills the VALU slots between them
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) sacc[mt] = mfma16x16x32(kf[mt][ks], qf[ks], sacc[mt]);
+    __builtin_amdgcn_s_setprio(0);
     uint4 vf[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -278,10 +283,12 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
     l += ps0 + ps1;
 
     // ---- O^T += V^T P^T over the two 32-key halves of the block
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) o[dt] = mfma16x16x32(vf[dt][h2], bp[h2], o[dt]);
+    __builtin_amdgcn_s_setprio(0);
   }
   l = xsum4(l);
 
@@ -394,103 +401,165 @@ __global__ __launch_bounds__(kAttnCombineThreads) void attn_combine_kernel(const
                  pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
-// fp32 path: a workgroup takes four query rows of one (sequence, KV head) and walks
-// the keys in chunks of 128. Logits: one key per thread (its row read straight from
-// memory), two of the four query rows per thread from LDS (broadcast reads). Online
-// base-2 softmax: one wave per query row. Output: the chunk's values staged d-major in
-// LDS (rows padded by one word, so the 64 lanes of a read hit 64 banks), each thread
-// accumulating D/64 output elements of its wave's row.
+// fp32 path (attn_f32_kernel): one workgroup per (sequence, KV head, 16-row query
+// tile). Its 8 waves take the 16-key tiles t = w, w + 8, ... of the key list (subset
+// tiles, then the in-block keys), with each tile's fragments loaded straight into
+// registers (the next tile's loads in flight while one is computed), S^T = K.Q^T and
+// O^T += V^T.P^T on v_mfma_f32_16x16x4_f32 (fp32 products and sums) and an online
+// base-2 softmax per query row; the eight partial results are merged through LDS.
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
+// holds D[4 (l / 16) + i][l % 16]. First product: A = K (key l % 16 of the tile), B =
+// Q^T (query row l % 16), contraction slot j = l / 16 of step c taking dimension
+// j D/4 + c, so each lane reads a contiguous quarter of its rows. The product leaves
+// lane l with keys 4 (l / 16) + i of row l % 16, which are the contraction slots of
+// step i of the second product: A = V^T (dimension l % 16 of a 16-dimension tile, keys
+// 4 (l / 16) + i), B = P^T, the lane's own probabilities.
 template <int D>
-__global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kb,
+struct AttnF32Frag {
+  float4 k[D / 16];  // K row (key l % 16 of the tile), dimensions (l / 16) D/4 .. + D/4
+  float4 v[D / 16];  // per 16-dimension tile dt: V^T row dt * 16 + l % 16, keys 4 (l / 16) .. + 4
+};
+
+template <int D>
+__device__ __forceinline__ void attn_f32_load_tile(int t, int nts, const float* __restrict__ kb,
+                                                   const float* __restrict__ vb, const float* __restrict__ k_sel,
+                                                   const float* __restrict__ v_sel, int64_t unit, int s, int g, int B,
+                                                   int Hkv, int topk, int64_t ldv, int lr, int j,
+                                                   AttnF32Frag<D>& f) {
+  constexpr int KQ = D / 4;
+  if (t < nts) {  // subset keys t*16 .. (the tail past topk masked by the caller, its values zeroed here)
+    const int key = min(t * 16 + lr, topk - 1);
+    const float* kr = k_sel + (unit * topk + key) * D + j * KQ;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) f.k[c] = *reinterpret_cast<const float4*>(kr + 4 * c);
+    const int k0 = t * 16 + 4 * j;  // < ldv: ldv is topk rounded up to 64
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      float4 v = *reinterpret_cast<const float4*>(v_sel + (unit * D + dt * 16 + lr) * ldv + k0);
+      if (k0 + 4 > topk) {
+        v.x = k0 < topk ? v.x : 0.f;
+        v.y = k0 + 1 < topk ? v.y : 0.f;
+        v.z = k0 + 2 < topk ? v.z : 0.f;
+        v.w = 0.f;
+      }
+      f.v[dt] = v;
+    }
+  } else {  // in-block keys b = (t - nts)*16 .., key-major rows of k_blk / v_blk
+    const int b0 = (t - nts) * 16;
+    const int bk = min(b0 + lr, B - 1);
+    const float* kr = kb + (((int64_t)s * B + bk) * Hkv + g) * D + j * KQ;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) f.k[c] = *reinterpret_cast<const float4*>(kr + 4 * c);
+    float e[4][D / 16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = b0 + 4 * j + i;
+      const float* vr = vb + (((int64_t)s * B + min(b, B - 1)) * Hkv + g) * D + lr;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) e[i][dt] = b < B ? vr[dt * 16] : 0.f;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = make_float4(e[0][dt], e[1][dt], e[2][dt], e[3][dt]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kb,
                                                        const float* __restrict__ vb, const float* __restrict__ k_sel,
                                                        const float* __restrict__ v_sel, int B, int Hq, int Hkv,
                                                        int G, int topk, int64_t ldv, float scale2,
                                                        float* __restrict__ out) {
-  constexpr int KC = 128, RB = 4, EP = D / 64;
-  __shared__ __align__(16) float qs[RB][D];
-  __shared__ float xs[RB][KC];
-  extern __shared__ float vs[];  // [D][KC + 1]
-  const int g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G, r0 = blockIdx.x * RB;
+  constexpr int NW = 8, NC = D / 16, DT = D / 16, LDO = D + 4;
+  extern __shared__ __align__(16) float xo[];  // [NW][16][LDO] partial outputs, then [NW][16] (max, sum)
+  float2* xml = reinterpret_cast<float2*>(xo + NW * 16 * LDO);
+  const int rt = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G;
   const int64_t unit = (int64_t)s * Hkv + g;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  auto qrow = [&](int r) { return q + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D; };
-  for (int i = threadIdx.x; i < RB * D; i += 256) qs[i / D][i % D] = qrow(min(r0 + i / D, R - 1))[i % D];
-  const int NK = topk + B;
-  float m = -INFINITY, l = 0.f, acc[EP];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, j = lane >> 4;
+  const int nts = (topk + 15) / 16, nt = nts + (B + 15) / 16;
+
+  float4 qf[NC];  // query row rt*16 + lr (rows past R re-read the last row), dimensions j D/4 ..
+  {
+    const int r = min(rt * 16 + lr, R - 1);
+    const float* qr = q + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D + j * (D / 4);
 #pragma unroll
-  for (int j = 0; j < EP; ++j) acc[j] = 0.f;
-  for (int k0 = 0; k0 < NK; k0 += KC) {
-    const int n = min(KC, NK - k0);
-    __syncthreads();  // qs ready; the previous chunk's xs and vs consumed
-    {
-      const int kk = threadIdx.x % KC, rp = (threadIdx.x / KC) * 2;
-      float x0 = -INFINITY, x1 = -INFINITY;
-      if (kk < n) {
-        const int key = k0 + kk;
-        const float* kr = key < topk ? k_sel + (unit * topk + key) * D
-                                     : kb + (((int64_t)s * B + (key - topk)) * Hkv + g) * D;
-        float d0 = 0.f, d1 = 0.f;
-#pragma unroll 8
-        for (int e = 0; e < D; e += 4) {
-          const float4 kv = *reinterpret_cast<const float4*>(kr + e);
-          const float4 qa = *reinterpret_cast<const float4*>(&qs[rp][e]);
-          const float4 qb = *reinterpret_cast<const float4*>(&qs[rp + 1][e]);
-          d0 = fmaf(qa.w, kv.w, fmaf(qa.z, kv.z, fmaf(qa.y, kv.y, fmaf(qa.x, kv.x, d0))));
-          d1 = fmaf(qb.w, kv.w, fmaf(qb.z, kv.z, fmaf(qb.y, kv.y, fmaf(qb.x, kv.x, d1))));
-        }
-        x0 = d0 * scale2;
-        x1 = d1 * scale2;
-      }
-      xs[rp][kk] = x0;
-      xs[rp + 1][kk] = x1;
-    }
-    {
-      constexpr int NV = D * KC / 256;  // values per thread: all loads first, then the LDS stores
-      float vv[NV];
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int i = threadIdx.x + u * 256, e = i / KC, kk = i % KC, key = k0 + kk;
-        vv[u] = 0.f;
-        if (kk < n)
-          vv[u] = key < topk ? v_sel[(unit * D + e) * ldv + key]
-                             : vb[(((int64_t)s * B + (key - topk)) * Hkv + g) * D + e];
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int i = threadIdx.x + u * 256;
-        vs[(i / KC) * (KC + 1) + i % KC] = vv[u];
-      }
-    }
-    __syncthreads();
-    const float x0 = xs[w][lane], x1 = xs[w][lane + 64];
-    float cm = fmaxf(x0, x1);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
-    const float mn = fmaxf(m, cm);  // finite: every chunk holds at least one key
-    const float al = fast_exp2(m - mn);
-    const float p0 = fast_exp2(x0 - mn), p1 = fast_exp2(x1 - mn);
-    float ps = p0 + p1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) ps += __shfl_xor(ps, o);
-    l = l * al + ps;
-    m = mn;
-    __syncthreads();  // every wave has read its logits before they become weights
-    xs[w][lane] = p0;
-    xs[w][lane + 64] = p1;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < EP; ++j) {
-      const float* vr = vs + (lane + 64 * j) * (KC + 1);
-      float a = acc[j] * al;
-      for (int kk = 0; kk < n; ++kk) a = fmaf(xs[w][kk], vr[kk], a);
-      acc[j] = a;
-    }
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const float4*>(qr + 4 * c);
   }
-  if (r0 + w < R) {
-    float* o = out + (((int64_t)s * B + (r0 + w) / G) * Hq + g * G + (r0 + w) % G) * D;
+  f32x4_t o[DT];
 #pragma unroll
-    for (int j = 0; j < EP; ++j) o[lane + 64 * j] = acc[j] / l;
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  AttnF32Frag<D> cur, nxt;
+  int t = w;
+  if (t < nt) attn_f32_load_tile<D>(t, nts, kb, vb, k_sel, v_sel, unit, s, g, B, Hkv, topk, ldv, lr, j, cur);
+  for (; t < nt; t += NW) {
+    if (t + NW < nt)
+      attn_f32_load_tile<D>(t + NW, nts, kb, vb, k_sel, v_sel, unit, s, g, B, Hkv, topk, ldv, lr, j, nxt);
+    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float ka[4] = {cur.k[c].x, cur.k[c].y, cur.k[c].z, cur.k[c].w};
+      const float qa[4] = {qf[c].x, qf[c].y, qf[c].z, qf[c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], sacc, 0, 0, 0);
+    }
+    // keys 4j + i of the tile: past topk (subset) or past B (in-block) do not exist
+    const int nvalid = t < nts ? topk - t * 16 : B - (t - nts) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * j + i >= nvalid) sacc[i] = -INFINITY;
+    const float mx = xmax4(fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]))) * scale2;
+    const float mn = fmaxf(m, mx);  // finite: every tile holds a key
+    const float alpha = fast_exp2(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    m = mn;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sacc[i], scale2, -m));
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float va[4] = {cur.v[dt].x, cur.v[dt].y, cur.v[dt].z, cur.v[dt].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], p[i], o[dt], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+  l = xsum4(l);
+  // merge the eight waves' (max, sum, output) per row
+  {
+    float* orow = xo + (w * 16 + lr) * LDO + 4 * j;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(orow + dt * 16) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (j == 0) xml[w * 16 + lr] = make_float2(m, l);
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < 16 * (D / 4); it += NW * 64) {
+    const int row = it / (D / 4), e = (it % (D / 4)) * 4, r = rt * 16 + row;
+    if (r >= R) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, xml[ww * 16 + row].x);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float2 ml = xml[ww * 16 + row];
+      if (ml.x == -INFINITY) continue;  // a wave without tiles
+      const float f = fast_exp2(ml.x - M);
+      L += f * ml.y;
+      const float4 ov = *reinterpret_cast<const float4*>(xo + (ww * 16 + row) * LDO + e);
+      acc.x += f * ov.x;
+      acc.y += f * ov.y;
+      acc.z += f * ov.z;
+      acc.w += f * ov.w;
+    }
+    const float inv = 1.f / L;
+    *reinterpret_cast<float4*>(out + (((int64_t)s * B + r / G) * Hq + g * G + r % G) * D + e) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
@@ -618,19 +687,17 @@ hipError_t launch_attn(const Shape& s, const void* q, const void* kb, const void
   const float scale2 = s.scale * kLog2e;
   if (!s.bf16) {
     const int64_t ldv = vsel_ld(s.topk);
-    const dim3 grid((s.B * s.G + 3) / 4, s.Hkv, s.nseq);
-    const size_t smem = (size_t)s.D * 129 * sizeof(float);
+    const dim3 grid((s.B * s.G + 15) / 16, s.Hkv, s.nseq);
+    const size_t smem = ((size_t)8 * 16 * (s.D + 4) + 2 * 8 * 16) * sizeof(float);
     const void* kern = s.D == 128 ? (const void*)attn_f32_kernel<128> : (const void*)attn_f32_kernel<64>;
     hipError_t e = allow_smem(kern, smem);
     if (e != hipSuccess) return e;
     if (s.D == 128)
-      klaunch(attn_f32_kernel<128>, grid, 256, smem, st, (const float*)q, (const float*)kb, (const float*)vb,
-                                                 (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G,
-                                                 s.topk, ldv, scale2, (float*)out);
+      klaunch(attn_f32_kernel<128>, grid, 512, smem, st, (const float*)q, (const float*)kb, (const float*)vb,
+              (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G, s.topk, ldv, scale2, (float*)out);
     else
-      klaunch(attn_f32_kernel<64>, grid, 256, smem, st, (const float*)q, (const float*)kb, (const float*)vb,
-                                                (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G,
-                                                s.topk, ldv, scale2, (float*)out);
+      klaunch(attn_f32_kernel<64>, grid, 512, smem, st, (const float*)q, (const float*)kb, (const float*)vb,
+              (const float*)k_sel, (const float*)v_sel, s.B, s.Hq, s.Hkv, s.G, s.topk, ldv, scale2, (float*)out);
     return hipGetLastError();
   }
   const AttnGeom a = attn_geom(s);
