@@ -348,8 +348,12 @@ static herald_status select_common(const herald_problem* p, const void* q, int n
   const SelectWs w = carve_select(s, ws, &need);
   Shape sq = s;
   sq.B = nq;
-  HERALD_HIP(launch_merge(sq, q, w, stream));
-  HERALD_LAUNCH(0, stream, launch_scan(s, k_cache, w, stream));
+  if (scan_merges_query(s)) {
+    HERALD_LAUNCH(0, stream, launch_scan(s, k_cache, w, stream, q, nq));
+  } else {
+    HERALD_HIP(launch_merge(sq, q, w, stream));
+    HERALD_LAUNCH(0, stream, launch_scan(s, k_cache, w, stream));
+  }
   HERALD_LAUNCH(1, stream, launch_score_hist(s, w, stream));
   if (topc_in_lds(s)) {
     HERALD_LAUNCH(3, stream, launch_topc_lds(s, w, cand_idx, cand_score, stream));

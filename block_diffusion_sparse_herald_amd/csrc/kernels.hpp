@@ -90,7 +90,11 @@ constexpr int kAttnCombineThreads = 64;   // range-merge workgroup (8 output dim
 
 // select
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);
-hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st);
+// q (with nq query rows per block): bf16 caches on the register scan form the merged
+// query inside the scan and zero the histograms (scan_merges_query), in place of launch_merge
+hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st, const void* q = nullptr,
+                       int nq = 0);
+bool scan_merges_query(const Shape& s);
 hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st);
 hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipStream_t st);
 hipError_t launch_emit_candidates(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score,

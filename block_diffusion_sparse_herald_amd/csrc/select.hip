@@ -71,8 +71,14 @@ __global__ __launch_bounds__(128) void merge_kernel(const T* __restrict__ q, int
 // straight from the token-major cache (each lane 16 bytes of one key row).
 // A workgroup covers kScanTok tokens of one (sequence, KV head); each wave takes
 // 64 of them, 16 per MFMA column block, all 16-byte loads issued up front.
-template <int D>
+// MERGE: the workgroup also forms the merged query of its G heads itself (the B query
+// rows of the block summed in B / parts runs per thread while the key rows are in
+// flight, the runs added in a fixed order, times mul), in place of merge_kernel, and
+// zeroes its share of the radix histograms.
+template <int D, bool MERGE>
 __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__ k, const float* __restrict__ qbar,
+                                                        const bf16* __restrict__ q, int B, float mul,
+                                                        uint32_t* __restrict__ zero, int64_t zero_words,
                                                         const int64_t* __restrict__ seq_start, int Hq, int Hkv, int G,
                                                         int64_t total, int nchunk, float* __restrict__ logits,
                                                         float2* __restrict__ partials) {
@@ -80,6 +86,11 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
   constexpr int NB = kScanTok / (4 * 16);    // 16-key column blocks per wave
   __shared__ float2 red[4][16];
   const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  if (MERGE) {  // histograms of the candidate selection, zeroed before any workgroup leaves
+    const int64_t wg = ((int64_t)s * gridDim.y + g) * gridDim.x + chunk;
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+    for (int64_t i = wg * 256 + threadIdx.x; i < zero_words; i += nwg * 256) zero[i] = 0u;
+  }
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
   const int64_t tok0 = (int64_t)chunk * kScanTok;
@@ -87,13 +98,65 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, kq = lane >> 4;  // MFMA column (key) and contraction quarter of this lane
 
+  // B operand: key rows, all loads of this wave in flight at once
+  const int64_t row_stride = (int64_t)Hkv * D;
+  const bf16* kbase = k + (j0 * Hkv + g) * D + kq * 8;
+  const int64_t wtok0 = tok0 + w * (NB * 16);
+  uint4 kb[NB][KS];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t j = wtok0 + b * 16 + n;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[b][ks] = j < L ? ld16(kbase + j * row_stride + ks * 32) : make_uint4(0, 0, 0, 0);
+  }
+
+  __shared__ __align__(16) float qm[MERGE ? 8 * D : 4];  // merged query of the group's heads (MERGE)
+  if (MERGE) {
+    __shared__ __align__(16) float part[256 * 8];
+    const int items = G * (D / 8), parts = 256 / items;  // (head, 8-dim chunk) items, G * D / 8 <= 128
+    const int t = threadIdx.x, it = t % items, pt = t / items;
+    const int per = (B + parts - 1) / parts;
+    if (pt < parts) {
+      const int h = it / (D / 8), c = it % (D / 8);
+      const bf16* src = q + ((int64_t)s * B * Hq + g * G + h) * D + c * 8;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      const int b1 = min(B, (pt + 1) * per);
+      for (int b = pt * per; b < b1; b += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? ld16(src + (int64_t)(b + u) * Hq * D) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += bf16_lo(x[e]);
+            acc[2 * e + 1] += bf16_hi(x[e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[(pt * items + it) * 8 + e] = acc[e];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += 256) {
+      const int it2 = i / 8, e = i % 8;
+      float x = 0.f;
+      for (int p2 = 0; p2 < parts; ++p2) x += part[(p2 * items + it2) * 8 + e];
+      qm[i] = x * mul;  // [head][D]: item it2 = head * D/8 + chunk
+    }
+    __syncthreads();
+  }
+
   // A operand: query head n of the group (rows >= G are zero), dims ks*32 + 8*kq .. +8, hi and lo parts
   uint4 ahi[KS], alo[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     float x[8];
     if (n < G) {
-      const float* qp = qbar + ((int64_t)s * Hq + g * G + n) * D + ks * 32 + kq * 8;
+      const float* qp = MERGE ? qm + n * D + ks * 32 + kq * 8 : qbar + ((int64_t)s * Hq + g * G + n) * D + ks * 32 + kq * 8;
       const float4 x0 = *reinterpret_cast<const float4*>(qp);
       const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
       x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
@@ -111,18 +174,6 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
     }
     ahi[ks] = make_uint4(h[0], h[1], h[2], h[3]);
     alo[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  }
-
-  // B operand: key rows, all loads of this wave in flight at once
-  const int64_t row_stride = (int64_t)Hkv * D;
-  const bf16* kbase = k + (j0 * Hkv + g) * D + kq * 8;
-  const int64_t wtok0 = tok0 + w * (NB * 16);
-  uint4 kb[NB][KS];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int64_t j = wtok0 + b * 16 + n;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[b][ks] = j < L ? ld16(kbase + j * row_stride + ks * 32) : make_uint4(0, 0, 0, 0);
   }
 
   // lane holds logits of query heads 4*kq + i (i = 0..3) for key n of each column block;
@@ -858,7 +909,9 @@ static bool scan_in_lds(const Shape& s) {
   return s.bf16 && s.Hkv == 8 && s.G <= 8 && s.total >= (int64_t)4 * 256 * kScanTok;
 }
 
-hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st) {
+bool scan_merges_query(const Shape& s) { return s.bf16 && !scan_in_lds(s); }
+
+hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st, const void* q, int nq) {
   dim3 grid(ws.nchunk, s.Hkv, s.nseq);
   if (scan_in_lds(s)) {
     const size_t smem = (size_t)s.Hkv * ws.tpc * (s.G <= 4 ? 4 : 8) * sizeof(float);
@@ -874,12 +927,15 @@ hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStr
     return hipGetLastError();
   }
   if (s.bf16) {
-    if (s.D == 128)
-      klaunch(scan_mfma_kernel<128>, grid, 256, 0, st, (const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
-                                                  ws.nchunk, ws.logits, ws.partials);
-    else
-      klaunch(scan_mfma_kernel<64>, grid, 256, 0, st, (const bf16*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G, s.total,
-                                                 ws.nchunk, ws.logits, ws.partials);
+    // with q: the merged query formed inside the scan (scan_merges_query), no merge_kernel
+    const bool merge = q != nullptr;
+    const int nq1 = merge ? nq : 1;
+    const float mul = s.scale * kLog2e / (float)nq1;
+    const int64_t zero_words = merge ? (int64_t)s.nseq * s.Hkv * 3 * kRadixBins : 0;
+    auto kern = s.D == 128 ? (merge ? scan_mfma_kernel<128, true> : scan_mfma_kernel<128, false>)
+                           : (merge ? scan_mfma_kernel<64, true> : scan_mfma_kernel<64, false>);
+    klaunch(kern, grid, 256, 0, st, (const bf16*)k, ws.qbar, (const bf16*)q, nq1, mul, ws.hist, zero_words,
+            s.seq_start, s.Hq, s.Hkv, s.G, s.total, ws.nchunk, ws.logits, ws.partials);
     return hipGetLastError();
   }
 #define HERALD_SCAN_CASE(GG)                                                                                        \
