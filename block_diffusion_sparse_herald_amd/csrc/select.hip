@@ -98,6 +98,21 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, kq = lane >> 4;  // MFMA column (key) and contraction quarter of this lane
 
+  // MERGE: (head, 8-dim chunk) items of the merged query, G * D / 8 <= 128, each summed over
+  // B / parts query rows by `parts` threads; a thread's first eight rows are requested
+  // before the key rows, so that they (served from L2) arrive first
+  const int items = G * (D / 8), parts = 256 / items;
+  const int qit = threadIdx.x % items, qpt = threadIdx.x / items;
+  const int qper = (B + parts - 1) / parts, qb0 = qpt * qper, qb1 = min(B, qb0 + qper);
+  const bool qthread = MERGE && qpt < parts;
+  const bf16* qsrc = MERGE ? q + ((int64_t)s * B * Hq + g * G + qit / (D / 8)) * D + (qit % (D / 8)) * 8 : nullptr;
+  uint4 qv[MERGE ? 8 : 1];
+  if (MERGE) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      qv[u] = qthread && qb0 + u < qb1 ? ld16(qsrc + (int64_t)(qb0 + u) * Hq * D) : make_uint4(0, 0, 0, 0);
+  }
+
   // B operand: key rows, all loads of this wave in flight at once
   const int64_t row_stride = (int64_t)Hkv * D;
   const bf16* kbase = k + (j0 * Hkv + g) * D + kq * 8;
@@ -113,23 +128,18 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
   __shared__ __align__(16) float qm[MERGE ? 8 * D : 4];  // merged query of the group's heads (MERGE)
   if (MERGE) {
     __shared__ __align__(16) float part[256 * 8];
-    const int items = G * (D / 8), parts = 256 / items;  // (head, 8-dim chunk) items, G * D / 8 <= 128
-    const int t = threadIdx.x, it = t % items, pt = t / items;
-    const int per = (B + parts - 1) / parts;
-    if (pt < parts) {
-      const int h = it / (D / 8), c = it % (D / 8);
-      const bf16* src = q + ((int64_t)s * B * Hq + g * G + h) * D + c * 8;
+    if (qthread) {
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      const int b1 = min(B, (pt + 1) * per);
-      for (int b = pt * per; b < b1; b += 8) {
-        uint4 v[8];
+      for (int b = qb0; b < qb1; b += 8) {
+        if (b > qb0) {  // rows past the first eight (B / parts > 8)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? ld16(src + (int64_t)(b + u) * Hq * D) : make_uint4(0, 0, 0, 0);
+          for (int u = 0; u < 8; ++u) qv[u] = b + u < qb1 ? ld16(qsrc + (int64_t)(b + u) * Hq * D) : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          const uint32_t x[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             acc[2 * e] += bf16_lo(x[e]);
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[(pt * items + it) * 8 + e] = acc[e];
+      for (int e = 0; e < 8; ++e) part[(qpt * items + qit) * 8 + e] = acc[e];
     }
     __syncthreads();
     for (int i = threadIdx.x; i < G * D; i += 256) {
@@ -909,7 +919,12 @@ static bool scan_in_lds(const Shape& s) {
   return s.bf16 && s.Hkv == 8 && s.G <= 8 && s.total >= (int64_t)4 * 256 * kScanTok;
 }
 
-bool scan_merges_query(const Shape& s) { return s.bf16 && !scan_in_lds(s); }
+// The merge inside the scan costs every scan workgroup a little; it pays only while
+// there are few of them (measured: ahead at 1024 workgroups, behind at ~5200).
+bool scan_merges_query(const Shape& s) {
+  const int64_t nwg = (s.max_len + kScanTok - 1) / kScanTok * s.Hkv * s.nseq;
+  return s.bf16 && !scan_in_lds(s) && nwg <= 2048;
+}
 
 hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st, const void* q, int nq) {
   dim3 grid(ws.nchunk, s.Hkv, s.nseq);
