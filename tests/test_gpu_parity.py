@@ -46,10 +46,17 @@ SMALL = {
                             T=2, planted=8, seed_base=7100),
     "f32_d128_g2": Workload("f32_d128_g2", nseq=2, L=2100, Hq=4, Hkv=2, d=128, dtype="f32", B=8, C=300, topk=77,
                             T=2, planted=4, seed_base=7200),
-    # fp32, 80 query rows (a partial second 64-row pass of the statistics), candidates
-    # ending inside a 64-candidate score tile and a 128-candidate statistics tile
+    # fp32, 80 query rows (five 16-row tiles), candidates ending inside a 64-candidate
+    # refine tile (333 = 5 * 64 + 13), 20 in-block keys (a partial second key tile)
     "f32_rows80_c333": Workload("f32_rows80_c333", nseq=2, L=3000, Hq=8, Hkv=2, d=64, dtype="f32", B=20, C=333,
                                 topk=100, T=2, planted=4, seed_base=7250),
+    # fp32, 15 query rows (one partial 16-row tile) and 5 in-block keys
+    "f32_g3_b5": Workload("f32_g3_b5", nseq=2, L=1500, Hq=6, Hkv=2, d=64, dtype="f32", B=5, C=200, topk=45, T=2,
+                          planted=4, seed_base=7260),
+    # fp32 at the most query rows a group can have (B * G = 256) and d = 128: 128 KiB of
+    # query rows in the refine's LDS, sixteen query tiles in the attention
+    "f32_d128_rows256": Workload("f32_d128_rows256", nseq=1, L=3000, Hq=8, Hkv=1, d=128, dtype="f32", B=32, C=512,
+                                 topk=130, T=1, planted=4, seed_base=7270),
     "g1_b1": Workload("g1_b1", nseq=2, L=2500, Hq=2, Hkv=2, d=128, dtype="bf16", B=1, C=700, topk=64, T=2,
                       seed_base=7300),
     "g8_b32": Workload("g8_b32", nseq=1, L=4000, Hq=16, Hkv=2, d=128, dtype="bf16", B=32, C=512, topk=200, T=2,
