@@ -525,7 +525,7 @@ __global__ __launch_bounds__(512) void attn_f32_kernel(const float* __restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[i], p[i], o[dt], 0, 0, 0);
     }
-    cur = nxt;
+    if (t + NW < nt) cur = nxt;
   }
   l = xsum4(l);
   // merge the eight waves' (max, sum, output) per row

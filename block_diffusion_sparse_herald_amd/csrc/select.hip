@@ -406,9 +406,14 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ 
 }
 
 // fp32 caches: VALU GEMV. 8 lanes share a key row (16-byte loads), the G query
-// heads of the row's group are reduced with 3 xor steps.
-template <int D, int MAXG>
+// heads of the row's group are reduced with 3 xor steps. MERGE: as scan_mfma_kernel,
+// the merged query of the group formed in the workgroup (16-byte chunks of the B query
+// rows summed in runs per thread, the runs added in a fixed order, times mul), and the
+// radix histograms zeroed.
+template <int D, int MAXG, bool MERGE>
 __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict__ k, const float* __restrict__ qbar,
+                                                        const float* __restrict__ q, int B, float mul,
+                                                        uint32_t* __restrict__ zero, int64_t zero_words,
                                                         const int64_t* __restrict__ seq_start, int Hq, int Hkv, int G,
                                                         int64_t total, int nchunk, float* __restrict__ logits,
                                                         float2* __restrict__ partials) {
@@ -418,11 +423,52 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
   constexpr int U = 4;               // key rows in flight per lane
   __shared__ float2 red[32][8];
   const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  if (MERGE) {  // histograms of the candidate selection, zeroed before any workgroup leaves
+    const int64_t wg = ((int64_t)s * gridDim.y + g) * gridDim.x + chunk;
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+    for (int64_t i = wg * 256 + threadIdx.x; i < zero_words; i += nwg * 256) zero[i] = 0u;
+  }
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
   const int64_t tok0 = (int64_t)chunk * kScanTok;
   if (tok0 >= L) return;
   const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
+
+  __shared__ __align__(16) float qm[MERGE ? MAXG * D : 4];  // merged query of the group's heads (MERGE)
+  if (MERGE) {
+    __shared__ float4 part[256];
+    const int items = G * (D / 4), parts = 256 / items;  // (head, 4-dim chunk) items, G * D / 4 <= 256
+    const int it = threadIdx.x % items, pt = threadIdx.x / items;
+    const int per = (B + parts - 1) / parts, b0 = pt * per, b1 = min(B, b0 + per);
+    if (pt < parts) {
+      const float* src = q + ((int64_t)s * B * Hq + g * G + it / (D / 4)) * D + (it % (D / 4)) * 4;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int b = b0; b < b1; b += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = b + u < b1 ? *reinterpret_cast<const float4*>(src + (int64_t)(b + u) * Hq * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          acc.x += v[u].x;
+          acc.y += v[u].y;
+          acc.z += v[u].z;
+          acc.w += v[u].w;
+        }
+      }
+      part[pt * items + it] = acc;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += 256) {
+      float x = 0.f;
+      for (int p2 = 0; p2 < parts; ++p2) {
+        const float4 pv = part[p2 * items + i / 4];
+        x += (i & 3) == 0 ? pv.x : (i & 3) == 1 ? pv.y : (i & 3) == 2 ? pv.z : pv.w;
+      }
+      qm[i] = x * mul;  // [head][D]
+    }
+    __syncthreads();
+  }
 
   float qr[MAXG][PER];
 #pragma unroll
@@ -431,7 +477,9 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
     for (int i = 0; i < NL; ++i)
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
-        qr[hh][i * EPL + e] = hh < G ? qbar[((int64_t)s * Hq + g * G + hh) * D + (i * 8 + sub) * EPL + e] : 0.f;
+        qr[hh][i * EPL + e] = hh >= G ? 0.f
+                              : MERGE ? qm[hh * D + (i * 8 + sub) * EPL + e]
+                                      : qbar[((int64_t)s * Hq + g * G + hh) * D + (i * 8 + sub) * EPL + e];
 
   const int64_t row_stride = (int64_t)Hkv * D;
   const float* kbase = k + (j0 * Hkv + g) * D;
@@ -923,7 +971,7 @@ static bool scan_in_lds(const Shape& s) {
 // there are few of them (measured: ahead at 1024 workgroups, behind at ~5200).
 bool scan_merges_query(const Shape& s) {
   const int64_t nwg = (s.max_len + kScanTok - 1) / kScanTok * s.Hkv * s.nseq;
-  return s.bf16 && !scan_in_lds(s) && nwg <= 2048;
+  return !scan_in_lds(s) && nwg <= 2048;
 }
 
 hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStream_t st, const void* q, int nq) {
@@ -941,26 +989,28 @@ hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStr
               s.Hq, s.Hkv, s.G, s.total, ws.tpc, ws.nchunk, ws.logits, ws.partials);
     return hipGetLastError();
   }
+  // with q: the merged query formed inside the scan (scan_merges_query), no merge_kernel
+  const bool merge = q != nullptr;
+  const int nq1 = merge ? nq : 1;
+  const float mul = s.scale * kLog2e / (float)nq1;
+  const int64_t zero_words = merge ? (int64_t)s.nseq * s.Hkv * 3 * kRadixBins : 0;
   if (s.bf16) {
-    // with q: the merged query formed inside the scan (scan_merges_query), no merge_kernel
-    const bool merge = q != nullptr;
-    const int nq1 = merge ? nq : 1;
-    const float mul = s.scale * kLog2e / (float)nq1;
-    const int64_t zero_words = merge ? (int64_t)s.nseq * s.Hkv * 3 * kRadixBins : 0;
     auto kern = s.D == 128 ? (merge ? scan_mfma_kernel<128, true> : scan_mfma_kernel<128, false>)
                            : (merge ? scan_mfma_kernel<64, true> : scan_mfma_kernel<64, false>);
     klaunch(kern, grid, 256, 0, st, (const bf16*)k, ws.qbar, (const bf16*)q, nq1, mul, ws.hist, zero_words,
             s.seq_start, s.Hq, s.Hkv, s.G, s.total, ws.nchunk, ws.logits, ws.partials);
     return hipGetLastError();
   }
-#define HERALD_SCAN_CASE(GG)                                                                                        \
-  case GG:                                                                                                          \
-    if (s.D == 128)                                                                                                 \
-      klaunch(scan_valu_kernel<128, GG>, grid, 256, 0, st, (const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,      \
-                                                      s.total, ws.nchunk, ws.logits, ws.partials);                  \
-    else                                                                                                            \
-      klaunch(scan_valu_kernel<64, GG>, grid, 256, 0, st, (const float*)k, ws.qbar, s.seq_start, s.Hq, s.Hkv, s.G,       \
-                                                     s.total, ws.nchunk, ws.logits, ws.partials);                   \
+#define HERALD_SCAN_CASE(GG)                                                                                       \
+  case GG:                                                                                                         \
+    if (s.D == 128)                                                                                                \
+      klaunch(merge ? scan_valu_kernel<128, GG, true> : scan_valu_kernel<128, GG, false>, grid, 256, 0, st,          \
+              (const float*)k, ws.qbar, (const float*)q, nq1, mul, ws.hist, zero_words, s.seq_start, s.Hq, s.Hkv,  \
+              s.G, s.total, ws.nchunk, ws.logits, ws.partials);                                                    \
+    else                                                                                                           \
+      klaunch(merge ? scan_valu_kernel<64, GG, true> : scan_valu_kernel<64, GG, false>, grid, 256, 0, st,            \
+              (const float*)k, ws.qbar, (const float*)q, nq1, mul, ws.hist, zero_words, s.seq_start, s.Hq, s.Hkv,  \
+              s.G, s.total, ws.nchunk, ws.logits, ws.partials);                                                    \
     break;
   switch (maxg_of(s.G)) {
     HERALD_SCAN_CASE(1)
