@@ -548,48 +548,50 @@ __device__ __forceinline__ uint2 topk_count_t(const uint32_t (&v)[MAXIT][4], int
 }
 
 // Collects this wave's picks: pos and tie are the wave's running output position and
-// tie rank (uniform); teq says whether the wave holds keys equal to thr.
-template <int MAXIT, bool FULL, typename IndexF>
+// tie rank (uniform); teq says whether the wave holds keys equal to thr. Branch-free: a
+// key that is not taken is written to this lane's discard slot k + lane (the pick arrays
+// hold k + kTopkSlack entries), so no store needs an exec-mask branch.
+constexpr int kTopkSlack = 64;
+template <int MAXIT, bool FULL, bool VAL, typename IndexF>
 __device__ __forceinline__ void topk_collect_t(const uint32_t (&v)[MAXIT][4], IndexF index, int n, int nit,
                                                uint32_t lo, uint32_t thr, uint32_t ties_wanted, uint32_t teq,
                                                uint32_t k, uint32_t pos, uint32_t tie, int32_t* pick_idx,
                                                float* pick_val) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t discard = k + (uint32_t)lane;
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {
     if (it >= nit) continue;
     const int e = (w * nit + it) * 256 + 4 * lane;
-    bool take[4];
+    uint32_t take[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) take[c] = (FULL || e + c < n) && v[it][c] >= lo;
+    for (int c = 0; c < 4; ++c) take[c] = ((FULL || e + c < n) && v[it][c] >= lo) ? 1u : 0u;
     if (teq) {  // this wave holds keys equal to the threshold: rank them by position
-      bool eq[4];
-      uint32_t ne = 0;
+      uint32_t eq[4], ne = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        eq[c] = (FULL || e + c < n) && v[it][c] == thr;
-        ne += eq[c] ? 1u : 0u;
+        eq[c] = ((FULL || e + c < n) && v[it][c] == thr) ? 1u : 0u;
+        ne += eq[c];
       }
       const uint32_t incl = wave_incl_scan(ne);
       uint32_t r = tie + incl - ne;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (eq[c]) take[c] = r++ < ties_wanted;
+      for (int c = 0; c < 4; ++c) {
+        if (eq[c]) take[c] = r < ties_wanted ? 1u : 0u;
+        r += eq[c];
+      }
       tie += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
     }
-    uint32_t nt = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) nt += take[c] ? 1u : 0u;
+    const uint32_t nt = (take[0] + take[1]) + (take[2] + take[3]);
     const uint32_t incl = wave_incl_scan(nt);
     uint32_t p = pos + incl - nt;
     pos += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      if (take[c] && p < k) {
-        pick_idx[p] = index(it, c, e + c);
-        if (pick_val) pick_val[p] = __uint_as_float(v[it][c]);
-      }
-      p += take[c] ? 1u : 0u;
+      const uint32_t dst = take[c] && p < k ? p : discard;
+      pick_idx[dst] = index(it, c, e + c);
+      if (VAL) pick_val[dst] = __uint_as_float(v[it][c]);
+      p += take[c];
     }
   }
 }
@@ -597,7 +599,8 @@ __device__ __forceinline__ void topk_collect_t(const uint32_t (&v)[MAXIT][4], In
 // Collects, in ascending position order, every key above thr plus the first ties_wanted
 // keys equal to it (all_ties: every key equal to thr is wanted, so the test is x >= thr)
 // into pick_idx[p] = index(chunk, element, position) and pick_val[p] (if not NULL) in
-// LDS, then writes the k picks to out / outs (outs may be NULL) with coalesced stores.
+// LDS (each of k + kTopkSlack entries), then writes the k picks to out / outs (outs may
+// be NULL) with coalesced stores.
 // wcnt holds kTopkWaves pairs in LDS. Every thread of the workgroup calls it. Waves whose
 // positions all lie below n skip the per-key validity tests.
 template <int MAXIT, typename IndexF>
@@ -624,10 +627,17 @@ __device__ __forceinline__ void topk_emit(const uint32_t (&v)[MAXIT][4], IndexF 
     pos += wcnt[x][0] + take;
     tie += wcnt[x][1];
   }
-  if (full)
-    topk_collect_t<MAXIT, true>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
-  else
-    topk_collect_t<MAXIT, false>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
+  if (pick_val) {
+    if (full)
+      topk_collect_t<MAXIT, true, true>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
+    else
+      topk_collect_t<MAXIT, false, true>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
+  } else {
+    if (full)
+      topk_collect_t<MAXIT, true, false>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
+    else
+      topk_collect_t<MAXIT, false, false>(v, index, n, nit, lo, thr, ties_wanted, teq, k, pos, tie, pick_idx, pick_val);
+  }
   __syncthreads();
   for (uint32_t i = threadIdx.x; i < k; i += kTopkWaves * 64) {
     out[i] = pick_idx[i];

@@ -292,7 +292,7 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
   if constexpr (STAGED) {
     constexpr int MAXIT = topk_chunks(kMaxCandidates);
     __shared__ uint32_t h2[kRadixBins], h3[kRadixBins / 2];
-    extern __shared__ int32_t picks[];  // [topk] picks, then [topk] scores when they are wanted
+    extern __shared__ int32_t picks[];  // [topk + kTopkSlack] picks, then as many scores when they are wanted
     const int tid = threadIdx.x, w = tid >> 6;
     const int nit = topk_chunks(C);
     uint32_t v[MAXIT][4], ix[MAXIT][4];
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
     const uint32_t thr = (prefix << 10) | dig[0];
     const uint32_t ties = want - dig[1];
     topk_emit<MAXIT>(v, [&](int it, int c, int) { return (int32_t)ix[it][c]; }, C, nit, thr, ties,
-                     h3[dig[0]] == ties, (uint32_t)topk, picks, outs ? reinterpret_cast<float*>(picks + topk) : nullptr,
+                     h3[dig[0]] == ties, (uint32_t)topk, picks, outs ? reinterpret_cast<float*>(picks + topk + kTopkSlack) : nullptr,
                      out, outs, wcnt);
   } else {
     const uint32_t* u = reinterpret_cast<const uint32_t*>(rscore + base);
@@ -408,7 +408,7 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
             topk_idx, topk_score);
     return hipGetLastError();
   }
-  const size_t smem = (size_t)s.topk * sizeof(int32_t) * (topk_score ? 2 : 1);
+  const size_t smem = (size_t)(s.topk + kTopkSlack) * sizeof(int32_t) * (topk_score ? 2 : 1);
   hipError_t e = allow_smem((const void*)refine_select_kernel<true>, smem);
   if (e != hipSuccess) return e;
   klaunch(refine_select_kernel<true>, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, s.Hkv, s.C, s.topk,

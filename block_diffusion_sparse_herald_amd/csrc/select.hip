@@ -882,7 +882,7 @@ __global__ __launch_bounds__(1024) void topc_lds_kernel(const float* __restrict_
   __shared__ uint32_t h2[kRadixBins], h3[kRadixBins / 2];
   __shared__ uint32_t wcnt[kTopkWaves][2];
   __shared__ uint32_t dig[4];
-  extern __shared__ int32_t picks[];  // [C] candidates, then [C] scores when they are wanted
+  extern __shared__ int32_t picks[];  // [C + kTopkSlack] candidates, then as many scores when they are wanted
   const int g = blockIdx.x, s = blockIdx.y;
   const int64_t j0 = seq_start[s];
   const int L = (int)(seq_start[s + 1] - j0);
@@ -936,7 +936,7 @@ __global__ __launch_bounds__(1024) void topc_lds_kernel(const float* __restrict_
   const uint32_t ties = want - dig[1];
   float* outs = cand_score ? cand_score + (int64_t)(s * Hkv + g) * C : nullptr;
   topk_emit<MAXIT>(v, [](int, int, int pos) { return (int32_t)pos; }, L, nit, thr, ties, h3[dig[0]] == ties,
-                   (uint32_t)C, picks, outs ? reinterpret_cast<float*>(picks + C) : nullptr,
+                   (uint32_t)C, picks, outs ? reinterpret_cast<float*>(picks + C + kTopkSlack) : nullptr,
                    cand + (int64_t)(s * Hkv + g) * C, outs, wcnt);
 }
 
@@ -1047,7 +1047,7 @@ hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipSt
 bool topc_in_lds(const Shape& s) { return s.max_len <= kTopcLdsMaxLen; }
 
 hipError_t launch_topc_lds(const Shape& s, const SelectWs& ws, int32_t* cand, float* cand_score, hipStream_t st) {
-  const size_t smem = (size_t)s.C * sizeof(int32_t) * (cand_score ? 2 : 1);
+  const size_t smem = (size_t)(s.C + kTopkSlack) * sizeof(int32_t) * (cand_score ? 2 : 1);
   hipError_t e = allow_smem((const void*)topc_lds_kernel, smem);
   if (e != hipSuccess) return e;
   klaunch(topc_lds_kernel, dim3(s.Hkv, s.nseq), 1024, smem, st, ws.scores, s.seq_start, s.Hkv, s.total, s.C, ws.hist,
