@@ -249,7 +249,8 @@ def main(argv=None):
                                               for _ in range(replicas - 1)]
     seq_dev = DevArray.from_host(hip, batch.seq_start)
     r = BlockRunner(batch.seq_start, wl.B, wl.Hq, wl.Hkv, wl.d, wl.C, wl.topk, wl.dtype,
-                    alloc=lambda shape, dt, zero=False: DevArray(hip, shape, dt, zero), seq_start_dev=seq_dev)
+                    alloc=lambda shape, dt, zero=False, contiguous=False: DevArray(hip, shape, dt, zero, contiguous),
+                    seq_start_dev=seq_dev)
     q0 = dev["q0"]
     qs, kbs, vbs = ([dev[n].offset(t) for t in range(wl.T)] for n in ("q_steps", "kb_steps", "vb_steps"))
     stream = hip.stream()

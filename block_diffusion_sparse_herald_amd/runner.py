@@ -33,7 +33,7 @@ def batch_to_device(batch, device="cuda") -> dict:
 def torch_alloc(device="cuda") -> Callable:
     import torch
 
-    def alloc(shape, dtype, zero=False):
+    def alloc(shape, dtype, zero=False, contiguous=False):  # the caching allocator places its own blocks
         dt = {np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32,
               np.dtype(np.uint16): torch.bfloat16, np.dtype(np.uint8): torch.uint8}[np.dtype(dtype)]
         return (torch.zeros if zero else torch.empty)(tuple(shape), dtype=dt, device=device)
@@ -44,8 +44,12 @@ def torch_alloc(device="cuda") -> Callable:
 class BlockRunner:
     """Outputs and workspaces for one (workload shape, sequence offsets).
 
-    `alloc(shape, numpy_dtype, zero=False)` returns device memory exposing data_ptr() and
-    nbytes (uint16 stands for bf16), zero-filled when asked (the attention workspace);
+    `alloc(shape, numpy_dtype, zero=False, contiguous=False)` returns device memory exposing
+    data_ptr() and nbytes (uint16 stands for bf16), zero-filled when asked (the attention
+    workspace); `contiguous` asks for physically contiguous memory where the allocator can
+    place it (the attention workspace, whose split partial results are written and read back
+    within one call, runs faster from it; the full-cache scan writes its logits faster to
+    scattered pages, so the other buffers do not ask);
     `seq_start_dev` is the device copy of the offsets (made with the allocator's
     framework when omitted).
     """
@@ -78,7 +82,7 @@ class BlockRunner:
                     self.ws[name] = None
                     continue
                 raise
-            self.ws[name] = alloc((max(n, 256),), np.uint8, zero=name == "attn")
+            self.ws[name] = alloc((max(n, 256),), np.uint8, zero=name == "attn", contiguous=name == "attn")
         self.attn_splits = H.herald_attn_splits(self.problem)
 
     def select(self, q_merge, k_cache, stream=None):
