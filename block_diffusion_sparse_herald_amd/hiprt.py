@@ -218,3 +218,17 @@ class DevArray:
         d = DevArray(self.hip, self.shape, self.dtype)
         self.hip.copy(d.ptr, self.ptr, self.nbytes)
         return d
+
+
+class DevView:
+    """Bytes [offset, offset + nbytes) of a device allocation, which it keeps alive."""
+
+    def __init__(self, parent: DevArray, offset: int, nbytes: int):
+        if offset < 0 or nbytes < 0 or offset + nbytes > parent.nbytes:
+            raise ValueError(f"view [{offset}, {offset + nbytes}) outside a {parent.nbytes}-byte allocation")
+        self.parent, self.offset, self.nbytes = parent, int(offset), int(nbytes)
+        self.ptr = parent.ptr + self.offset
+
+    def data_ptr(self) -> int:
+        return self.ptr
+
