@@ -344,13 +344,14 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
 
 // Merges the key ranges of one (sequence, KV head): 8 output dimensions per thread
 // (two 16-byte fp32 loads per range, one 16-byte bf16 store), the ranges taken 8 at a
-// time (loads first) with a running (max, sum).
-template <int D>
-__global__ __launch_bounds__(kAttnCombineThreads) void attn_combine_kernel(const float* __restrict__ o_part,
+// time (loads first) with a running (max, sum). NT threads per workgroup: 64 for small
+// merges (more workgroups), 256 for large ones (fewer to dispatch).
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void attn_combine_kernel(const float* __restrict__ o_part,
                                                                            const float2* __restrict__ ml_part,
                                                                            AttnGeom a, bf16* __restrict__ out) {
   constexpr int CH = 8, TPR = D / 8;  // threads per output row
-  const int idx = blockIdx.x * kAttnCombineThreads + threadIdx.x;
+  const int idx = blockIdx.x * NT + threadIdx.x;
   const int R = a.B * a.G;
   const int per_unit = R * TPR;
   const int unit = a.rcp_pu ? (int)__umulhi((uint32_t)idx, a.rcp_pu) : idx / per_unit;
@@ -674,11 +675,19 @@ hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t 
   const float* o_part = static_cast<const float*>(ws);
   const float2* ml_part = reinterpret_cast<const float2*>(static_cast<char*>(ws) + align256(rows * s.D * sizeof(float)));
   const int64_t n = (int64_t)a.nunits * a.B * a.G * (s.D / 8);
-  const dim3 grid((unsigned)((n + kAttnCombineThreads - 1) / kAttnCombineThreads));
-  if (s.D == 128)
-    klaunch(attn_combine_kernel<128>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
-  else
-    klaunch(attn_combine_kernel<64>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
+  const int nt = n >= (int64_t)256 * 256 ? 256 : kAttnCombineThreads;
+  const dim3 grid((unsigned)((n + nt - 1) / nt));
+  if (nt == 256) {
+    if (s.D == 128)
+      klaunch(attn_combine_kernel<128, 256>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
+    else
+      klaunch(attn_combine_kernel<64, 256>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
+  } else {
+    if (s.D == 128)
+      klaunch(attn_combine_kernel<128, kAttnCombineThreads>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
+    else
+      klaunch(attn_combine_kernel<64, kAttnCombineThreads>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
+  }
   return hipGetLastError();
 }
 

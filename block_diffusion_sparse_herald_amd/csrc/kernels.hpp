@@ -86,7 +86,8 @@ constexpr int kAttnTargetWorkgroups = 256;  // one per compute unit
 constexpr int kAttnFewPairs = 96;  // below this (pairs x four-tile row groups x 5) the few-pairs geometry applies
 constexpr int kAttnTargetWorkgroupsFew = 192;  // with two query tiles per workgroup
 constexpr int kAttnMaxStages = 4;
-constexpr int kAttnCombineThreads = 64;   // range-merge workgroup (8 output dims per thread)
+constexpr int kAttnCombineThreads = 64;   // range-merge workgroup (8 output dims per thread); 256 once that
+                                           // still gives >= 256 workgroups
 
 // select
 hipError_t launch_merge(const Shape& s, const void* q, const SelectWs& ws, hipStream_t st);

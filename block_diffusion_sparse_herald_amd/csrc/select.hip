@@ -253,8 +253,9 @@ __device__ __forceinline__ int scan_swz(int r, int hshift) {
 // instruction reads 1 KiB of contiguous cache. A workgroup covers tpc tokens of one
 // sequence, all KV heads, in steps of SR cache rows (SR / Hkv tokens x Hkv heads,
 // contiguous in the token-major cache): direct-to-LDS loads of the step, one wait,
-// then the products. Several workgroups share a compute unit, so one's loads overlap
-// another's products. Wave w takes the step's 16-row blocks p = w, w + 4, ...; block p
+// every wave's fragments of the step into registers, then the next step's loads are
+// issued before this step's products. Several workgroups share a compute unit, so
+// one's loads also overlap another's products. Wave w takes the step's 16-row blocks p = w, w + 4, ...; block p
 // is 16 tokens (16 (p / Hkv) ..) of KV head p % Hkv. The logits of the tpc tokens
 // collect in LDS and leave at the end as one contiguous run per KV head (small
 // scattered stores between the loads cost several times their bytes).
@@ -327,8 +328,8 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ 
     }
 
   const int rr = lane / CPR, pc = lane % CPR;
-  for (int i = 0; i < nstep; ++i) {
-    // ---- the step's rows into LDS: instruction u of wave w fills rows (4u + w) * RPI ..
+  // the step's rows into LDS: instruction u of wave w fills rows (4u + w) * RPI ..
+  auto issue = [&](int i) {
     const int64_t t0 = tok0 + (int64_t)i * TS;
 #pragma unroll
     for (int u = 0; u < NIS; ++u) {
@@ -337,23 +338,37 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ 
       const bf16* src = k + ((j0 + tok) * Hkv + (r & (Hkv - 1))) * D + ((pc ^ scan_swz<D>(r, hshift)) * 8);
       lds_dma16(src, lds0 + (uint32_t)((4 * u + w) * RPI * D) * 2u);
     }
+  };
+  issue(0);
+  for (int i = 0; i < nstep; ++i) {
+    const int64_t t0 = tok0 + (int64_t)i * TS;
     wait_vm<0>();
-    __syncthreads();
+    __syncthreads();  // step i's rows are in LDS
+    // every fragment of the step into registers, then the rows are free for step i + 1,
+    // whose loads run while this step's products and softmax do
+    uint4 kb[NBW][KS];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const int p = w + 4 * q;
+      const int gg = p & (Hkv - 1);
+      const int tl = (p >> hshift) * 16 + n;
+      const int r = (tl << hshift) + gg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[q][ks] = *reinterpret_cast<const uint4*>(rows + r * D + (((ks * 4 + kq) ^ scan_swz<D>(r, hshift)) * 8));
+    }
+    __syncthreads();  // every wave has its fragments
+    if (i + 1 < nstep) issue(i + 1);
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
       const int p = w + 4 * q;
       const int gg = p & (Hkv - 1);
       const int tl = (p >> hshift) * 16 + n;  // token within the step
-      const int r = (tl << hshift) + gg;
-      uint4 kb[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kb[ks] = *reinterpret_cast<const uint4*>(rows + r * D + (((ks * 4 + kq) ^ scan_swz<D>(r, hshift)) * 8));
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        acc = mfma16x16x32(ahi[q & 1][ks], kb[ks], acc);
-        acc = mfma16x16x32(alo[q & 1][ks], kb[ks], acc);
+        acc = mfma16x16x32(ahi[q & 1][ks], kb[q][ks], acc);
+        acc = mfma16x16x32(alo[q & 1][ks], kb[q][ks], acc);
       }
       const int64_t j = t0 + tl;
       if (j < L) {
@@ -374,7 +389,6 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ 
         }
       }
     }
-    __syncthreads();  // every wave is done with the rows before the next step's loads
   }
   // (max, sum) per block and head: over the 16 tokens of the lane group
 #pragma unroll
