@@ -14,7 +14,8 @@
 //                         sum over rows, in a fixed order (each lane over its row's
 //                         tiles, then over the 16 lanes of a row with DPP shifts).
 // A workgroup of four waves covers 256 candidates (bf16: four 16-candidate MFMA tiles
-// per wave) or 64 (fp32: one tile per wave). The candidate key rows, gathered from the
+// per wave) or 64 (fp32: one tile per wave); large bf16 candidate sets take eight waves
+// and 512 candidates (refine_waves). The candidate key rows, gathered from the
 // cache by index, go straight into registers as the A operand; the group's B*G query
 // rows, shared by the waves, are streamed into LDS with direct-to-LDS loads and read as
 // the B operand (v_mfma_f32_16x16x32_bf16 or v_mfma_f32_16x16x4_f32, fp32 accumulate).
@@ -35,8 +36,8 @@ namespace herald {
 // candidates).
 template <typename T>
 constexpr int refine_mt() { return sizeof(T) == 2 ? 4 : 1; }
-template <typename T>
-constexpr int refine_tile() { return 4 * 16 * refine_mt<T>(); }
+template <typename T, int NW>
+constexpr int refine_tile() { return NW * 16 * refine_mt<T>(); }
 
 // 16-byte chunk c of an LDS query row r is stored at chunk c ^ refine_swz(r): the 16
 // rows one MFMA fragment read touches hit distinct banks.
@@ -96,7 +97,7 @@ __device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[MT][RefineFr
 // (candidates past C re-read the last one, masked later); every lane reads 16 bytes of
 // a row per load. refine_wait_rows: once both have landed, the workgroup may read the
 // query rows.
-template <typename T, int D, int MT>
+template <typename T, int D, int MT, int NW>
 __device__ __forceinline__ void refine_issue_rows(const T* __restrict__ q, const T* __restrict__ k,
                                                   const int32_t* __restrict__ cand, int64_t j0, int s, int g, int B,
                                                   int Hq, int Hkv, int G, int C, int R, int RT, int ctile, T* qs,
@@ -104,7 +105,6 @@ __device__ __forceinline__ void refine_issue_rows(const T* __restrict__ q, const
   using F = RefineFrag<T, D>;
   constexpr int CPR = D / F::EPC;  // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;    // rows per load instruction
-  constexpr int NW = 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rr = lane / CPR, p = lane % CPR;
   // query rows: the waves take turns by instruction
@@ -120,7 +120,7 @@ __device__ __forceinline__ void refine_issue_rows(const T* __restrict__ q, const
   const T* rows[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int c = min(ctile * refine_tile<T>() + (w * MT + mt) * 16 + (lane & 15), C - 1);
+    const int c = min(ctile * refine_tile<T, NW>() + (w * MT + mt) * 16 + (lane & 15), C - 1);
     rows[mt] = k + ((j0 + cd[c]) * Hkv + g) * D;
   }
 #pragma unroll
@@ -134,22 +134,22 @@ __device__ __forceinline__ void refine_wait_rows() {
   __syncthreads();
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void refine_stats_kernel(const T* __restrict__ q, const T* __restrict__ k,
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void refine_stats_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const int32_t* __restrict__ cand,
                                                            const int64_t* __restrict__ seq_start, int B, int Hq,
                                                            int Hkv, int G, int C, float scale2, int ntile,
                                                            float2* __restrict__ row_stats) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NW = 4, MT = refine_mt<T>();
+  constexpr int MT = refine_mt<T>();
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = B * G, RT = (R + 15) / 16;
   T* qs = reinterpret_cast<T*>(smem);                           // [RT*16][D]
   float2* wstat = reinterpret_cast<float2*>(qs + RT * 16 * D);  // [NW][RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int cbase = tile * refine_tile<T>() + w * MT * 16;
+  const int cbase = tile * refine_tile<T, NW>() + w * MT * 16;
   uint4 a[MT][RefineFrag<T, D>::NC];
-  refine_issue_rows<T, D, MT>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
+  refine_issue_rows<T, D, MT, NW>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
   refine_wait_rows();
 
   const bool full = cbase + MT * 16 <= C;  // no candidate of this wave past C
@@ -192,8 +192,8 @@ __global__ __launch_bounds__(256) void refine_stats_kernel(const T* __restrict__
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void refine_scores_kernel(const T* __restrict__ q, const T* __restrict__ k,
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                             const int32_t* __restrict__ cand,
                                                             const int64_t* __restrict__ seq_start, int B, int Hq,
                                                             int Hkv, int G, int C, float scale2, int ntile,
@@ -207,12 +207,12 @@ __global__ __launch_bounds__(256) void refine_scores_kernel(const T* __restrict_
   float* rowM = reinterpret_cast<float*>(qs + RT * 16 * D);  // [RT*16]
   float* rowIZ = rowM + RT * 16;                             // [RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int cbase = tile * refine_tile<T>() + w * MT * 16;
+  const int cbase = tile * refine_tile<T, NW>() + w * MT * 16;
   uint4 a[MT][RefineFrag<T, D>::NC];
-  refine_issue_rows<T, D, MT>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
+  refine_issue_rows<T, D, MT, NW>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
   // per-row normalisers over all tiles, merged in tile order while the rows stream in
   // (a row's tile statistics are contiguous; 16 tiles per batch of loads)
-  for (int r = threadIdx.x; r < RT * 16; r += 256) {
+  for (int r = threadIdx.x; r < RT * 16; r += NW * 64) {
     float M = -INFINITY, Z = 0.f;
     if (r < R) {
       const float2* rs = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);  // 16-byte aligned rows
@@ -356,40 +356,60 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
 
 // ------------------------------------------------------------------ launchers
 
+// Waves per refine workgroup: 4 (256 bf16 candidates), or 8 (512) when a (sequence,
+// KV head) has more than 16 tiles of 256 and 512-candidate workgroups still number
+// >= 256: the scores kernel then merges at most 16 tile statistics per row (one batch
+// of loads), and the query rows in LDS serve twice the candidates. Measured at
+// C = 8192 over 32 pairs: -6 us per step; at C = 4096 over 128 pairs 8 waves were
+// not faster.
+static int refine_waves(const Shape& s) {
+  if (!s.bf16) return 4;
+  const int t4 = (s.C + refine_tile<bf16, 4>() - 1) / refine_tile<bf16, 4>();
+  const int64_t wg8 = (int64_t)((s.C + refine_tile<bf16, 8>() - 1) / refine_tile<bf16, 8>()) * s.Hkv * s.nseq;
+  return t4 > 16 && wg8 >= 256 ? 8 : 4;
+}
+
 static size_t refine_smem(const Shape& s, bool stats) {
   const int RT = (s.B * s.G + 15) / 16;
   const size_t rows = (size_t)RT * 16 * s.D * (s.bf16 ? 2 : 4);
-  return rows + (stats ? (size_t)4 * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
+  return rows + (stats ? (size_t)refine_waves(s) * RT * 16 * sizeof(float2) : (size_t)2 * RT * 16 * sizeof(float));
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 static hipError_t launch_refine_t(const Shape& s, const void* q, const void* k, const int32_t* cand,
                                   const RefineWs& ws, bool stats, hipStream_t st) {
   const dim3 grid(ws.ntile, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
   const size_t smem = refine_smem(s, stats);
-  const void* kern = stats ? (const void*)refine_stats_kernel<T, D> : (const void*)refine_scores_kernel<T, D>;
+  const void* kern = stats ? (const void*)refine_stats_kernel<T, D, NW> : (const void*)refine_scores_kernel<T, D, NW>;
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
   if (stats)
-    klaunch(refine_stats_kernel<T, D>, grid, 256, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B, s.Hq,
-            s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
+    klaunch(refine_stats_kernel<T, D, NW>, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B,
+            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
   else
-    klaunch(refine_scores_kernel<T, D>, grid, 256, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B, s.Hq,
-            s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
+    klaunch(refine_scores_kernel<T, D, NW>, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B,
+            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
   return hipGetLastError();
 }
 
 static hipError_t launch_refine(const Shape& s, const void* q, const void* k, const int32_t* cand,
                                 const RefineWs& ws, bool stats, hipStream_t st) {
-  if (s.bf16)
-    return s.D == 128 ? launch_refine_t<bf16, 128>(s, q, k, cand, ws, stats, st)
-                      : launch_refine_t<bf16, 64>(s, q, k, cand, ws, stats, st);
-  return s.D == 128 ? launch_refine_t<float, 128>(s, q, k, cand, ws, stats, st)
-                    : launch_refine_t<float, 64>(s, q, k, cand, ws, stats, st);
+  if (s.bf16) {
+    if (refine_waves(s) == 8)
+      return s.D == 128 ? launch_refine_t<bf16, 128, 8>(s, q, k, cand, ws, stats, st)
+                        : launch_refine_t<bf16, 64, 8>(s, q, k, cand, ws, stats, st);
+    return s.D == 128 ? launch_refine_t<bf16, 128, 4>(s, q, k, cand, ws, stats, st)
+                      : launch_refine_t<bf16, 64, 4>(s, q, k, cand, ws, stats, st);
+  }
+  return s.D == 128 ? launch_refine_t<float, 128, 4>(s, q, k, cand, ws, stats, st)
+                    : launch_refine_t<float, 64, 4>(s, q, k, cand, ws, stats, st);
 }
 
-int refine_tile_of(const Shape& s) { return s.bf16 ? refine_tile<bf16>() : refine_tile<float>(); }
+int refine_tile_of(const Shape& s) {
+  if (!s.bf16) return refine_tile<float, 4>();
+  return refine_waves(s) == 8 ? refine_tile<bf16, 8>() : refine_tile<bf16, 4>();
+}
 
 hipError_t launch_refine_stats(const Shape& s, const void* q, const void* k, const int32_t* cand, const RefineWs& ws,
                                hipStream_t st) {

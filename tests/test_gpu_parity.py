@@ -81,6 +81,10 @@ SMALL = {
     # two rounds, the largest candidate set spreads picks over both
     "radix_two_rounds": Workload("radix_two_rounds", nseq=1, L=300000, Hq=4, Hkv=1, d=64, dtype="bf16", B=4,
                                  C=16384, topk=2000, T=1, planted=8, seed_base=8400),
+    # more than 16 refine tiles of 256 candidates over enough pairs: 8-wave refine
+    # workgroups of 512 candidates, a ragged last tile (4500 = 8 x 512 + 404), head dim 64
+    "refine_8waves": Workload("refine_8waves", nseq=4, L=6000, Hq=16, Hkv=8, d=64, dtype="bf16", B=16, C=4500,
+                              topk=600, T=1, planted=8, seed_base=8500),
     # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
     "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
                            T=2, seed_base=7800),
