@@ -549,7 +549,7 @@ def offload_pipeline(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, str
         pool_v.numpy()[...] = batch.v_cache
         k_src, v_src = pool_k, pool_v
     k_scan = [k for k, _ in kv]
-    alloc = lambda shape, dt, zero=False: DevArray(hip, shape, dt, zero)  # noqa: E731
+    alloc = lambda shape, dt, zero=False, contiguous=False: DevArray(hip, shape, dt, zero, contiguous)  # noqa: E731
     pipe = SpeculativePipeline(r, alloc, StreamOps.hip(hip), src_is_host=0 if device else 2,
                                overlap_refine=args.overlap_refine)
     a_stream, b_stream = stream, hip.stream()
@@ -655,7 +655,7 @@ def other_method(args, hip, wl, batch, kv, seq_dev, r, q0, qs, kbs, vbs, stream)
               f"workload {wl.name} is ragged", file=sys.stderr)
         return 2
     L = int(lengths.max())
-    alloc = lambda shape, dt, zero=False: DevArray(hip, shape, dt, zero)  # noqa: E731
+    alloc = lambda shape, dt, zero=False, contiguous=False: DevArray(hip, shape, dt, zero, contiguous)  # noqa: E731
     iota = None if args.method == "compressed" else DevArray.from_host(hip, np.ascontiguousarray(
         np.broadcast_to(np.arange(L, dtype=np.int32), (wl.nseq, wl.Hkv, L))))
     if args.method == "compressed":

@@ -9,6 +9,7 @@ herald_block_attn once per denoising step.
 
 from __future__ import annotations
 
+import inspect
 from typing import Callable, Optional
 
 import numpy as np
@@ -30,6 +31,15 @@ def batch_to_device(batch, device="cuda") -> dict:
             for n in ["q0", "k_cache", "v_cache", "q_steps", "kb_steps", "vb_steps"]}
 
 
+def _takes_keyword(fn: Callable, name: str) -> bool:
+    """Whether `fn` accepts keyword `name` (allocators written before the placement hint do not)."""
+    try:
+        params = inspect.signature(fn).parameters
+    except (TypeError, ValueError):
+        return False
+    return name in params or any(p.kind is inspect.Parameter.VAR_KEYWORD for p in params.values())
+
+
 def torch_alloc(device="cuda") -> Callable:
     import torch
 
@@ -44,7 +54,7 @@ def torch_alloc(device="cuda") -> Callable:
 class BlockRunner:
     """Outputs and workspaces for one (workload shape, sequence offsets).
 
-    `alloc(shape, numpy_dtype, zero=False, contiguous=False)` returns device memory exposing
+    `alloc(shape, numpy_dtype, zero=False[, contiguous=False])` returns device memory exposing
     data_ptr() and nbytes (uint16 stands for bf16), zero-filled when asked (the attention
     workspace); `contiguous` asks for physically contiguous memory where the allocator can
     place it (the attention workspace, whose split partial results are written and read back
@@ -82,7 +92,8 @@ class BlockRunner:
                     self.ws[name] = None
                     continue
                 raise
-            self.ws[name] = alloc((max(n, 256),), np.uint8, zero=name == "attn", contiguous=name == "attn")
+            hint = {"contiguous": True} if name == "attn" and _takes_keyword(alloc, "contiguous") else {}
+            self.ws[name] = alloc((max(n, 256),), np.uint8, zero=name == "attn", **hint)
         self.attn_splits = H.herald_attn_splits(self.problem)
 
     def select(self, q_merge, k_cache, stream=None):
