@@ -85,6 +85,17 @@ SMALL = {
     # workgroups of 512 candidates, a ragged last tile (4500 = 8 x 512 + 404), head dim 64
     "refine_8waves": Workload("refine_8waves", nseq=4, L=6000, Hq=16, Hkv=8, d=64, dtype="bf16", B=16, C=4500,
                               topk=600, T=1, planted=8, seed_base=8500),
+    # the same eight-wave refine at head dim 128
+    "refine_8waves_d128": Workload("refine_8waves_d128", nseq=4, L=5000, Hq=32, Hkv=8, d=128, dtype="bf16", B=8,
+                                   C=4500, topk=300, T=1, planted=8, seed_base=8600),
+    # 256 rows per (sequence, KV head) over 16 pairs: four key ranges merged by 256-thread
+    # workgroups on the XCD that ran each pair's ranges
+    "merge_256_home": Workload("merge_256_home", nseq=2, L=3000, Hq=32, Hkv=8, d=128, dtype="bf16", B=64, C=1200,
+                               topk=1000, T=1, planted=8, seed_base=8700),
+    # 12 pairs, four key ranges each: the merge's pairs straddle XCD boundaries (12 work
+    # items per XCD, 8 per pair)
+    "merge_home_12units": Workload("merge_home_12units", nseq=3, L=2500, Hq=16, Hkv=4, d=128, dtype="bf16", B=16,
+                                   C=900, topk=600, T=2, planted=8, seed_base=8800),
     # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
     "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
                            T=2, seed_base=7800),
