@@ -81,6 +81,17 @@ struct Vec16<bf16> {
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// A 16-byte load whose value is replaced by zeros when `ok` is false. The load is always
+// issued (p must be a valid address either way: callers clamp it) and the zeros are
+// selected afterwards. Written as `ok ? ld16(p) : 0`, the load sits in a branch, and the
+// register copy the compiler makes at the join needs the loaded value there: it waits for
+// every load in flight at that point, which serialised the rest of a kernel's loads
+// behind a full memory round trip.
+__device__ __forceinline__ uint4 ld16_or_zero(const void* p, bool ok) {
+  const uint4 v = ld16(p);
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 // 16-byte store marked non-temporal (global_store_dwordx4 ... nt).
 __device__ __forceinline__ void st16_stream(void* p, const float4& v) {
@@ -158,6 +169,23 @@ __device__ __forceinline__ float row_sum16_last(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));  // row_shr:2
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));  // row_shr:4
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));  // row_shr:8
+  return x;
+}
+
+// max / sum over the 16 lanes of each row, left in every lane of the row: rotations by
+// 8, 4, 2, 1 within the row (DPP row_ror, no LDS traffic)
+__device__ __forceinline__ float row_max16_all(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
+  return x;
+}
+__device__ __forceinline__ float row_sum16_all(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
   return x;
 }
 

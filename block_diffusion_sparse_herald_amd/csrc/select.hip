@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
   const int n = lane & 15, kq = lane >> 4;  // MFMA column (key) and contraction quarter of this lane
 
   // MERGE: (head, 8-dim chunk) items of the merged query, G * D / 8 <= 128, each summed over
-  // B / parts query rows by `parts` threads; a thread's first eight rows are requested
-  // before the key rows, so that they (served from L2) arrive first
+  // B / parts query rows by `parts` threads; a thread's first eight rows are in flight
+  // together with the key rows (every load unconditional, from a clamped address)
   const int items = G * (D / 8), parts = 256 / items;
   const int qit = threadIdx.x % items, qpt = threadIdx.x / items;
   const int qper = (B + parts - 1) / parts, qb0 = qpt * qper, qb1 = min(B, qb0 + qper);
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
   if (MERGE) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      qv[u] = qthread && qb0 + u < qb1 ? ld16(qsrc + (int64_t)(qb0 + u) * Hq * D) : make_uint4(0, 0, 0, 0);
+      qv[u] = ld16_or_zero(qsrc + (int64_t)min(qb0 + u, B - 1) * Hq * D, qthread && qb0 + u < qb1);
   }
 
   // B operand: key rows, all loads of this wave in flight at once
@@ -121,8 +121,10 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int64_t j = wtok0 + b * 16 + n;
+    // keys past the sequence re-read its last row: their logits are computed and dropped
+    const int64_t jc = j < L ? j : L - 1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[b][ks] = j < L ? ld16(kbase + j * row_stride + ks * 32) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) kb[b][ks] = ld16(kbase + jc * row_stride + ks * 32);
   }
 
   __shared__ __align__(16) float qm[MERGE ? 8 * D : 4];  // merged query of the group's heads (MERGE)
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
       for (int b = qb0; b < qb1; b += 8) {
         if (b > qb0) {  // rows past the first eight (B / parts > 8)
 #pragma unroll
-          for (int u = 0; u < 8; ++u) qv[u] = b + u < qb1 ? ld16(qsrc + (int64_t)(b + u) * Hq * D) : make_uint4(0, 0, 0, 0);
+          for (int u = 0; u < 8; ++u) qv[u] = ld16_or_zero(qsrc + (int64_t)min(b + u, B - 1) * Hq * D, b + u < qb1);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -189,12 +191,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
   // lane holds logits of query heads 4*kq + i (i = 0..3) for key n of each column block;
   // stored token-major, the group's heads padded to 4 or 8 per token
   const int GP = G <= 4 ? 4 : 8;
-  float m[4], z[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    z[i] = 0.f;
-  }
+  float xs[NB][4];  // the logits again, -inf past the sequence or the group's heads
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -204,33 +201,27 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const bf16* __restrict__
       acc = mfma16x16x32(alo[ks], kb[b][ks], acc);
     }
     const int64_t j = wtok0 + b * 16 + n;
-    if (j < L) {
-      if (4 * kq < GP)
-        st16_stream(logits + ((int64_t)g * total + j0 + j) * GP + 4 * kq, make_float4(acc[0], acc[1], acc[2], acc[3]));
+    if (j < L && 4 * kq < GP)
+      st16_stream(logits + ((int64_t)g * total + j0 + j) * GP + 4 * kq, make_float4(acc[0], acc[1], acc[2], acc[3]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = kq * 4 + i;
-        if (hh < G) {
-          const float x = acc[i];
-          if (x > m[i]) {
-            z[i] = z[i] * fast_exp2(m[i] - x) + 1.f;
-            m[i] = x;
-          } else {
-            z[i] += fast_exp2(x - m[i]);
-          }
-        }
-      }
-    }
+    for (int i = 0; i < 4; ++i) xs[b][i] = j < L && kq * 4 + i < G ? acc[i] : -INFINITY;
   }
-  // (max, sum) per head: over the 16 keys of the lane group, then over the 4 waves in order
+  // (max, sum) per head over the wave's 64 keys: the max over the row of 16 lanes (every
+  // lane gets it), each lane's sum of 2^(x - max), the sum over the row; then over the 4
+  // waves in order
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float mx = xs[0][i];
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float m2 = __shfl_xor(m[i], o), z2 = __shfl_xor(z[i], o);
-      ms_merge(m[i], z[i], m2, z2);
+    for (int b = 1; b < NB; ++b) mx = fmaxf(mx, xs[b][i]);
+    mx = row_max16_all(mx);
+    float zs = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) zs += fast_exp2(xs[b][i] - mx);
     }
-    if (n == 0) red[w][kq * 4 + i] = make_float2(m[i], z[i]);
+    zs = row_sum16_all(zs);
+    if (n == 0) red[w][kq * 4 + i] = make_float2(mx, zs);
   }
   __syncthreads();
   if (threadIdx.x < G) {
@@ -390,17 +381,15 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ 
       }
     }
   }
-  // (max, sum) per block and head: over the 16 tokens of the lane group
+  // (max, sum) per block and head over the 16 tokens of the lane group: the row max (every
+  // lane gets it), each lane's sum rescaled to it, the row sum (DPP, no LDS traffic)
 #pragma unroll
   for (int q = 0; q < NBW; ++q)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float m2 = __shfl_xor(m[q][t], o), z2 = __shfl_xor(z[q][t], o);
-        ms_merge(m[q][t], z[q][t], m2, z2);
-      }
-      if (n == 0 && kq * 4 + t < 8) red[w + 4 * q][kq * 4 + t] = make_float2(m[q][t], z[q][t]);
+      const float M = row_max16_all(m[q][t]);
+      const float zz = row_sum16_all(M == -INFINITY ? 0.f : z[q][t] * fast_exp2(m[q][t] - M));
+      if (n == 0 && kq * 4 + t < 8) red[w + 4 * q][kq * 4 + t] = make_float2(M, zz);
     }
   __syncthreads();
   // per query head: the blocks of its KV head (p = g, g + Hkv, ...) in order
@@ -506,7 +495,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
       jj[u] = tok0 + (it + u) * 32 + slot;
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        v[u][i] = jj[u] < L ? ld16(kbase + jj[u] * row_stride + (i * 8 + sub) * EPL) : make_uint4(0, 0, 0, 0);
+        v[u][i] = ld16(kbase + (jj[u] < L ? jj[u] : L - 1) * row_stride + (i * 8 + sub) * EPL);  // past L: dropped
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -522,10 +511,16 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
 #pragma unroll
           for (int hh = 0; hh < MAXG; ++hh) acc[hh] = fmaf(qr[hh][i * EPL + e], f[e], acc[hh]);
       }
+      // sum over the 8 lanes sharing the row: quad swaps 1 and 2, then the half-row mirror
+      // (DPP, no LDS traffic; every lane gets the same sum, paired as an xor butterfly)
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1)
-#pragma unroll
-        for (int hh = 0; hh < MAXG; ++hh) acc[hh] += __shfl_xor(acc[hh], o);
+      for (int hh = 0; hh < MAXG; ++hh) {
+        float a = acc[hh];
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x141, 0xf, 0xf, false));  // row_half_mirror
+        acc[hh] = a;
+      }
       float x = acc[0];
 #pragma unroll
       for (int hh = 1; hh < MAXG; ++hh)
