@@ -96,6 +96,10 @@ SMALL = {
     # items per XCD, 8 per pair)
     "merge_home_12units": Workload("merge_home_12units", nseq=3, L=2500, Hq=16, Hkv=4, d=128, dtype="bf16", B=16,
                                    C=900, topk=600, T=2, planted=8, seed_base=8800),
+    # fp32 with 66 refine tiles of 64 candidates (4200 = 65 * 64 + 40): the scores kernel
+    # merges each row's tile statistics in five batches of loads, the last one partial
+    "f32_c4200": Workload("f32_c4200", nseq=1, L=6000, Hq=4, Hkv=1, d=64, dtype="f32", B=4,
+                                     C=4200, topk=500, T=1, planted=4, seed_base=8900),
     # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
     "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
                            T=2, seed_base=7800),
