@@ -32,26 +32,27 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k, co
   const int64_t j0 = PACKED ? 0 : seq_start[s];
   const int64_t L = PACKED ? 0 : seq_start[s + 1] - j0;
 
-  // K rows (copied straight through) and V rows (staged in LDS): all loads first
+  // K rows (copied straight through) and V rows (staged in LDS): all loads first, the
+  // indices of every chunk, then every row chunk. No load sits behind a branch (an
+  // index outside the sequence reads its row 0, L >= 1, and the value is dropped), so
+  // all of them are in flight together.
   constexpr int NPT = 64 * CPR / 256;  // 16-byte chunks per thread, each of K and V
   uint4 kv[NPT], vv[NPT];
+  int32_t jj[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int i = min(i0 + (int)(threadIdx.x + u * 256) / CPR, topk - 1);
+    jj[u] = PACKED ? i : idx[unit * topk + i];
+  }
   bool bad = false;
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
-    const int c = threadIdx.x + u * 256;
-    const int i = min(i0 + c / CPR, topk - 1), ch = c % CPR;
-    int64_t row;
-    bool ok = true;
-    if (PACKED) {
-      row = unit * topk + i;
-    } else {
-      const int32_t j = idx[unit * topk + i];
-      ok = j >= 0 && j < L;
-      row = (j0 + (ok ? j : 0)) * Hkv + g;
-    }
+    const int ch = (int)(threadIdx.x + u * 256) % CPR;
+    const bool ok = PACKED || (jj[u] >= 0 && jj[u] < L);
+    const int64_t row = PACKED ? unit * topk + jj[u] : (j0 + (ok ? jj[u] : 0)) * Hkv + g;
     bad |= !ok;
-    kv[u] = ok ? ld16(k + row * D + ch * EPL) : make_uint4(0, 0, 0, 0);
-    vv[u] = ok ? ld16(v + row * D + ch * EPL) : make_uint4(0, 0, 0, 0);
+    kv[u] = ld16_or_zero(k + row * D + ch * EPL, ok);
+    vv[u] = ld16_or_zero(v + row * D + ch * EPL, ok);
   }
   if (!PACKED && bad && status) *status = 1;
 #pragma unroll
