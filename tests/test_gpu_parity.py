@@ -100,6 +100,16 @@ SMALL = {
     # merges each row's tile statistics in five batches of loads, the last one partial
     "f32_c4200": Workload("f32_c4200", nseq=1, L=6000, Hq=4, Hkv=1, d=64, dtype="f32", B=4,
                                      C=4200, topk=500, T=1, planted=4, seed_base=8900),
+    # 64 (sequence, KV head) pairs of eight 16-row query tiles, three key ranges merged on
+    # the XCD that ran them
+    "pairs64_g4": Workload("pairs64_g4", nseq=8, L=2500, Hq=32, Hkv=8, d=128, dtype="bf16", B=32, C=800, topk=500, T=2,
+                       planted=4, seed_base=9000),
+    # G = 7 over 32 pairs: 14 query tiles in row groups of 4, 4, 4 and 2, ragged lengths
+    "pairs32_g7_ragged": Workload("pairs32_g7_ragged", nseq=8, L=3000, L_min=1500, Hq=28, Hkv=4, d=128, dtype="bf16",
+                              B=32, C=900, topk=600, T=2, seed_base=9100),
+    # the same pair count at head dim 64
+    "pairs64_d64": Workload("pairs64_d64", nseq=8, L=2000, Hq=32, Hkv=8, d=64, dtype="bf16", B=32, C=700, topk=480, T=1,
+                        planted=4, seed_base=9200),
     # 15 rows (a ragged row tile), subset longer than 8 blocks per wave round
     "b5_g3_long": Workload("b5_g3_long", nseq=1, L=6000, Hq=3, Hkv=1, d=128, dtype="bf16", B=5, C=3000, topk=1100,
                            T=2, seed_base=7800),
