@@ -120,6 +120,14 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same with the non-temporal hint (nt): for data read once in a long stream, so that
+// it does not displace from the caches what the next kernels read (the full-cache scan:
+// the candidate rows and logits that the score, refine and gather kernels read next).
+__device__ __forceinline__ void lds_dma16_nt(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // s_waitcnt with vmcnt <= n (n < 64), the other counters not waited on.
 template <int N>
 __device__ __forceinline__ void wait_vm() {

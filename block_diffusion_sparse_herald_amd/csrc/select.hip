@@ -245,9 +245,11 @@ __device__ __forceinline__ int scan_swz(int r, int hshift) {
 // sequence, all KV heads, in steps of SR cache rows (SR / Hkv tokens x Hkv heads,
 // contiguous in the token-major cache): direct-to-LDS loads of the step, one wait,
 // every wave's fragments of the step into registers, then the next step's loads are
-// issued before this step's products. Several workgroups share a compute unit, so
-// one's loads also overlap another's products. Wave w takes the step's 16-row blocks p = w, w + 4, ...; block p
-// is 16 tokens (16 (p / Hkv) ..) of KV head p % Hkv. The logits of the tpc tokens
+// issued before this step's products. The cache rows are loaded non-temporal: the
+// gigabyte-scale stream then leaves the caches to what the next kernels read (16 x 32K
+// and 4 x 128K steps -30 us). Several workgroups share a compute unit, so one's loads
+// also overlap another's products. Wave w takes the step's 16-row blocks p = w, w + 4,
+// ...; block p is 16 tokens (16 (p / Hkv) ..) of KV head p % Hkv. The logits of the tpc tokens
 // collect in LDS and leave at the end as one contiguous run per KV head (small
 // scattered stores between the loads cost several times their bytes).
 template <int D, int SR>
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ 
       const int r = (4 * u + w) * RPI + rr;
       const int64_t tok = min(t0 + (r >> hshift), L - 1);
       const bf16* src = k + ((j0 + tok) * Hkv + (r & (Hkv - 1))) * D + ((pc ^ scan_swz<D>(r, hshift)) * 8);
-      lds_dma16(src, lds0 + (uint32_t)((4 * u + w) * RPI * D) * 2u);
+      lds_dma16_nt(src, lds0 + (uint32_t)((4 * u + w) * RPI * D) * 2u);  // read once: not kept in the caches
     }
   };
   issue(0);
