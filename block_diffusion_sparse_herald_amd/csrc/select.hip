@@ -971,11 +971,12 @@ static int maxg_of(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
 // The LDS-staged scan streams faster once there are enough workgroups to keep
 // several on every compute unit; below that the register-load scan, with its 8x more
-// workgroups (one KV head each), finishes sooner. Measured ahead with 8 KV heads
-// (1 KiB of contiguous cache per 16-row block pair); with 4 KV heads the register
-// scan was ahead, so the LDS scan is used for 8 only (the kernel takes 1, 2, 4, 8).
+// workgroups (one KV head each), finishes sooner. Measured ahead with 8 KV heads and,
+// since its cache rows are loaded non-temporal, with 4 (8 ragged sequences of
+// 16K-64K tokens, 28/4 heads: step 880.9 -> 871.3 us); the kernel also takes 1 and 2
+// KV heads, not measured, so those stay on the register scan.
 static bool scan_in_lds(const Shape& s) {
-  return s.bf16 && s.Hkv == 8 && s.G <= 8 && s.total >= (int64_t)4 * 256 * kScanTok;
+  return s.bf16 && (s.Hkv == 8 || s.Hkv == 4) && s.G <= 8 && s.total >= (int64_t)4 * 256 * kScanTok;
 }
 
 // The merge inside the scan costs every scan workgroup a little; it pays only while

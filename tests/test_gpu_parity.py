@@ -75,6 +75,9 @@ SMALL = {
     # head dim 64 with a partial last step; 8 query heads per KV head
     "lds_scan_d64": Workload("lds_scan_d64", nseq=3, L=90000, Hq=16, Hkv=8, d=64, dtype="bf16", B=4,
                              C=700, topk=100, T=1, planted=8, seed_base=8100),
+    # the LDS-staged scan at 4 KV heads (G = 7, query heads padded to 8 per token)
+    "lds_scan_hkv4_g7": Workload("lds_scan_hkv4_g7", nseq=2, L=140000, Hq=28, Hkv=4, d=128, dtype="bf16", B=4,
+                                 C=600, topk=100, T=1, planted=8, seed_base=8350),
     "lds_scan_g8": Workload("lds_scan_g8", nseq=2, L=131100, Hq=64, Hkv=8, d=128, dtype="bf16", B=2, C=600,
                             topk=64, T=1, planted=8, seed_base=8200),
     # a sequence of more than 4096 bitmap words (262144 tokens): the radix emission runs
