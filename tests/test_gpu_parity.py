@@ -493,7 +493,8 @@ def test_graph_replay_matches_eager():
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), f"replay {rep} differs"
 
 
-@pytest.mark.parametrize("name", ["gqa32x8_L5000_b2", "ragged_g7_L1500-6000", "tiny_f32_L4096"])
+@pytest.mark.parametrize("name", ["gqa32x8_L5000_b2", "ragged_g7_L1500-6000", "tiny_f32_L4096", "lds_scan_hkv4_g7",
+                                  "lds_scan_d64"])
 def test_select_query_parity(name):
     """Selection from one given query per head (a [MASK]-query stand-in: the block's first query),
     band test against the oracle's single-query selection."""
