@@ -231,8 +231,9 @@ RefineWs carve_refine(const Shape& s, void* ws, size_t* bytes) {
   RefineWs w;
   const int tile = refine_tile_of(s);
   w.ntile = (s.C + tile - 1) / tile;
+  w.nsplit = refine_splits(s);
   w.row_stats = c.take<float2>((size_t)s.nseq * s.Hkv * ((w.ntile + 1) & ~1) * s.B * s.G);
-  w.rscore = c.take<float>((size_t)s.nseq * s.Hkv * s.C);
+  w.rscore = c.take<float>((size_t)w.nsplit * s.nseq * s.Hkv * s.C);
   *bytes = c.off;
   return w;
 }

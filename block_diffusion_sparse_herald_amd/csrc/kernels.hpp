@@ -57,9 +57,12 @@ struct SelectWs {
 
 struct RefineWs {
   float2* row_stats;   // [nseq][Hkv][rows][ntile rounded up to even] (max, sum) per refine tile
-  float* rscore;       // [nseq][Hkv][C]
+  float* rscore;       // [nsplit][nseq][Hkv][C] partial refine scores of the row splits
   int ntile;
+  int nsplit;          // row splits (refine_splits)
 };
+constexpr int kRefineMaxSplits = 4;
+constexpr int kRefineSplitTarget = 256;  // split rows while the grid stays within one workgroup per compute unit
 
 // Attention work split (see attn_geom): query tiles per workgroup, key ranges.
 struct AttnGeom {
@@ -116,6 +119,7 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
                                 float* topk_score, hipStream_t st);
 // candidates per refine workgroup (256 for bf16, 64 for fp32)
 int refine_tile_of(const Shape& s);
+int refine_splits(const Shape& s);
 // gather
 hipError_t launch_gather(const Shape& s, const void* k, const void* v, const int32_t* idx, void* k_sel, void* v_sel,
                          int32_t* status, hipStream_t st);

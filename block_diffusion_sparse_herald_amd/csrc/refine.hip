@@ -100,17 +100,17 @@ __device__ __forceinline__ void refine_tile_logits(const uint4 (&a)[MT][RefineFr
 template <typename T, int D, int MT, int NW>
 __device__ __forceinline__ void refine_issue_rows(const T* __restrict__ q, const T* __restrict__ k,
                                                   const int32_t* __restrict__ cand, int64_t j0, int s, int g, int B,
-                                                  int Hq, int Hkv, int G, int C, int R, int RT, int ctile, T* qs,
-                                                  uint4 (&a)[MT][RefineFrag<T, D>::NC]) {
+                                                  int Hq, int Hkv, int G, int C, int R, int row0, int RT, int ctile,
+                                                  T* qs, uint4 (&a)[MT][RefineFrag<T, D>::NC]) {
   using F = RefineFrag<T, D>;
   constexpr int CPR = D / F::EPC;  // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;    // rows per load instruction
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rr = lane / CPR, p = lane % CPR;
-  // query rows: the waves take turns by instruction
+  // query rows row0 .. row0 + 16 RT: the waves take turns by instruction
   for (int r0 = w * RPI; r0 < RT * 16; r0 += NW * RPI) {
     const int r = r0 + rr;
-    const int rq = r < R ? r : 0;
+    const int rq = row0 + r < R ? row0 + r : 0;
     const T* src = q + (((int64_t)s * B + rq / G) * Hq + g * G + rq % G) * D + (p ^ refine_swz<T, D>(r)) * F::EPC;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)(qs + r0 * D), 16, 0, 0);
@@ -139,17 +139,18 @@ __global__ __launch_bounds__(NW * 64) void refine_stats_kernel(const T* __restri
                                                            const int32_t* __restrict__ cand,
                                                            const int64_t* __restrict__ seq_start, int B, int Hq,
                                                            int Hkv, int G, int C, float scale2, int ntile,
-                                                           float2* __restrict__ row_stats) {
+                                                           int nsplit, float2* __restrict__ row_stats) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int MT = refine_mt<T>();
-  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G, RT = (R + 15) / 16;
+  const int tile = blockIdx.x / nsplit, rsp = blockIdx.x - tile * nsplit, g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G, RTA = (R + 15) / 16, RTS = (RTA + nsplit - 1) / nsplit;
+  const int row0 = rsp * RTS * 16, RT = min(RTS, RTA - rsp * RTS);  // this workgroup's row tiles
   T* qs = reinterpret_cast<T*>(smem);                           // [RT*16][D]
   float2* wstat = reinterpret_cast<float2*>(qs + RT * 16 * D);  // [NW][RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cbase = tile * refine_tile<T, NW>() + w * MT * 16;
   uint4 a[MT][RefineFrag<T, D>::NC];
-  refine_issue_rows<T, D, MT, NW>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
+  refine_issue_rows<T, D, MT, NW>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, row0, RT, tile, qs, a);
   refine_wait_rows();
 
   const bool full = cbase + MT * 16 <= C;  // no candidate of this wave past C
@@ -182,13 +183,13 @@ __global__ __launch_bounds__(NW * 64) void refine_stats_kernel(const T* __restri
     if (lane < 16) wstat[w * RT * 16 + rt * 16 + lane] = make_float2(m, l);
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += NW * 64) {
+  for (int r = threadIdx.x; r < RT * 16 && row0 + r < R; r += NW * 64) {
     float M = -INFINITY, Z = 0.f;
     for (int ww = 0; ww < NW; ++ww) {
       const float2 p = wstat[ww * RT * 16 + r];
       ms_merge(M, Z, p.x, p.y);
     }
-    row_stats[(((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1) + tile] = make_float2(M, Z);
+    row_stats[(((int64_t)s * Hkv + g) * R + row0 + r) * ((ntile + 1) & ~1) + tile] = make_float2(M, Z);
   }
 }
 
@@ -197,25 +198,26 @@ __global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restr
                                                             const int32_t* __restrict__ cand,
                                                             const int64_t* __restrict__ seq_start, int B, int Hq,
                                                             int Hkv, int G, int C, float scale2, int ntile,
-                                                            const float2* __restrict__ row_stats,
+                                                            int nsplit, const float2* __restrict__ row_stats,
                                                             float* __restrict__ rscore) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int MT = refine_mt<T>();
-  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G, RT = (R + 15) / 16;
+  const int tile = blockIdx.x / nsplit, rsp = blockIdx.x - tile * nsplit, g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G, RTA = (R + 15) / 16, RTS = (RTA + nsplit - 1) / nsplit;
+  const int row0 = rsp * RTS * 16, RT = min(RTS, RTA - rsp * RTS);  // this workgroup's row tiles
   T* qs = reinterpret_cast<T*>(smem);                        // [RT*16][D]
   float* rowM = reinterpret_cast<float*>(qs + RT * 16 * D);  // [RT*16]
   float* rowIZ = rowM + RT * 16;                             // [RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cbase = tile * refine_tile<T, NW>() + w * MT * 16;
   uint4 a[MT][RefineFrag<T, D>::NC];
-  refine_issue_rows<T, D, MT, NW>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, RT, tile, qs, a);
+  refine_issue_rows<T, D, MT, NW>(q, k, cand, seq_start[s], s, g, B, Hq, Hkv, G, C, R, row0, RT, tile, qs, a);
   // per-row normalisers over all tiles, merged in tile order while the rows stream in
   // (a row's tile statistics are contiguous; 16 tiles per batch of loads)
   for (int r = threadIdx.x; r < RT * 16; r += NW * 64) {
     float M = -INFINITY, Z = 0.f;
-    if (r < R) {
-      const float2* rs = row_stats + (((int64_t)s * Hkv + g) * R + r) * ((ntile + 1) & ~1);  // 16-byte aligned rows
+    if (row0 + r < R) {
+      const float2* rs = row_stats + (((int64_t)s * Hkv + g) * R + row0 + r) * ((ntile + 1) & ~1);  // 16-byte aligned
       for (int t0 = 0; t0 < ntile; t0 += 16) {
         float2 p[16];
 #pragma unroll
@@ -234,8 +236,8 @@ __global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restr
       }
     }
     // rows past R: a reference far above any logit and a zero weight, so they add 0
-    rowM[r] = r < R ? M : 3.0e38f;
-    rowIZ[r] = r < R ? 1.f / Z : 0.f;
+    rowM[r] = row0 + r < R ? M : 3.0e38f;
+    rowIZ[r] = row0 + r < R ? 1.f / Z : 0.f;
   }
   refine_wait_rows();
 
@@ -265,7 +267,8 @@ __global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restr
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = cbase + mt * 16 + (lane >> 4) * 4 + i;
-        if (c < C) rscore[((int64_t)s * Hkv + g) * C + c] = rs[mt][i];
+        // the row split's partial sum; the top-K kernel adds the splits in order
+        if (c < C) rscore[(((int64_t)rsp * gridDim.z + s) * Hkv + g) * C + c] = rs[mt][i];
       }
   }
 }
@@ -278,8 +281,8 @@ __global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restr
 // whole sequence) the passes read them from global memory.
 template <bool STAGED>
 __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __restrict__ cand,
-                                                            const float* __restrict__ rscore, int Hkv, int C,
-                                                            int topk, int32_t* __restrict__ topk_idx,
+                                                            const float* __restrict__ rscore, int nsplit, int Hkv,
+                                                            int C, int topk, int32_t* __restrict__ topk_idx,
                                                             float* __restrict__ topk_score) {
   constexpr int NT = 1024;
   const int g = blockIdx.x, s = blockIdx.y;
@@ -298,6 +301,15 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
     uint32_t v[MAXIT][4], ix[MAXIT][4];
     topk_load<MAXIT>(rscore + base, C, nit, v);
     topk_load<MAXIT>(cand + base, C, nit, ix);
+    // row splits: R is the sum of the splits' partial scores, added in split order
+    for (int sp = 1; sp < nsplit; ++sp) {
+      uint32_t u[MAXIT][4];
+      topk_load<MAXIT>(rscore + (int64_t)sp * gridDim.y * Hkv * C + base, C, nit, u);
+#pragma unroll
+      for (int it = 0; it < MAXIT; ++it)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[it][c] = __float_as_uint(__uint_as_float(v[it][c]) + __uint_as_float(u[it][c]));
+    }
     for (int i = tid; i < kRadixBins; i += NT) h[i] = h2[i] = 0u;
     if (tid < kRadixBins / 2) h3[tid] = 0u;
     __syncthreads();
@@ -369,6 +381,20 @@ static int refine_waves(const Shape& s) {
   return t4 > 16 && wg8 >= 256 ? 8 : 4;
 }
 
+// Row splits of the refine: when the (sequence, KV head, candidate tile) grid leaves
+// compute units idle, each tile's query rows are split over 2 or 4 workgroups (each
+// with its rows' statistics and a partial score; the top-K kernel adds the partials).
+// Only for candidate sets the top-K kernel stages in registers.
+int refine_splits(const Shape& s) {
+  const int tile = refine_tile_of(s);
+  const int64_t nwg = (int64_t)((s.C + tile - 1) / tile) * s.Hkv * s.nseq;
+  const int RT = (s.B * s.G + 15) / 16;
+  int ns = 1;
+  if (s.C <= kMaxCandidates)
+    while (ns < kRefineMaxSplits && nwg * ns * 2 <= kRefineSplitTarget && RT % (ns * 2) == 0) ns *= 2;  // equal splits
+  return ns;
+}
+
 static size_t refine_smem(const Shape& s, bool stats) {
   const int RT = (s.B * s.G + 15) / 16;
   const size_t rows = (size_t)RT * 16 * s.D * (s.bf16 ? 2 : 4);
@@ -378,7 +404,7 @@ static size_t refine_smem(const Shape& s, bool stats) {
 template <typename T, int D, int NW>
 static hipError_t launch_refine_t(const Shape& s, const void* q, const void* k, const int32_t* cand,
                                   const RefineWs& ws, bool stats, hipStream_t st) {
-  const dim3 grid(ws.ntile, s.Hkv, s.nseq);
+  const dim3 grid(ws.ntile * ws.nsplit, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
   const size_t smem = refine_smem(s, stats);
   const void* kern = stats ? (const void*)refine_stats_kernel<T, D, NW> : (const void*)refine_scores_kernel<T, D, NW>;
@@ -386,10 +412,10 @@ static hipError_t launch_refine_t(const Shape& s, const void* q, const void* k, 
   if (e != hipSuccess) return e;
   if (stats)
     klaunch(refine_stats_kernel<T, D, NW>, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B,
-            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats);
+            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.nsplit, ws.row_stats);
   else
     klaunch(refine_scores_kernel<T, D, NW>, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B,
-            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.row_stats, ws.rscore);
+            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.nsplit, ws.row_stats, ws.rscore);
   return hipGetLastError();
 }
 
@@ -424,15 +450,15 @@ hipError_t launch_refine_scores(const Shape& s, const void* q, const void* k, co
 hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const RefineWs& ws, int32_t* topk_idx,
                                 float* topk_score, hipStream_t st) {
   if (s.C > kMaxCandidates) {
-    klaunch(refine_select_kernel<false>, dim3(s.Hkv, s.nseq), 1024, 0, st, cand, ws.rscore, s.Hkv, s.C, s.topk,
+    klaunch(refine_select_kernel<false>, dim3(s.Hkv, s.nseq), 1024, 0, st, cand, ws.rscore, 1, s.Hkv, s.C, s.topk,
             topk_idx, topk_score);
     return hipGetLastError();
   }
   const size_t smem = (size_t)(s.topk + kTopkSlack) * sizeof(int32_t) * (topk_score ? 2 : 1);
   hipError_t e = allow_smem((const void*)refine_select_kernel<true>, smem);
   if (e != hipSuccess) return e;
-  klaunch(refine_select_kernel<true>, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, s.Hkv, s.C, s.topk,
-          topk_idx, topk_score);
+  klaunch(refine_select_kernel<true>, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, ws.nsplit, s.Hkv, s.C,
+          s.topk, topk_idx, topk_score);
   return hipGetLastError();
 }
 
