@@ -134,7 +134,7 @@ __device__ __forceinline__ void refine_wait_rows() {
   __syncthreads();
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void refine_stats_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const int32_t* __restrict__ cand,
                                                            const int64_t* __restrict__ seq_start, int B, int Hq,
@@ -142,9 +142,11 @@ __global__ __launch_bounds__(NW * 64) void refine_stats_kernel(const T* __restri
                                                            int nsplit, float2* __restrict__ row_stats) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int MT = refine_mt<T>();
-  const int tile = blockIdx.x / nsplit, rsp = blockIdx.x - tile * nsplit, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G, RTA = (R + 15) / 16, RTS = (RTA + nsplit - 1) / nsplit;
-  const int row0 = rsp * RTS * 16, RT = min(RTS, RTA - rsp * RTS);  // this workgroup's row tiles
+  // SPLIT: row split rsp of tile; otherwise the whole tile (nsplit = 1)
+  const int tile = SPLIT ? blockIdx.x / nsplit : blockIdx.x, rsp = SPLIT ? blockIdx.x - tile * nsplit : 0;
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G, RTA = (R + 15) / 16, RTS = SPLIT ? (RTA + nsplit - 1) / nsplit : RTA;
+  const int row0 = SPLIT ? rsp * RTS * 16 : 0, RT = SPLIT ? min(RTS, RTA - rsp * RTS) : RTA;  // its row tiles
   T* qs = reinterpret_cast<T*>(smem);                           // [RT*16][D]
   float2* wstat = reinterpret_cast<float2*>(qs + RT * 16 * D);  // [NW][RT*16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) void refine_stats_kernel(const T* __restri
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                             const int32_t* __restrict__ cand,
                                                             const int64_t* __restrict__ seq_start, int B, int Hq,
@@ -202,9 +204,11 @@ __global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restr
                                                             float* __restrict__ rscore) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int MT = refine_mt<T>();
-  const int tile = blockIdx.x / nsplit, rsp = blockIdx.x - tile * nsplit, g = blockIdx.y, s = blockIdx.z;
-  const int R = B * G, RTA = (R + 15) / 16, RTS = (RTA + nsplit - 1) / nsplit;
-  const int row0 = rsp * RTS * 16, RT = min(RTS, RTA - rsp * RTS);  // this workgroup's row tiles
+  // SPLIT: row split rsp of tile; otherwise the whole tile (nsplit = 1)
+  const int tile = SPLIT ? blockIdx.x / nsplit : blockIdx.x, rsp = SPLIT ? blockIdx.x - tile * nsplit : 0;
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int R = B * G, RTA = (R + 15) / 16, RTS = SPLIT ? (RTA + nsplit - 1) / nsplit : RTA;
+  const int row0 = SPLIT ? rsp * RTS * 16 : 0, RT = SPLIT ? min(RTS, RTA - rsp * RTS) : RTA;  // its row tiles
   T* qs = reinterpret_cast<T*>(smem);                        // [RT*16][D]
   float* rowM = reinterpret_cast<float*>(qs + RT * 16 * D);  // [RT*16]
   float* rowIZ = rowM + RT * 16;                             // [RT*16]
@@ -407,15 +411,22 @@ static hipError_t launch_refine_t(const Shape& s, const void* q, const void* k, 
   const dim3 grid(ws.ntile * ws.nsplit, s.Hkv, s.nseq);
   const float scale2 = s.scale * kLog2e;
   const size_t smem = refine_smem(s, stats);
-  const void* kern = stats ? (const void*)refine_stats_kernel<T, D, NW> : (const void*)refine_scores_kernel<T, D, NW>;
+  const bool split = ws.nsplit > 1;
+  const void* kern = stats ? (split ? (const void*)refine_stats_kernel<T, D, NW, true>
+                                    : (const void*)refine_stats_kernel<T, D, NW, false>)
+                           : (split ? (const void*)refine_scores_kernel<T, D, NW, true>
+                                    : (const void*)refine_scores_kernel<T, D, NW, false>);
   hipError_t e = allow_smem(kern, smem);
   if (e != hipSuccess) return e;
-  if (stats)
-    klaunch(refine_stats_kernel<T, D, NW>, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B,
-            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.nsplit, ws.row_stats);
-  else
-    klaunch(refine_scores_kernel<T, D, NW>, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B,
-            s.Hq, s.Hkv, s.G, s.C, scale2, ws.ntile, ws.nsplit, ws.row_stats, ws.rscore);
+  if (stats) {
+    auto kf = split ? refine_stats_kernel<T, D, NW, true> : refine_stats_kernel<T, D, NW, false>;
+    klaunch(kf, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G, s.C,
+            scale2, ws.ntile, ws.nsplit, ws.row_stats);
+  } else {
+    auto kf = split ? refine_scores_kernel<T, D, NW, true> : refine_scores_kernel<T, D, NW, false>;
+    klaunch(kf, grid, NW * 64, smem, st, (const T*)q, (const T*)k, cand, s.seq_start, s.B, s.Hq, s.Hkv, s.G, s.C,
+            scale2, ws.ntile, ws.nsplit, ws.row_stats, ws.rscore);
+  }
   return hipGetLastError();
 }
 
