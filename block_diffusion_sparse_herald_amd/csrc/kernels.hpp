@@ -21,6 +21,8 @@ constexpr int kScoreTok = 1024;
 // workgroups amortise the per-workgroup normaliser merge and histogram flush.
 constexpr int kScoreTokLarge = 2048;
 constexpr int64_t kScoreTokLargeFrom = 262144;
+constexpr int kScoreTokSmall = 256;
+constexpr int64_t kScoreTokSmallUpTo = 16384;  // (token, KV head) pairs in the batch
 constexpr int kRadixBins = 2048;
 // Longest sequence whose selection scores one 1024-thread workgroup keeps in registers
 // (36 per thread) for the one-kernel top-C.

@@ -1034,20 +1034,29 @@ hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStr
   return hipGetLastError();
 }
 
-static int score_tok(const Shape& s) { return s.total >= kScoreTokLargeFrom ? kScoreTokLarge : kScoreTok; }
+// Tokens per score workgroup: 2048 on large caches, 256 on small ones (a few thousand
+// (token, KV head) pairs would otherwise make a handful of workgroups), else 1024. The
+// small size never reaches the radix passes (sequences past the register top-C are longer).
+static int score_tok(const Shape& s) {
+  if (s.total >= kScoreTokLargeFrom) return kScoreTokLarge;
+  return s.total * s.Hkv <= kScoreTokSmallUpTo ? kScoreTokSmall : kScoreTok;
+}
 static int score_chunks(const Shape& s) { return (int)((s.max_len + score_tok(s) - 1) / score_tok(s)); }
 
 hipError_t launch_score_hist(const Shape& s, const SelectWs& ws, hipStream_t st) {
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
-  const bool large = score_tok(s) == kScoreTokLarge;
-  auto kern = s.G <= 4 ? (large ? score_hist_kernel<4, kScoreTokLarge> : score_hist_kernel<4, kScoreTok>)
-                       : (large ? score_hist_kernel<8, kScoreTokLarge> : score_hist_kernel<8, kScoreTok>);
+  const int tok = score_tok(s);
+  auto kern = s.G <= 4 ? (tok == kScoreTokLarge ? score_hist_kernel<4, kScoreTokLarge>
+                          : tok == kScoreTokSmall ? score_hist_kernel<4, kScoreTokSmall> : score_hist_kernel<4, kScoreTok>)
+                       : (tok == kScoreTokLarge ? score_hist_kernel<8, kScoreTokLarge>
+                          : tok == kScoreTokSmall ? score_hist_kernel<8, kScoreTokSmall> : score_hist_kernel<8, kScoreTok>);
   klaunch(kern, grid, 256, 0, st, ws.logits, ws.partials, s.seq_start, s.Hq, s.Hkv, s.G, s.total, ws.nchunk, ws.tpc,
           ws.scores, ws.hist);
   return hipGetLastError();
 }
 
 hipError_t launch_radix_pass(const Shape& s, const SelectWs& ws, int pass, hipStream_t st) {
+  if (score_tok(s) == kScoreTokSmall) return hipErrorInvalidValue;  // small caches take the register top-C
   dim3 grid(score_chunks(s), s.Hkv, s.nseq);
   const bool large = score_tok(s) == kScoreTokLarge;
   auto kern = pass == 2 ? (large ? radix_kernel<2, kScoreTokLarge> : radix_kernel<2, kScoreTok>)
