@@ -160,7 +160,7 @@ struct Carver {
 SelectWs carve_select(const Shape& s, void* ws, size_t* bytes) {
   Carver c{static_cast<char*>(ws)};
   SelectWs w;
-  w.tpc = kScanTok;
+  w.tpc = !s.bf16 && s.total * s.Hkv <= kScoreTokSmallUpTo ? kScanTokSmall : kScanTok;
   w.nchunk = (int)((s.max_len + w.tpc - 1) / w.tpc);
   w.nwords = (int)((s.max_len + 63) / 64);
   w.qbar = c.take<float>((size_t)s.nseq * s.Hq * s.D);

@@ -16,6 +16,9 @@ inline void klaunch(F kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st
 // Tokens one scan workgroup covers (one KV head), and tokens one score / radix
 // workgroup covers.
 constexpr int kScanTok = 256;
+// fp32 caches of up to kScoreTokSmallUpTo (token, KV head) pairs scan in chunks of 64
+// tokens, four times the workgroups of the full chunk on a cache that would fill few.
+constexpr int kScanTokSmall = 64;
 constexpr int kScoreTok = 1024;
 // Score / radix workgroups of 2048 tokens once the cache holds this many tokens: fewer
 // workgroups amortise the per-workgroup normaliser merge and histogram flush.

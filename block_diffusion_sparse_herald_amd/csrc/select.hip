@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(const bf16* __restrict__ 
 // the merged query of the group formed in the workgroup (16-byte chunks of the B query
 // rows summed in runs per thread, the runs added in a fixed order, times mul), and the
 // radix histograms zeroed.
-template <int D, int MAXG, bool MERGE>
+template <int D, int MAXG, bool MERGE, int TOK>
 __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict__ k, const float* __restrict__ qbar,
                                                         const float* __restrict__ q, int B, float mul,
                                                         uint32_t* __restrict__ zero, int64_t zero_words,
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
   constexpr int EPL = 4;             // fp32 elements per 16-byte load
   constexpr int NL = D / (8 * EPL);  // loads per lane per key row
   constexpr int PER = D / 8;         // elements per lane per key row
-  constexpr int U = 4;               // key rows in flight per lane
+  constexpr int U = TOK >= 128 ? 4 : TOK / 32;  // key rows in flight per lane
   __shared__ float2 red[32][8];
   const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   if (MERGE) {  // histograms of the candidate selection, zeroed before any workgroup leaves
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
   }
   const int64_t j0 = seq_start[s];
   const int64_t L = seq_start[s + 1] - j0;
-  const int64_t tok0 = (int64_t)chunk * kScanTok;
+  const int64_t tok0 = (int64_t)chunk * TOK;
   if (tok0 >= L) return;
   const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
 
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
   const int64_t row_stride = (int64_t)Hkv * D;
   const float* kbase = k + (j0 * Hkv + g) * D;
   float m = -INFINITY, ssum = 0.f;
-  for (int it = 0; it < kScanTok / 32; it += U) {
+  for (int it = 0; it < TOK / 32; it += U) {
     uint4 v[U][NL];
     int64_t jj[U];
 #pragma unroll
@@ -1016,14 +1016,18 @@ hipError_t launch_scan(const Shape& s, const void* k, const SelectWs& ws, hipStr
 #define HERALD_SCAN_CASE(GG)                                                                                       \
   case GG:                                                                                                         \
     if (s.D == 128)                                                                                                \
-      klaunch(merge ? scan_valu_kernel<128, GG, true> : scan_valu_kernel<128, GG, false>, grid, 256, 0, st,          \
-              (const float*)k, ws.qbar, (const float*)q, nq1, mul, ws.hist, zero_words, s.seq_start, s.Hq, s.Hkv,  \
-              s.G, s.total, ws.nchunk, ws.logits, ws.partials);                                                    \
+      klaunch(small ? (merge ? scan_valu_kernel<128, GG, true, kScanTokSmall> : scan_valu_kernel<128, GG, false, kScanTokSmall>) \
+                    : (merge ? scan_valu_kernel<128, GG, true, kScanTok> : scan_valu_kernel<128, GG, false, kScanTok>),      \
+              grid, 256, 0, st, (const float*)k, ws.qbar, (const float*)q, nq1, mul, ws.hist, zero_words, s.seq_start,      \
+              s.Hq, s.Hkv, s.G, s.total, ws.nchunk, ws.logits, ws.partials);                                              \
     else                                                                                                           \
-      klaunch(merge ? scan_valu_kernel<64, GG, true> : scan_valu_kernel<64, GG, false>, grid, 256, 0, st,            \
-              (const float*)k, ws.qbar, (const float*)q, nq1, mul, ws.hist, zero_words, s.seq_start, s.Hq, s.Hkv,  \
-              s.G, s.total, ws.nchunk, ws.logits, ws.partials);                                                    \
+      klaunch(small ? (merge ? scan_valu_kernel<64, GG, true, kScanTokSmall> : scan_valu_kernel<64, GG, false, kScanTokSmall>)   \
+                    : (merge ? scan_valu_kernel<64, GG, true, kScanTok> : scan_valu_kernel<64, GG, false, kScanTok>),        \
+              grid, 256, 0, st, (const float*)k, ws.qbar, (const float*)q, nq1, mul, ws.hist, zero_words, s.seq_start,      \
+              s.Hq, s.Hkv, s.G, s.total, ws.nchunk, ws.logits, ws.partials);                                              \
     break;
+  if (ws.tpc != kScanTok && ws.tpc != kScanTokSmall) return hipErrorInvalidValue;
+  const bool small = ws.tpc == kScanTokSmall;
   switch (maxg_of(s.G)) {
     HERALD_SCAN_CASE(1)
     HERALD_SCAN_CASE(2)
