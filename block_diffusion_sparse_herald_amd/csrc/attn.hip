@@ -351,11 +351,11 @@ __global__ __launch_bounds__(512) void attn_kernel(const bf16* __restrict__ q, c
 // with two ranges (ragged 28/4 workload) the plain order was 0.25 us faster.
 __host__ __device__ inline bool attn_combine_home(const AttnGeom& a) { return a.nks >= 3; }
 
-template <int D, int NT>
+template <int D, int NT, int CH, bool EXACT>
 __global__ __launch_bounds__(NT) void attn_combine_kernel(const float* __restrict__ o_part,
                                                                            const float2* __restrict__ ml_part,
                                                                            AttnGeom a, bf16* __restrict__ out) {
-  constexpr int CH = 8, TPR = D / 8;  // threads per output row
+  constexpr int TPR = D / 8;  // threads per output row
   const int R = a.B * a.G;
   const int per_unit = R * TPR;
   int unit, iu;
@@ -384,14 +384,15 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(const float* __restric
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int k0 = 0; k0 < a.nks; k0 += CH) {
+  const int nks = EXACT ? CH : a.nks;  // EXACT: a single, fully known chunk
+  for (int k0 = 0; k0 < nks; k0 += CH) {
     float2 p[CH];
     float4 va[CH], vc[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       p[j] = make_float2(-INFINITY, 0.f);
       va[j] = vc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k0 + j < a.nks) {
+      if (EXACT || k0 + j < a.nks) {  // EXACT: CH == nks, one chunk, every load unconditional
         const int64_t row = base + (int64_t)(k0 + j) * a.rpad;
         p[j] = ml_part[row];
         va[j] = *reinterpret_cast<const float4*>(o_part + row * D + e);
@@ -711,17 +712,25 @@ hipError_t launch_attn_combine(const Shape& s, void* ws, void* out, hipStream_t 
   }
   if (nwg == 0) return hipSuccess;
   const dim3 grid((unsigned)nwg);
-  if (nt == 256) {
-    if (s.D == 128)
-      klaunch(attn_combine_kernel<128, 256>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
-    else
-      klaunch(attn_combine_kernel<64, 256>, grid, 256, 0, st, o_part, ml_part, a, (bf16*)out);
-  } else {
-    if (s.D == 128)
-      klaunch(attn_combine_kernel<128, kAttnCombineThreads>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
-    else
-      klaunch(attn_combine_kernel<64, kAttnCombineThreads>, grid, kAttnCombineThreads, 0, st, o_part, ml_part, a, (bf16*)out);
+  // key-range counts with a kernel of their own take every load unconditionally
+#define HERALD_COMBINE(NTT, CHH, EX)                                                                      \
+  klaunch(s.D == 128 ? attn_combine_kernel<128, NTT, CHH, EX> : attn_combine_kernel<64, NTT, CHH, EX>, grid, NTT, 0, st, \
+          o_part, ml_part, a, (bf16*)out)
+#define HERALD_COMBINE_NKS(NTT)              \
+  switch (a.nks) {                           \
+    case 2: HERALD_COMBINE(NTT, 2, true); break; \
+    case 3: HERALD_COMBINE(NTT, 3, true); break; \
+    case 4: HERALD_COMBINE(NTT, 4, true); break; \
+    case 6: HERALD_COMBINE(NTT, 6, true); break; \
+    default: HERALD_COMBINE(NTT, 8, false);      \
   }
+  if (nt == 256) {
+    HERALD_COMBINE_NKS(256)
+  } else {
+    HERALD_COMBINE_NKS(kAttnCombineThreads)
+  }
+#undef HERALD_COMBINE_NKS
+#undef HERALD_COMBINE
   return hipGetLastError();
 }
 
