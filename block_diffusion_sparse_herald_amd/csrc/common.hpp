@@ -468,13 +468,15 @@ constexpr int kTopkWaves = 16;
 __host__ __device__ constexpr int topk_chunks(int n) { return ((n + kTopkWaves - 1) / kTopkWaves + 255) / 256; }
 
 // Loads this lane's keys src[0..n) (positions past n read as 0): 16-byte loads when src
-// is 16-byte aligned and n a multiple of 4, else 4-byte loads.
-template <int MAXIT, typename T>
+// is 16-byte aligned and n a multiple of 4, else 4-byte loads. ALIGN = 1 or 2 fixes the
+// choice at compile time (the caller knows it): with one path only, the compiler does not
+// wait for the loads of an earlier call before issuing these.
+template <int MAXIT, typename T, int ALIGN = 0>
 __device__ __forceinline__ void topk_load(const T* __restrict__ src, int n, int nit, uint32_t (&v)[MAXIT][4]) {
   static_assert(sizeof(T) == 4, "32-bit keys");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
-  if (((uintptr_t)src & 15) == 0 && (n & 3) == 0) {
+  if (ALIGN == 1 || (ALIGN == 0 && ((uintptr_t)src & 15) == 0 && (n & 3) == 0)) {
 #pragma unroll
     for (int it = 0; it < MAXIT; ++it) {
       const int e = (w * nit + it) * 256 + 4 * lane;

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(NW * 64) void refine_scores_kernel(const T* __restr
 // (topk_load's layout: each wave a contiguous range of positions), the histograms take
 // LDS atomics and the picks are ordered by wave scans in LDS, then written out. Otherwise (candidate sets up to the
 // whole sequence) the passes read them from global memory.
-template <bool STAGED>
+template <bool STAGED, int ALIGN = 0>
 __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __restrict__ cand,
                                                             const float* __restrict__ rscore, int nsplit, int Hkv,
                                                             int C, int topk, int32_t* __restrict__ topk_idx,
@@ -303,16 +303,25 @@ __global__ __launch_bounds__(1024) void refine_select_kernel(const int32_t* __re
     const int tid = threadIdx.x, w = tid >> 6;
     const int nit = topk_chunks(C);
     uint32_t v[MAXIT][4], ix[MAXIT][4];
-    topk_load<MAXIT>(rscore + base, C, nit, v);
-    topk_load<MAXIT>(cand + base, C, nit, ix);
-    // row splits: R is the sum of the splits' partial scores, added in split order
-    for (int sp = 1; sp < nsplit; ++sp) {
-      uint32_t u[MAXIT][4];
-      topk_load<MAXIT>(rscore + (int64_t)sp * gridDim.y * Hkv * C + base, C, nit, u);
+    topk_load<MAXIT, float, ALIGN>(rscore + base, C, nit, v);
+    topk_load<MAXIT, int32_t, ALIGN>(cand + base, C, nit, ix);
+    // row splits: R is the sum of the splits' partial scores, added in split order. All
+    // splits are loaded before the first sum (a split past nsplit re-reads the last one and
+    // is not added), so their loads are in flight together
+    if (nsplit > 1) {
+      uint32_t u[kRefineMaxSplits - 1][MAXIT][4];
 #pragma unroll
-      for (int it = 0; it < MAXIT; ++it)
+      for (int sp = 1; sp < kRefineMaxSplits; ++sp)
+        topk_load<MAXIT, float, ALIGN>(rscore + (int64_t)min(sp, nsplit - 1) * gridDim.y * Hkv * C + base, C, nit,
+                                       u[sp - 1]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[it][c] = __float_as_uint(__uint_as_float(v[it][c]) + __uint_as_float(u[it][c]));
+      for (int sp = 1; sp < kRefineMaxSplits; ++sp)
+        if (sp < nsplit)
+#pragma unroll
+          for (int it = 0; it < MAXIT; ++it)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              v[it][c] = __float_as_uint(__uint_as_float(v[it][c]) + __uint_as_float(u[sp - 1][it][c]));
     }
     for (int i = tid; i < kRadixBins; i += NT) h[i] = h2[i] = 0u;
     if (tid < kRadixBins / 2) h3[tid] = 0u;
@@ -466,9 +475,13 @@ hipError_t launch_refine_select(const Shape& s, const int32_t* cand, const Refin
     return hipGetLastError();
   }
   const size_t smem = (size_t)(s.topk + kTopkSlack) * sizeof(int32_t) * (topk_score ? 2 : 1);
-  hipError_t e = allow_smem((const void*)refine_select_kernel<true>, smem);
+  // the rows of C scores and candidates start 16-byte aligned when C % 4 == 0 and both
+  // buffers do; then the kernel takes the 16-byte loads without a run-time check
+  const bool aligned = s.C % 4 == 0 && ((uintptr_t)cand & 15) == 0 && ((uintptr_t)ws.rscore & 15) == 0;
+  auto kern = aligned ? refine_select_kernel<true, 1> : refine_select_kernel<true, 0>;
+  hipError_t e = allow_smem((const void*)kern, smem);
   if (e != hipSuccess) return e;
-  klaunch(refine_select_kernel<true>, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, ws.nsplit, s.Hkv, s.C,
+  klaunch(kern, dim3(s.Hkv, s.nseq), 1024, smem, st, cand, ws.rscore, ws.nsplit, s.Hkv, s.C,
           s.topk, topk_idx, topk_score);
   return hipGetLastError();
 }
